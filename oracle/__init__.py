@@ -1,0 +1,166 @@
+"""CPU oracle for GPU-resident attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never loads it.
+
+``liboracle.so`` (plain C, fp64, OpenMP over independent (batch, head) or
+(sequence, head) units) is built from ``oracle.c`` by :func:`build`.  The
+functions here only marshal numpy arrays; the arithmetic is in ``oracle.c``
+and follows the definitions cited there:
+
+* prefill -- trueno-gpu 0.4.11 ``src/memory/resident/attention.rs``,
+  ``batched_multihead_attention``; trustformers-core 0.2.0
+  ``src/gpu_ops/cuda/oxicuda/attention.rs``, ``attention_prefill_gpu_to_gpu``
+  and ``prefill_reference``;
+* decode -- trueno-gpu ``incremental_attention_gpu``; realizar 0.8.5
+  ``src/cuda/executor/cache_from_cache_from_kv_cache.rs``,
+  ``init_kv_cache_gpu`` / ``init_batched_kv_cache_gpu`` (GQA cache layout);
+* scatter -- trueno-gpu ``kv_cache_scatter_gpu``.
+
+``brute.py`` is a second, independent numpy fp64 formulation used only to
+cross-check this one on tiny shapes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile oracle.c into a shared library (gcc, -O2, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    p = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    lib.oracle_prefill.argtypes = [p, p, p, p, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int]
+    lib.oracle_prefill.restype = ctypes.c_int
+    lib.oracle_prefill_rows.argtypes = [p, p, p, p, i64, p, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int]
+    lib.oracle_prefill_rows.restype = ctypes.c_int
+    lib.oracle_decode.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, ctypes.c_float]
+    lib.oracle_decode.restype = ctypes.c_int
+    lib.oracle_decode_rows.argtypes = [p, p, p, p, p, i64, p, i64, i64, i64, i64, i64, ctypes.c_float]
+    lib.oracle_decode_rows.restype = ctypes.c_int
+    lib.oracle_scatter.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64]
+    lib.oracle_scatter.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load (building first if absent) the oracle library; ``path`` loads another copy."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+def _f32(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.float32:
+        raise TypeError(f"oracle inputs are the exact f32 values given to the GPU, got {a.dtype}")
+    return a
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+class Oracle:
+    """Thin numpy-facing wrapper over one loaded copy of the oracle library."""
+
+    def __init__(self, lib: ctypes.CDLL | None = None):
+        self.lib = lib if lib is not None else load()
+
+    def prefill(self, q, k, v, B, S, H, d, scale, causal):
+        """O[b, i, h*d:(h+1)*d] for every (b, i, h); q/k/v are [B, S, H*d] f32."""
+        q, k, v = _f32(q), _f32(k), _f32(v)
+        n = B * S * H * d
+        assert q.size == n and k.size == n and v.size == n
+        out = np.empty(n, dtype=np.float64)
+        rc = self.lib.oracle_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, H, d,
+                                     float(np.float32(scale)), int(bool(causal)))
+        if rc != 0:
+            raise ValueError("oracle_prefill rejected its arguments")
+        return out.reshape(B, S, H * d)
+
+    def prefill_rows(self, q, k, v, sel, B, S, H, d, scale, causal):
+        """Selected rows; ``sel`` is an (n, 3) int array of (b, i, h)."""
+        q, k, v = _f32(q), _f32(k), _f32(v)
+        sel = np.ascontiguousarray(sel, dtype=np.int64).reshape(-1, 3)
+        out = np.empty((sel.shape[0], d), dtype=np.float64)
+        rc = self.lib.oracle_prefill_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(sel), sel.shape[0],
+                                          _ptr(out), B, S, H, d, float(np.float32(scale)),
+                                          int(bool(causal)))
+        if rc != 0:
+            raise ValueError("oracle_prefill_rows rejected its arguments")
+        return out
+
+    def decode(self, q, k_cache, v_cache, lens, M, H, Hkv, d, max_len, scale):
+        """out[m, h*d:(h+1)*d]; q is [M, H*d], caches [M, Hkv, max_len, d]."""
+        q, k_cache, v_cache = _f32(q), _f32(k_cache), _f32(v_cache)
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        assert lens.size == M and q.size == M * H * d
+        assert k_cache.size == M * Hkv * max_len * d and v_cache.size == k_cache.size
+        out = np.empty(M * H * d, dtype=np.float64)
+        rc = self.lib.oracle_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens), _ptr(out),
+                                    M, H, Hkv, d, max_len, float(np.float32(scale)))
+        if rc != 0:
+            raise ValueError("oracle_decode rejected its arguments")
+        return out.reshape(M, H * d)
+
+    def decode_rows(self, q, k_cache, v_cache, lens, sel, M, H, Hkv, d, max_len, scale):
+        """Selected (m, h) outputs; ``sel`` is an (n, 2) int array."""
+        q, k_cache, v_cache = _f32(q), _f32(k_cache), _f32(v_cache)
+        lens = np.ascontiguousarray(lens, dtype=np.int32)
+        sel = np.ascontiguousarray(sel, dtype=np.int64).reshape(-1, 2)
+        out = np.empty((sel.shape[0], d), dtype=np.float64)
+        rc = self.lib.oracle_decode_rows(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens),
+                                         _ptr(sel), sel.shape[0], _ptr(out), M, H, Hkv, d,
+                                         max_len, float(np.float32(scale)))
+        if rc != 0:
+            raise ValueError("oracle_decode_rows rejected its arguments")
+        return out
+
+    def scatter(self, k_new, v_new, k_cache, v_cache, cache_lens, M, n_new, Hkv, d, max_len):
+        """In-place append into numpy caches (modified); returns them."""
+        k_new, v_new = _f32(k_new), _f32(v_new)
+        if not (k_cache.flags.c_contiguous and v_cache.flags.c_contiguous):
+            raise ValueError("caches must be C-contiguous (updated in place)")
+        cache_lens = np.ascontiguousarray(cache_lens, dtype=np.int32)
+        rc = self.lib.oracle_scatter(_ptr(k_new), _ptr(v_new), _ptr(_f32(k_cache)),
+                                     _ptr(_f32(v_cache)), _ptr(cache_lens), M, n_new, Hkv, d,
+                                     max_len)
+        if rc != 0:
+            raise ValueError("oracle_scatter rejected its arguments")
+        return k_cache, v_cache
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+
+_default: Oracle | None = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

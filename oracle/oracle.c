@@ -1,0 +1,244 @@
+/*
+ * oracle.c -- plain, slow, obviously-correct CPU reference for GPU-resident
+ * scaled-dot-product attention: full-sequence prefill (optionally causal),
+ * batched GQA decode against a preallocated KV cache, and the KV-cache append
+ * scatter.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: it is used by tests/, by the smoke check and by the bench's
+ * CPU-baseline leg.  It shares no code, header, table or helper with the HIP
+ * library, and it is written from the definitions, not from the GPU algorithm:
+ * no tiling, no online softmax, no split-KV.  Every score is formed, the full
+ * row is max-subtracted, exponentiated, summed, and the weighted sum of V is
+ * divided by that sum, all in double precision.  Inputs are the exact f32
+ * values handed to the GPU; scale is the same f32 value widened to double.
+ *
+ * Sources (page title, then section):
+ *  - trueno-gpu 0.4.11 src/memory/resident/attention.rs,
+ *    `batched_multihead_attention`: output = softmax(Q K^T / sqrt(d_k)) V over
+ *    interleaved [seq, n_heads * head_dim] activations, one head at a time.
+ *  - trustformers-core 0.2.0 src/gpu_ops/cuda/oxicuda/attention.rs,
+ *    `attention_prefill_gpu_to_gpu` (causal mask "from empty cache": query i
+ *    sees keys 0..=i), `softmax_causal_gpu_to_gpu` (masked cells are exactly
+ *    zero) and the test helper `prefill_reference` (max-subtracted softmax,
+ *    then (p / sum) * v).
+ *  - trueno-gpu ..., `incremental_attention_gpu`: one query token per head
+ *    against a head-first cache [heads, max_seq_len, head_dim]; an empty
+ *    sequence yields zeros.
+ *  - realizar 0.8.5 src/cuda/executor/cache_from_cache_from_kv_cache.rs,
+ *    `init_kv_cache_gpu` (GQA cache [num_kv_heads, max_len, head_dim],
+ *    num_kv_heads <= num_heads) and `init_batched_kv_cache_gpu` (batched cache
+ *    [M, num_kv_heads, max_len, head_dim], per-sequence stride
+ *    num_kv_heads * max_len * head_dim, 1 <= M <= 32).
+ *  - trueno-gpu ..., `kv_cache_scatter_gpu`: position pos of an interleaved
+ *    [n_heads * head_dim] row is written to cache[head, pos, :].
+ *
+ * Readings where the pages leave a step open (each is listed in the design
+ * notes): GQA query head h reads KV head h / (H / Hkv) (contiguous groups);
+ * prefill batch elements are independent with layout [B, S, H*d]; the decode
+ * length L_m counts the keys attended (rows 0..L_m-1), L_m == 0 gives zeros;
+ * scatter row r of sequence m lands at cache position cache_lens[m] + r.
+ *
+ * Build: gcc -O2 -fopenmp -fPIC -shared oracle.c -o liboracle.so -lm
+ * (no -ffast-math: the IEEE semantics of exp and of the sums are relied on).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* One attention row, written out from the definition.
+ * q: the query vector (d floats); keys/values: row j starts at
+ * kbase + j * kstride (resp. vbase + j * vstride); n keys are visible.
+ * out: d doubles.  scores: caller-provided scratch of n doubles. */
+static void attend_row(const float *q, const float *kbase, int64_t kstride,
+                       const float *vbase, int64_t vstride, int64_t n,
+                       int64_t d, double scale, double *scores, double *out)
+{
+    int64_t j, l;
+    double mu, z;
+    if (n == 0) {
+        for (l = 0; l < d; ++l) out[l] = 0.0;
+        return;
+    }
+    /* s_j = scale * sum_l q[l] * k_j[l] */
+    for (j = 0; j < n; ++j) {
+        const float *kj = kbase + j * kstride;
+        double dot = 0.0;
+        for (l = 0; l < d; ++l) dot += (double)q[l] * (double)kj[l];
+        scores[j] = scale * dot;
+    }
+    /* mu = max_j s_j ; e_j = exp(s_j - mu) ; Z = sum_j e_j */
+    mu = scores[0];
+    for (j = 1; j < n; ++j)
+        if (scores[j] > mu) mu = scores[j];
+    z = 0.0;
+    for (j = 0; j < n; ++j) {
+        scores[j] = exp(scores[j] - mu);
+        z += scores[j];
+    }
+    /* out[l] = (sum_j e_j * v_j[l]) / Z */
+    for (l = 0; l < d; ++l) {
+        double acc = 0.0;
+        for (j = 0; j < n; ++j) acc += scores[j] * (double)vbase[j * vstride + l];
+        out[l] = acc / z;
+    }
+}
+
+/* Full prefill.  q, k, v: [B, S, H*d] f32.  out: [B, S, H*d] f64.
+ * causal != 0: query i sees keys 0..i; otherwise all S keys.
+ * Returns 0, or -1 on a non-positive dimension / allocation failure. */
+int oracle_prefill(const float *q, const float *k, const float *v, double *out,
+                   int64_t B, int64_t S, int64_t H, int64_t d, float scale,
+                   int causal)
+{
+    int64_t unit, n_units;
+    int failed = 0;
+    if (B <= 0 || S <= 0 || H <= 0 || d <= 0) return -1;
+    n_units = B * H;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (unit = 0; unit < n_units; ++unit) {
+        int64_t b = unit / H, h = unit % H, i;
+        int64_t row = H * d; /* floats between consecutive tokens */
+        double *scores = (double *)malloc(sizeof(double) * (size_t)S);
+        if (!scores) { failed |= 1; continue; }
+        for (i = 0; i < S; ++i) {
+            const float *qi = q + (b * S + i) * row + h * d;
+            int64_t n = causal ? i + 1 : S;
+            attend_row(qi, k + b * S * row + h * d, row, v + b * S * row + h * d,
+                       row, n, d, (double)scale, scores,
+                       out + (b * S + i) * row + h * d);
+        }
+        free(scores);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Selected prefill rows.  sel: n_sel triples (b, i, h).  out: n_sel x d f64,
+ * row t holds O[b, i, h*d : (h+1)*d].  Same definition as oracle_prefill. */
+int oracle_prefill_rows(const float *q, const float *k, const float *v,
+                        const int64_t *sel, int64_t n_sel, double *out,
+                        int64_t B, int64_t S, int64_t H, int64_t d, float scale,
+                        int causal)
+{
+    int64_t t;
+    int failed = 0;
+    if (B <= 0 || S <= 0 || H <= 0 || d <= 0 || n_sel < 0) return -1;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (t = 0; t < n_sel; ++t) {
+        int64_t b = sel[3 * t], i = sel[3 * t + 1], h = sel[3 * t + 2];
+        int64_t row = H * d;
+        double *scores;
+        if (b < 0 || b >= B || i < 0 || i >= S || h < 0 || h >= H) { failed |= 1; continue; }
+        scores = (double *)malloc(sizeof(double) * (size_t)S);
+        if (!scores) { failed |= 1; continue; }
+        attend_row(q + (b * S + i) * row + h * d, k + b * S * row + h * d, row,
+                   v + b * S * row + h * d, row, causal ? i + 1 : S, d,
+                   (double)scale, scores, out + t * d);
+        free(scores);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Batched GQA decode.  q: [M, H*d] (one token per sequence).  k_cache,
+ * v_cache: [M, Hkv, max_len, d].  lens: M keys-attended counts, each in
+ * [0, max_len].  out: [M, H*d] f64.  Only rows j < lens[m] are read. */
+int oracle_decode(const float *q, const float *k_cache, const float *v_cache,
+                  const int32_t *lens, double *out, int64_t M, int64_t H,
+                  int64_t Hkv, int64_t d, int64_t max_len, float scale)
+{
+    int64_t unit, n_units, m;
+    int failed = 0;
+    if (M <= 0 || H <= 0 || Hkv <= 0 || d <= 0 || max_len <= 0) return -1;
+    if (H % Hkv != 0) return -1;
+    for (m = 0; m < M; ++m)
+        if (lens[m] < 0 || lens[m] > max_len) return -1;
+    n_units = M * H;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (unit = 0; unit < n_units; ++unit) {
+        int64_t mm = unit / H, h = unit % H;
+        int64_t group = H / Hkv;     /* query heads per KV head */
+        int64_t kh = h / group;      /* contiguous-group GQA map */
+        int64_t off = (mm * Hkv + kh) * max_len * d;
+        double *scores = (double *)malloc(sizeof(double) * (size_t)max_len);
+        if (!scores) { failed |= 1; continue; }
+        attend_row(q + mm * H * d + h * d, k_cache + off, d, v_cache + off, d,
+                   lens[mm], d, (double)scale, scores, out + mm * H * d + h * d);
+        free(scores);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Selected decode outputs.  sel: n_sel pairs (m, h); out: n_sel x d f64. */
+int oracle_decode_rows(const float *q, const float *k_cache, const float *v_cache,
+                       const int32_t *lens, const int64_t *sel, int64_t n_sel,
+                       double *out, int64_t M, int64_t H, int64_t Hkv, int64_t d,
+                       int64_t max_len, float scale)
+{
+    int64_t t;
+    int failed = 0;
+    if (M <= 0 || H <= 0 || Hkv <= 0 || d <= 0 || max_len <= 0 || n_sel < 0) return -1;
+    if (H % Hkv != 0) return -1;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (t = 0; t < n_sel; ++t) {
+        int64_t mm = sel[2 * t], h = sel[2 * t + 1];
+        int64_t kh, off;
+        double *scores;
+        if (mm < 0 || mm >= M || h < 0 || h >= H) { failed |= 1; continue; }
+        if (lens[mm] < 0 || lens[mm] > max_len) { failed |= 1; continue; }
+        kh = h / (H / Hkv);
+        off = (mm * Hkv + kh) * max_len * d;
+        scores = (double *)malloc(sizeof(double) * (size_t)max_len);
+        if (!scores) { failed |= 1; continue; }
+        attend_row(q + mm * H * d + h * d, k_cache + off, d, v_cache + off, d,
+                   lens[mm], d, (double)scale, scores, out + t * d);
+        free(scores);
+    }
+    return failed ? -1 : 0;
+}
+
+/* KV-cache append.  k_new, v_new: [M, n_new, Hkv*d] interleaved rows.
+ * k_cache, v_cache: [M, Hkv, max_len, d].  Row r of sequence m, KV head kh,
+ * is copied bit for bit to cache position cache_lens[m] + r.  Every other
+ * cache element is left as it was.  Returns -1 (and writes nothing) when a
+ * write would fall outside [0, max_len). */
+int oracle_scatter(const float *k_new, const float *v_new, float *k_cache,
+                   float *v_cache, const int32_t *cache_lens, int64_t M,
+                   int64_t n_new, int64_t Hkv, int64_t d, int64_t max_len)
+{
+    int64_t m, r, kh, l;
+    if (M <= 0 || n_new <= 0 || Hkv <= 0 || d <= 0 || max_len <= 0) return -1;
+    for (m = 0; m < M; ++m)
+        if (cache_lens[m] < 0 || (int64_t)cache_lens[m] + n_new > max_len) return -1;
+    for (m = 0; m < M; ++m)
+        for (r = 0; r < n_new; ++r)
+            for (kh = 0; kh < Hkv; ++kh) {
+                int64_t src = (m * n_new + r) * Hkv * d + kh * d;
+                int64_t dst = ((m * Hkv + kh) * max_len + cache_lens[m] + r) * d;
+                for (l = 0; l < d; ++l) {
+                    uint32_t bits;
+                    memcpy(&bits, &k_new[src + l], 4);
+                    memcpy(&k_cache[dst + l], &bits, 4);
+                    memcpy(&bits, &v_new[src + l], 4);
+                    memcpy(&v_cache[dst + l], &bits, 4);
+                }
+            }
+    return 0;
+}
+
+/* Number of OpenMP threads a parallel region would use (for reporting). */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        {
+#ifdef _OPENMP
+            extern int omp_get_num_threads(void);
+            n = omp_get_num_threads();
+#endif
+        }
+    }
+    return n;
+}

@@ -1,0 +1,431 @@
+"""Pins that tie the CPU oracle to facts fixed by the pages and by mathematics.
+
+Each pin takes an ``oracle.Oracle`` (so the same checks can be re-run against
+deliberately broken copies of the oracle, see test_oracle_mutants.py) and
+raises AssertionError when the oracle disagrees with:
+
+* closed forms (one-hot selection, uniform/prefix means, two-key softmax),
+* invariants (rows of a softmax sum to one, linearity in V, permutation
+  invariance, reads only the first L_m cache rows),
+* relations the pages state (decode equals the last row of a causal prefill
+  -- trustformers-core 0.2.0 src/gpu_ops/cuda/oxicuda/attention.rs,
+  gpu_tests ``oxicuda_resident_decode_attention_parity``; an empty sequence
+  gives zeros -- trueno-gpu 0.4.11 src/memory/resident/attention.rs,
+  ``incremental_attention_gpu``),
+* printed offsets (tests/golden/), and
+* an independent numpy fp64 brute force on every tiny shape.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+import zlib
+
+import numpy as np
+
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _scale(d):
+    return float(np.float32(1.0) / np.sqrt(np.float32(d)))
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite output"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+def _rng(tag):
+    return np.random.default_rng(zlib.crc32(tag.encode()))
+
+
+def _build_cache_by_scatter(orc, k_rows, v_rows, Hkv, d, max_len, fill):
+    """[1, S, Hkv*d] rows appended one position at a time into a [1, Hkv, max_len, d] cache."""
+    S = k_rows.shape[1]
+    kc = np.full((1, Hkv, max_len, d), fill, dtype=np.float32)
+    vc = np.full((1, Hkv, max_len, d), fill, dtype=np.float32)
+    for t in range(S):
+        orc.scatter(np.ascontiguousarray(k_rows[:, t:t + 1]), np.ascontiguousarray(v_rows[:, t:t + 1]),
+                    kc, vc, np.array([t], np.int32), 1, 1, Hkv, d, max_len)
+    return kc, vc
+
+
+# --------------------------------------------------------------------------- prefill
+
+
+def pin_rows_sum_to_one(orc):
+    """V = 1 everywhere gives O = sum_j p_j = 1 (softmax rows sum to one)."""
+    r = _rng("rowsum")
+    for causal in (False, True):
+        B, S, H, d = 2, 7, 3, 5
+        q = r.standard_normal((B, S, H * d)).astype(np.float32) * 3
+        k = r.standard_normal((B, S, H * d)).astype(np.float32) * 3
+        v = np.ones((B, S, H * d), np.float32)
+        _close(orc.prefill(q, k, v, B, S, H, d, _scale(d), causal), v, 1e-12, f"row sum causal={causal}")
+    M, H, Hkv, d, max_len = 3, 4, 2, 4, 9
+    q = r.standard_normal((M, H * d)).astype(np.float32)
+    kc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    vc = np.ones_like(kc)
+    lens = np.array([1, 5, 9], np.int32)
+    _close(orc.decode(q, kc, vc, lens, M, H, Hkv, d, max_len, _scale(d)), np.ones((M, H * d)), 1e-12,
+           "decode row sum")
+
+
+def _onehot_case(c_times_scale, causal):
+    """Key j* = e_0, all other keys 0, every query c*e_0: scores c*scale at j*, 0 elsewhere."""
+    B, S, H, d = 1, 6, 2, 4
+    jstar = 3
+    scale = _scale(d)
+    c = np.float32(c_times_scale / scale)
+    q = np.zeros((B, S, H, d), np.float32)
+    q[..., 0] = c
+    k = np.zeros((B, S, H, d), np.float32)
+    k[:, jstar, :, 0] = 1.0
+    v = _rng("onehot-v").standard_normal((B, S, H, d)).astype(np.float32)
+    return B, S, H, d, jstar, scale, q.reshape(B, S, H * d), k.reshape(B, S, H * d), v
+
+
+def pin_one_hot_selects_row(orc):
+    """A dominant score reproduces the selected V row (error ~ S*e^-200)."""
+    for causal in (False, True):
+        B, S, H, d, jstar, scale, q, k, v = _onehot_case(200.0, causal)
+        o = orc.prefill(q, k, v, B, S, H, d, scale, causal).reshape(B, S, H, d)
+        v4 = v.reshape(B, S, H, d)
+        for i in range(S):
+            if causal and i < jstar:
+                # Row i does not see j*: every visible score is 0 -> prefix mean.
+                want = v4[0, : i + 1].astype(np.float64).mean(axis=0)
+            else:
+                want = v4[0, jstar]
+            _close(o[0, i], want, 1e-12, f"one-hot row {i} causal={causal}")
+
+
+def pin_large_logits_stay_finite(orc):
+    """Scores of 1000 overflow exp() in double unless the row max is subtracted first."""
+    for causal in (False, True):
+        B, S, H, d, jstar, scale, q, k, v = _onehot_case(1000.0, causal)
+        o = orc.prefill(q, k, v, B, S, H, d, scale, causal).reshape(B, S, H, d)
+        v4 = v.reshape(B, S, H, d)
+        _close(o[0, S - 1], v4[0, jstar], 1e-12, f"large logits causal={causal}")
+
+
+def pin_uniform_prefix_mean(orc):
+    """q = 0: all visible scores equal -> mean of visible V rows (prefix mean when causal)."""
+    r = _rng("uniform")
+    B, S, H, d = 2, 9, 3, 4
+    q = np.zeros((B, S, H * d), np.float32)
+    k = r.standard_normal((B, S, H * d)).astype(np.float32)
+    v = r.standard_normal((B, S, H * d)).astype(np.float32)
+    v64 = v.astype(np.float64)
+    o = orc.prefill(q, k, v, B, S, H, d, _scale(d), False)
+    _close(o, np.broadcast_to(v64.mean(axis=1, keepdims=True), o.shape), 1e-12, "uniform non-causal")
+    o = orc.prefill(q, k, v, B, S, H, d, _scale(d), True)
+    prefix = np.cumsum(v64, axis=1) / np.arange(1, S + 1)[None, :, None]
+    _close(o, prefix, 1e-12, "uniform causal prefix mean")
+
+
+def pin_two_key_closed_form(orc):
+    """d = 1, S = 2, causal: o_0 = v_0; o_1 = sigmoid(s11 - s10) v_1 + sigmoid(s10 - s11) v_0."""
+    q = np.array([[[0.7], [-1.3]]], np.float32)
+    k = np.array([[[0.4], [1.9]]], np.float32)
+    v = np.array([[[2.5], [-0.75]]], np.float32)
+    scale = np.float32(0.8)
+    o = orc.prefill(q, k, v, 1, 2, 1, 1, float(scale), True)
+    s10 = float(scale) * float(q[0, 1, 0]) * float(k[0, 0, 0])
+    s11 = float(scale) * float(q[0, 1, 0]) * float(k[0, 1, 0])
+    sig = lambda x: 1.0 / (1.0 + math.exp(-x))
+    want1 = sig(s11 - s10) * float(v[0, 1, 0]) + sig(s10 - s11) * float(v[0, 0, 0])
+    _close(o[0, 0, 0], float(v[0, 0, 0]), 1e-15, "two-key row 0")
+    _close(o[0, 1, 0], want1, 1e-14, "two-key row 1")
+    # Non-causal: row 0 now also sees key 1.
+    o = orc.prefill(q, k, v, 1, 2, 1, 1, float(scale), False)
+    s00 = float(scale) * float(q[0, 0, 0]) * float(k[0, 0, 0])
+    s01 = float(scale) * float(q[0, 0, 0]) * float(k[0, 1, 0])
+    want0 = sig(s01 - s00) * float(v[0, 1, 0]) + sig(s00 - s01) * float(v[0, 0, 0])
+    _close(o[0, 0, 0], want0, 1e-14, "two-key non-causal row 0")
+
+
+def pin_linear_in_v(orc):
+    """O(Q, K, a V + b W) = a O(Q, K, V) + b O(Q, K, W); constant V rows give that constant."""
+    r = _rng("linear")
+    B, S, H, d = 1, 8, 2, 6
+    q, k, v, w = (r.standard_normal((B, S, H * d)).astype(np.float32) for _ in range(4))
+    # Disjoint column supports and power-of-two weights keep a*v + b*w exact in f32.
+    v[..., 1::2] = 0.0
+    w[..., 0::2] = 0.0
+    a, b = np.float32(0.5), np.float32(-2.0)
+    for causal in (False, True):
+        lhs = orc.prefill(q, k, (a * v + b * w).astype(np.float32), B, S, H, d, _scale(d), causal)
+        rhs = float(a) * orc.prefill(q, k, v, B, S, H, d, _scale(d), causal) + \
+            float(b) * orc.prefill(q, k, w, B, S, H, d, _scale(d), causal)
+        _close(lhs, rhs, 1e-12, f"linearity causal={causal}")
+        const = np.full((B, S, H * d), 3.25, np.float32)
+        _close(orc.prefill(q, k, const, B, S, H, d, _scale(d), causal), const, 1e-12, "constant V")
+
+
+def pin_permutation(orc):
+    """Non-causal: jointly permuting K and V rows changes nothing; permuting Q permutes O."""
+    r = _rng("perm")
+    B, S, H, d = 1, 10, 2, 4
+    q, k, v = (r.standard_normal((B, S, H * d)).astype(np.float32) for _ in range(3))
+    perm = r.permutation(S)
+    o = orc.prefill(q, k, v, B, S, H, d, _scale(d), False)
+    _close(orc.prefill(q, k[:, perm], v[:, perm], B, S, H, d, _scale(d), False), o, 1e-12,
+           "joint K/V permutation")
+    _close(orc.prefill(q[:, perm], k, v, B, S, H, d, _scale(d), False), o[:, perm], 1e-12,
+           "query permutation")
+
+
+def pin_heads_and_batches_independent(orc):
+    """Each (b, h) output depends only on that batch element's head-h columns."""
+    r = _rng("indep")
+    B, S, H, d = 2, 5, 3, 4
+    q, k, v = (r.standard_normal((B, S, H * d)).astype(np.float32) for _ in range(3))
+    o = orc.prefill(q, k, v, B, S, H, d, _scale(d), True)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    # Perturb head 1 of batch 0 only.
+    for t in (q2, k2, v2):
+        t[0, :, d:2 * d] += 1.0
+    o2 = orc.prefill(q2, k2, v2, B, S, H, d, _scale(d), True)
+    mask = np.ones((B, S, H * d), bool)
+    mask[0, :, d:2 * d] = False
+    _close(o2[mask], o[mask], 0.0, "untouched heads unchanged")
+    assert np.max(np.abs(o2[0, :, d:2 * d] - o[0, :, d:2 * d])) > 1e-3, "perturbed head must change"
+
+
+def pin_prefill_rows_match(orc):
+    """The sampled-row entry point equals the full computation at those rows."""
+    r = _rng("rows")
+    B, S, H, d = 2, 11, 3, 4
+    q, k, v = (r.standard_normal((B, S, H * d)).astype(np.float32) for _ in range(3))
+    for causal in (False, True):
+        full = orc.prefill(q, k, v, B, S, H, d, _scale(d), causal)
+        sel = np.array([[0, 0, 0], [1, 10, 2], [0, 5, 1], [1, 3, 0]], np.int64)
+        rows = orc.prefill_rows(q, k, v, sel, B, S, H, d, _scale(d), causal)
+        want = np.stack([full[b, i, h * d:(h + 1) * d] for b, i, h in sel])
+        _close(rows, want, 0.0, f"prefill_rows causal={causal}")
+
+
+# --------------------------------------------------------------------------- decode
+
+
+def pin_decode_equals_causal_prefill_row(orc):
+    """Decode at step t over a cache filled by appends equals row t of a causal prefill."""
+    r = _rng("dec=pre")
+    S, H, d, max_len = 6, 3, 4, 8
+    q, k, v = (r.standard_normal((1, S, H * d)).astype(np.float32) for _ in range(3))
+    pre = orc.prefill(q, k, v, 1, S, H, d, _scale(d), True)
+    kc, vc = _build_cache_by_scatter(orc, k, v, H, d, max_len, np.nan)
+    for t in range(S):
+        # Cache holds rows 0..S-1; attending over L = t+1 reads rows 0..t only.
+        out = orc.decode(np.ascontiguousarray(q[:, t]), kc, vc, np.array([t + 1], np.int32),
+                         1, H, H, d, max_len, _scale(d))
+        _close(out[0], pre[0, t], 1e-12, f"decode step {t}")
+
+
+def pin_gqa_head_map(orc):
+    """Query head h reads KV head floor(h / (H/Hkv)): V rows of KV head kh hold kh+1."""
+    r = _rng("gqa-map")
+    M, H, Hkv, d, max_len = 2, 8, 2, 4, 5
+    q = r.standard_normal((M, H * d)).astype(np.float32)
+    kc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    vc = np.zeros_like(kc)
+    for kh in range(Hkv):
+        vc[:, kh] = kh + 1
+    out = orc.decode(q, kc, vc, np.array([5, 3], np.int32), M, H, Hkv, d, max_len, _scale(d))
+    g = H // Hkv
+    want = np.repeat((np.arange(H) // g + 1).astype(np.float64), d)[None].repeat(M, axis=0)
+    _close(out, want, 1e-12, "GQA head map")
+
+
+def pin_gqa_equals_mha_on_repeated_cache(orc):
+    """GQA over Hkv heads equals MHA (Hkv = H) over a cache with each KV head repeated g times."""
+    r = _rng("gqa=mha")
+    M, H, Hkv, d, max_len = 3, 6, 2, 4, 7
+    q = r.standard_normal((M, H * d)).astype(np.float32)
+    kc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    vc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    lens = np.array([7, 1, 4], np.int32)
+    g = H // Hkv
+    gqa = orc.decode(q, kc, vc, lens, M, H, Hkv, d, max_len, _scale(d))
+    mha = orc.decode(q, np.ascontiguousarray(np.repeat(kc, g, axis=1)),
+                     np.ascontiguousarray(np.repeat(vc, g, axis=1)), lens, M, H, H, d, max_len, _scale(d))
+    _close(gqa, mha, 0.0, "GQA vs repeated-cache MHA")
+
+
+def pin_decode_reads_only_live_rows(orc):
+    """Rows at positions >= L_m (NaN / 1e30 here) and other sequences never reach out[m]."""
+    r = _rng("live")
+    M, H, Hkv, d, max_len = 3, 4, 2, 4, 10
+    q = r.standard_normal((M, H * d)).astype(np.float32)
+    kc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    vc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    lens = np.array([4, 10, 1], np.int32)
+    base = orc.decode(q, kc, vc, lens, M, H, Hkv, d, max_len, _scale(d))
+    for fill in (np.nan, 1e30):
+        kc2, vc2 = kc.copy(), vc.copy()
+        for m in range(M):
+            kc2[m, :, lens[m]:] = fill
+            vc2[m, :, lens[m]:] = fill
+        _close(orc.decode(q, kc2, vc2, lens, M, H, Hkv, d, max_len, _scale(d)), base, 0.0,
+               f"rows beyond L filled with {fill}")
+    kc3 = kc.copy()
+    kc3[1] += 5.0
+    o3 = orc.decode(q, kc3, vc, lens, M, H, Hkv, d, max_len, _scale(d))
+    _close(o3[[0, 2]], base[[0, 2]], 0.0, "other sequences unchanged")
+
+
+def pin_empty_sequence_gives_zeros(orc):
+    """L_m = 0 yields zeros for that sequence only."""
+    r = _rng("empty")
+    M, H, Hkv, d, max_len = 2, 2, 1, 4, 3
+    q = r.standard_normal((M, H * d)).astype(np.float32)
+    kc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    vc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    out = orc.decode(q, kc, vc, np.array([0, 2], np.int32), M, H, Hkv, d, max_len, _scale(d))
+    _close(out[0], np.zeros(H * d), 0.0, "empty sequence")
+    assert np.max(np.abs(out[1])) > 0
+
+
+def pin_decode_rows_match(orc):
+    r = _rng("decrows")
+    M, H, Hkv, d, max_len = 3, 8, 4, 4, 6
+    q = r.standard_normal((M, H * d)).astype(np.float32)
+    kc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    vc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    lens = np.array([6, 0, 3], np.int32)
+    full = orc.decode(q, kc, vc, lens, M, H, Hkv, d, max_len, _scale(d))
+    sel = np.array([[0, 7], [1, 0], [2, 3], [2, 4]], np.int64)
+    rows = orc.decode_rows(q, kc, vc, lens, sel, M, H, Hkv, d, max_len, _scale(d))
+    _close(rows, np.stack([full[m, h * d:(h + 1) * d] for m, h in sel]), 0.0, "decode_rows")
+
+
+# --------------------------------------------------------------------------- brute force
+
+
+def pin_brute_force_tiny_shapes(orc):
+    """C oracle == independent numpy fp64 on every S<=5, d<=4, H<=4, Hkv | H."""
+    r = _rng("brute")
+    for S, d, H in itertools.product(range(1, 6), range(1, 5), range(1, 5)):
+        B = 2
+        q, k, v = (r.standard_normal((B, S, H * d)).astype(np.float32) * 2 for _ in range(3))
+        for causal in (False, True):
+            _close(orc.prefill(q, k, v, B, S, H, d, _scale(d), causal),
+                   brute.prefill(q, k, v, B, S, H, d, _scale(d), causal), 1e-12,
+                   f"brute prefill S={S} d={d} H={H} causal={causal}")
+        for Hkv in [x for x in range(1, H + 1) if H % x == 0]:
+            M, max_len = 3, 5
+            qd = r.standard_normal((M, H * d)).astype(np.float32) * 2
+            kc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+            vc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+            lens = r.integers(0, max_len + 1, size=M).astype(np.int32)
+            _close(orc.decode(qd, kc, vc, lens, M, H, Hkv, d, max_len, _scale(d)),
+                   brute.decode(qd, kc, vc, lens, M, H, Hkv, d, max_len, _scale(d)), 1e-12,
+                   f"brute decode H={H} Hkv={Hkv} d={d}")
+
+
+def pin_pages_inputs_brute(orc):
+    """The pages' deterministic test inputs (sin/cos/linear ramps) agree with the brute force.
+
+    trustformers-core 0.2.0 ..., gpu_tests: prefill q = sin(0.37 i), k = cos(0.53 i),
+    v = 0.25 i - 1 with H=2, seq=3, d=2; decode q = sin(0.41 i), k = cos(0.29 i),
+    v = 1.5 - 0.2 i.  The page prints no expected values, so these are cross-checks
+    against the independent formulation only (heads-major [H, seq, d] there, so the
+    arrays are re-laid out to interleaved [seq, H*d] here).
+    """
+    H, S, d = 2, 3, 2
+    i = np.arange(H * S * d, dtype=np.float32)
+    def interleave(x):
+        return np.ascontiguousarray(x.reshape(H, S, d).transpose(1, 0, 2).reshape(1, S, H * d))
+    for qf, kf, vf in [(np.sin(i * np.float32(0.37)), np.cos(i * np.float32(0.53)), i * np.float32(0.25) - 1),
+                       (np.sin(i * np.float32(0.41)), np.cos(i * np.float32(0.29)), np.float32(1.5) - i * np.float32(0.2))]:
+        q, k, v = (interleave(x.astype(np.float32)) for x in (qf, kf, vf))
+        _close(orc.prefill(q, k, v, 1, S, H, d, _scale(d), True),
+               brute.prefill(q, k, v, 1, S, H, d, _scale(d), True), 1e-13, "pages' inputs")
+
+
+# --------------------------------------------------------------------------- scatter
+
+
+def pin_scatter_printed_offsets(orc):
+    """Append offsets printed on the page (tests/golden/kv_append_offsets.json)."""
+    g = json.load(open(os.path.join(GOLDEN, "kv_append_offsets.json")))
+    Hkv, kv_old, kv_new, d = g["num_heads"], g["kv_old"], g["kv_new"], g["head_dim"]
+    max_len = kv_old + kv_new
+    # Old rows first (positions 0..kv_old-1), marked with 1000 + source index.
+    old = (1000 + np.arange(kv_old * Hkv * d, dtype=np.float32)).reshape(1, kv_old, Hkv * d)
+    new = np.arange(kv_new * Hkv * d, dtype=np.float32).reshape(1, kv_new, Hkv * d)
+    kc = np.full((1, Hkv, max_len, d), -1.0, np.float32)
+    vc = kc.copy()
+    orc.scatter(old, old, kc, vc, np.array([0], np.int32), 1, kv_old, Hkv, d, max_len)
+    orc.scatter(new, new, kc, vc, np.array([kv_old], np.int32), 1, kv_new, Hkv, d, max_len)
+    flat = kc.reshape(-1)
+    for h, (src, dst) in enumerate(g["new_src_dst"]):
+        assert np.array_equal(flat[dst:dst + d], new.reshape(-1)[src:src + d]), f"new row head {h}"
+    for h, (_, dst) in enumerate(g["old_src_dst"]):
+        # Old row 0 of head h sits at the printed destination.
+        assert np.array_equal(flat[dst:dst + d], old[0, 0, h * d:(h + 1) * d]), f"old row head {h}"
+    assert not np.any(flat == -1.0), "every position of the appended cache is written"
+    assert np.array_equal(kc, vc)
+
+
+def pin_scatter_layout_offsets(orc):
+    """Slot stride and head-0 position offsets (tests/golden/kv_cache_layout.json)."""
+    g = json.load(open(os.path.join(GOLDEN, "kv_cache_layout.json")))
+    for c in g["cases"]:
+        Hkv, max_len, d, slot, head, pos = (c[x] for x in ("num_kv_heads", "max_len", "head_dim", "slot", "head", "pos"))
+        M = slot + 1
+        src = np.zeros((M, 1, Hkv * d), np.float32)
+        marker = np.arange(1, d + 1, dtype=np.float32)
+        src[slot, 0, head * d:(head + 1) * d] = marker
+        kc = np.zeros((M, Hkv, max_len, d), np.float32)
+        vc = kc.copy()
+        lens = np.zeros(M, np.int32)
+        lens[slot] = pos
+        orc.scatter(src, src, kc, vc, lens, M, 1, Hkv, d, max_len)
+        flat = kc.reshape(-1)
+        assert np.array_equal(flat[c["offset"]:c["offset"] + d], marker), f"case {c}"
+        assert np.count_nonzero(flat) == d
+
+
+def pin_scatter_matches_fancy_index(orc):
+    """Bit-exact agreement with a numpy fancy-index append; untouched sentinel bytes stay."""
+    r = _rng("scatter")
+    for M, n_new, Hkv, d, max_len in [(3, 4, 2, 8, 9), (1, 1, 1, 4, 1), (4, 2, 3, 4, 6)]:
+        kn = r.standard_normal((M, n_new, Hkv * d)).astype(np.float32)
+        vn = r.standard_normal((M, n_new, Hkv * d)).astype(np.float32)
+        kn.view(np.uint32)[0, 0, 0] = 0x7FA00001  # a NaN payload must survive bit for bit
+        lens = r.integers(0, max_len - n_new + 1, size=M).astype(np.int32)
+        sent = np.full((M, Hkv, max_len, d), 0x7FC0DEAD, np.uint32).view(np.float32)
+        kc, vc = sent.copy(), sent.copy()
+        orc.scatter(kn, vn, kc, vc, lens, M, n_new, Hkv, d, max_len)
+        bk, bv = brute.scatter(kn, vn, sent, sent, lens, M, n_new, Hkv, d, max_len)
+        assert np.array_equal(kc.view(np.uint32), bk.reshape(kc.shape).view(np.uint32))
+        assert np.array_equal(vc.view(np.uint32), bv.reshape(vc.shape).view(np.uint32))
+        written = M * n_new * Hkv * d
+        assert np.count_nonzero(kc.view(np.uint32) != 0x7FC0DEAD) == written
+
+
+def pin_scatter_rejects_overflow(orc):
+    """A write at or past max_len is refused and leaves the caches untouched."""
+    kn = np.ones((1, 2, 4), np.float32)
+    kc = np.zeros((1, 1, 3, 4), np.float32)
+    vc = kc.copy()
+    try:
+        orc.scatter(kn, kn, kc, vc, np.array([2], np.int32), 1, 2, 1, 4, 3)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("append past max_len accepted")
+    assert not kc.any() and not vc.any()
+
+
+ALL_PINS = [(name, fn) for name, fn in sorted(globals().items()) if name.startswith("pin_")]

@@ -1,0 +1,85 @@
+"""The pins are strong enough: every plausible slip planted in a copy of the oracle fails one.
+
+Each mutant is a one-place textual change to oracle/oracle.c, compiled on the
+CPU into a temporary library; the pin suite from oracle_pins.py is run against
+it and at least one pin must fail.  Nothing here touches a GPU.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.c")
+
+# (id, exact text in oracle.c, replacement) -- each a mistake one could plausibly make.
+MUTANTS = [
+    ("no_max_subtraction", "scores[j] = exp(scores[j] - mu);", "scores[j] = exp(scores[j]);"),
+    ("min_instead_of_max", "if (scores[j] > mu) mu = scores[j];", "if (scores[j] < mu) mu = scores[j];"),
+    ("sign_flip_exp", "scores[j] = exp(scores[j] - mu);", "scores[j] = exp(mu - scores[j]);"),
+    ("dropped_scale", "scores[j] = scale * dot;", "scores[j] = dot;"),
+    ("dropped_normalisation", "out[l] = acc / z;", "out[l] = acc;"),
+    ("v_index_ignores_column", "vbase[j * vstride + l]", "vbase[j * vstride]"),
+    ("k_used_as_q", "const float *qi = q + (b * S + i) * row + h * d;",
+     "const float *qi = k + (b * S + i) * row + h * d;"),
+    ("causal_excludes_diagonal", "int64_t n = causal ? i + 1 : S;", "int64_t n = causal ? i : S;"),
+    ("causal_sees_next", "int64_t n = causal ? i + 1 : S;", "int64_t n = causal ? (i + 2 < S ? i + 2 : S) : S;"),
+    ("head_offset_dropped_in_q", "const float *qi = q + (b * S + i) * row + h * d;",
+     "const float *qi = q + (b * S + i) * row;"),
+    ("token_stride_is_d", "attend_row(qi, k + b * S * row + h * d, row, v + b * S * row + h * d,\n                       row,",
+     "attend_row(qi, k + b * S * row + h * d, d, v + b * S * row + h * d,\n                       d,"),
+    ("gqa_modulo_map", "int64_t kh = h / group;", "int64_t kh = h % Hkv;"),
+    ("decode_reads_max_len", "lens[mm], d, (double)scale, scores, out + mm * H * d + h * d);",
+     "max_len, d, (double)scale, scores, out + mm * H * d + h * d);"),
+    ("decode_one_short", "lens[mm], d, (double)scale, scores, out + mm * H * d + h * d);",
+     "lens[mm] > 0 ? lens[mm] - 1 : 0, d, (double)scale, scores, out + mm * H * d + h * d);"),
+    ("scatter_ignores_cache_len", "cache_lens[m] + r) * d;", "r) * d;"),
+    ("scatter_rows_reversed", "cache_lens[m] + r) * d;", "cache_lens[m] + (n_new - 1 - r)) * d;"),
+    ("scatter_head_major_swap", "int64_t dst = ((m * Hkv + kh) * max_len", "int64_t dst = ((kh * M + m) * max_len"),
+    ("scatter_src_heads_major", "int64_t src = (m * n_new + r) * Hkv * d + kh * d;",
+     "int64_t src = (m * Hkv + kh) * n_new * d + r * d;"),
+    ("scatter_v_from_k", "memcpy(&bits, &v_new[src + l], 4);", "memcpy(&bits, &k_new[src + l], 4);"),
+    ("empty_sequence_not_zero", "for (l = 0; l < d; ++l) out[l] = 0.0;", "for (l = 0; l < d; ++l) out[l] = 1.0;"),
+    ("rows_entry_ignores_causal", "row, causal ? i + 1 : S, d,", "row, S, d,"),
+]
+
+
+_RUNNER = """
+import json, sys
+sys.path[:0] = [{root!r}, {tests!r}]
+import oracle
+from oracle_pins import ALL_PINS
+orc = oracle.Oracle(oracle.load({lib!r}))
+failed = []
+for name, pin in ALL_PINS:
+    try:
+        pin(orc)
+    except (AssertionError, ValueError, FloatingPointError):
+        failed.append(name)
+print(json.dumps(failed))
+"""
+
+
+def _failing_pins(lib_path):
+    """Run every pin against one mutant in a fresh process (a mutant may corrupt memory)."""
+    tests = os.path.dirname(os.path.abspath(__file__))
+    code = _RUNNER.format(root=os.path.dirname(tests), tests=tests, lib=lib_path)
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, f"pin run crashed: {res.stderr[-2000:]}"
+    return json.loads(res.stdout.strip().splitlines()[-1])
+
+
+@pytest.mark.parametrize("mid,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(mid, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {mid} must be unique in oracle.c"
+    mutated = tmp_path / f"oracle_{mid}.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / f"liboracle_{mid}.so"
+    oracle.build(str(mutated), str(lib))
+    failed = _failing_pins(str(lib))
+    assert failed, f"mutant {mid} passed every pin"
