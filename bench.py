@@ -1,0 +1,222 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic inputs:
+
+  1. causal prefill, B=4, S=2048, H=32, d=128 (attn_prefill);
+  2. bulk KV append of that prefill's K/V into a [4, 32, 4096, 128] cache
+     from position 0 (kv_cache_scatter);
+  3. long-context GQA decode step, M=16, H=64, Hkv=8, d=128,
+     max_len=32768, L_m ~ U{16384..32768}: append each sequence's new K/V row
+     at L_m - 1 (kv_cache_scatter), then attend over L_m keys
+     (attn_decode_gqa_batched: split pass + merge pass).
+
+Inputs are resident in HBM before the timed region.  Every call is bracketed
+by HIP events on the stream it is launched on (torch's current stream, which
+the binding passes to the library), so each kernel's average duration is
+measured live over the timed steps.  ``value`` is the decode's algorithmic
+HBM throughput (K/V rows 0..L_m-1 of every KV head read once, q read, out
+written) over the decode's measured time; the prefill's algorithmic TFLOP/s
+(visible query/key pairs only) is reported next to it and, being the longest
+kernel of the step, in the ``roofline`` object.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+METRIC = "decode attn HBM GB/s (% peak) + prefill TFLOP/s (% fp32 MFMA peak), 1 GPU"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, cfg, target_s):
+    """The oracle's decode over whole sequences of the same workload, on the host cores."""
+    import oracle
+
+    orc = oracle.default()
+    M1 = 1
+    t0 = time.perf_counter()
+    orc.decode(inp["q"][:M1], inp["k_cache"][:M1], inp["v_cache"][:M1], inp["lens"][:M1], M1, cfg.H,
+               cfg.Hkv, cfg.d, cfg.max_len, cfg.scale)
+    t_one = time.perf_counter() - t0
+    n = int(min(cfg.M, max(1, np.ceil(target_s / max(t_one, 1e-3)))))
+    if n > 1:
+        t0 = time.perf_counter()
+        orc.decode(inp["q"][:n], inp["k_cache"][:n], inp["v_cache"][:n], inp["lens"][:n], n, cfg.H,
+                   cfg.Hkv, cfg.d, cfg.max_len, cfg.scale)
+        t = time.perf_counter() - t0
+    else:
+        t = t_one
+    lens = inp["lens"][:n]
+    nbytes = 2 * cfg.Hkv * cfg.d * 4 * int(lens.sum()) + 2 * n * cfg.H * cfg.d * 4
+    return {
+        "value": round(nbytes / t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": orc.num_threads(),
+        "kind": "oracle",
+        "sample": f"fp64 oracle decode of the first {n} of {cfg.M} sequences (all {cfg.H} heads, "
+                  f"sum L = {int(lens.sum())} keys) of the same workload, {t:.1f} s wall",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import transformer_attention_flash_amd as taf
+    from transformer_attention_flash_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    taf.library()  # fail loudly before any setup if the HIP library is missing
+
+    pcfg, scfg, dcfg = wl.PREFILL[3], wl.BULK_SCATTER, wl.DECODE[5]
+
+    log("generating inputs ...")
+    q, k, v = wl.prefill_inputs(pcfg)
+    dinp = wl.decode_inputs(dcfg)
+    lens = dinp["lens"]
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    pq, pk, pv = up(q), up(k), up(v)
+    pout = torch.empty_like(pq)
+    cache_shape = (scfg.M, scfg.Hkv, scfg.max_len, scfg.d)
+    bk = torch.from_numpy(wl.sentinel_cache(cache_shape)).to(dev)
+    bv = torch.from_numpy(wl.sentinel_cache(cache_shape)).to(dev)
+    dq, dkn, dvn = up(dinp["q"]), up(dinp["k_new"]), up(dinp["v_new"])
+    dkc, dvc = up(dinp["k_cache"]), up(dinp["v_cache"])
+    dout = torch.empty((dcfg.M, dcfg.H * dcfg.d), device=dev)
+    ws = torch.empty(taf.attn_decode_workspace_bytes(dcfg.M, dcfg.H, dcfg.d, dcfg.max_len) // 4, device=dev)
+    torch.cuda.synchronize()
+    log("inputs resident on the GPU")
+
+    append_pos = (lens - 1).tolist()
+    lens_list = lens.tolist()
+    names = ("prefill", "bulk_scatter", "append", "decode")
+    calls = {
+        "prefill": lambda: taf.attn_prefill(pq, pk, pv, pout, pcfg.B, pcfg.S, pcfg.H, pcfg.d, pcfg.scale, True),
+        "bulk_scatter": lambda: taf.kv_cache_scatter(pk, pv, bk, bv, [0] * scfg.M, scfg.M, scfg.n_new,
+                                                     scfg.Hkv, scfg.d, scfg.max_len),
+        "append": lambda: taf.kv_cache_scatter(dkn, dvn, dkc, dvc, append_pos, dcfg.M, 1, dcfg.Hkv, dcfg.d,
+                                               dcfg.max_len),
+        "decode": lambda: taf.attn_decode_gqa_batched(dq, dkc, dvc, lens_list, dout, dcfg.M, dcfg.H, dcfg.Hkv,
+                                                      dcfg.d, dcfg.max_len, dcfg.scale, ws),
+    }
+
+    def step(events=None):
+        for i, n in enumerate(names):
+            if events is not None:
+                events[n][0].record()
+            calls[n]()
+            if events is not None:
+                events[n][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    evs = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    per = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step; " +
+        ", ".join(f"{n} {per[n] * 1e3:.1f} us" for n in names))
+
+    if not (torch.isfinite(pout).all() and torch.isfinite(dout).all()):
+        raise RuntimeError("non-finite outputs")
+
+    pre_flops = pcfg.flops
+    pre_tflops = pre_flops / (per["prefill"] * 1e-3) / 1e12
+    dec_bytes = dcfg.decode_bytes(lens)
+    dec_gbs = dec_bytes / (per["decode"] * 1e-3) / 1e9
+    blk_gbs = scfg.bytes / (per["bulk_scatter"] * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "causal prefill B4 S2048 H32 d128 + bulk KV append into [4,32,4096,128] from 0, "
+                        "then GQA decode step M16 H64 Hkv8 d128 max_len 32768 L~U{16384..32768} "
+                        "(append at L-1, attend over L)",
+            "prefill": {"B": pcfg.B, "S": pcfg.S, "H": pcfg.H, "d": pcfg.d, "causal": True},
+            "decode": {"M": dcfg.M, "H": dcfg.H, "Hkv": dcfg.Hkv, "d": dcfg.d, "max_len": dcfg.max_len,
+                       "sum_L": int(lens.sum())},
+        },
+        "decode": {"gbs": round(dec_gbs, 2), "frac_hbm": round(dec_gbs / HBM_PEAK_GBS, 4),
+                   "us": round(per["decode"] * 1e3, 2), "algorithmic_bytes": dec_bytes},
+        "prefill": {"tflops": round(pre_tflops, 3), "frac_mfma": round(pre_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
+                    "us": round(per["prefill"] * 1e3, 2), "algorithmic_flops": pre_flops},
+        "bulk_scatter": {"gbs": round(blk_gbs, 2), "frac_hbm": round(blk_gbs / HBM_PEAK_GBS, 4),
+                         "us": round(per["bulk_scatter"] * 1e3, 2), "algorithmic_bytes": scfg.bytes},
+        "append": {"us": round(per["append"] * 1e3, 2), "algorithmic_bytes": dcfg.append_bytes},
+        "roofline": {"kernel": "prefill_kernel<128, causal>", "bound": "mfma", "achieved": round(pre_tflops, 3),
+                     "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(pre_tflops / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None},
+        "roofline_decode": {"kernels": "decode_split_kernel<128> + decode_combine_kernel<128>", "bound": "hbm",
+                            "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+
+    # Free the GPU copies before the host-side leg.
+    del pq, pk, pv, pout, bk, bv, dq, dkn, dvn, dkc, dvc, dout, ws
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample of the decode workload ...")
+        result["cpu_baseline"] = cpu_baseline(dinp, dcfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+/*
+ * attn.h -- C ABI of libattn.so: GPU-resident scaled-dot-product attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ *   out = softmax(scale * Q K^T [+ causal mask]) V
+ *
+ * Three operations, each enqueued on a caller-supplied HIP stream:
+ *   attn_prefill             full-sequence attention over interleaved
+ *                            [batch, seq, n_heads * head_dim] activations,
+ *                            optionally causal;
+ *   attn_decode_gqa_batched  one query token per sequence for up to 32
+ *                            sequences against a preallocated GQA KV cache,
+ *                            each sequence with its own length;
+ *   kv_cache_scatter         append rows of new keys/values into that cache
+ *                            at each sequence's current length.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are f32, row-major, contiguous, in DEVICE memory owned by the
+ *     caller.  The library allocates nothing, keeps no per-call state and is
+ *     safe to call from several host threads.  Pointers marked HOST are read
+ *     synchronously during the call and may be reused on return.
+ *   - Device pointers must be 16-byte aligned (128-bit accesses).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued and
+ *     the call returns without synchronising; the caller orders later work on
+ *     the same stream.
+ *   - Every argument is validated on the host before anything is enqueued.  A
+ *     non-zero return therefore means nothing was queued and every output is
+ *     untouched.  The only exception is ATTN_ERR_HIP, returned when the HIP
+ *     runtime rejects a launch (work may then have been partly queued).
+ *   - Outputs must not overlap inputs (ATTN_ERR_ALIAS).
+ *
+ * Sources (page title, then section): trueno-gpu 0.4.11
+ * src/memory/resident/attention.rs (`batched_multihead_attention`,
+ * `incremental_attention_gpu_with_stream`, `kv_cache_scatter_gpu`);
+ * trustformers-core 0.2.0 src/gpu_ops/cuda/oxicuda/attention.rs
+ * (`attention_prefill_gpu_to_gpu`, `attention_decode_gpu_to_gpu`,
+ * `checked_len`); realizar 0.8.5
+ * src/cuda/executor/cache_from_cache_from_kv_cache.rs (`init_kv_cache_gpu`,
+ * `init_batched_kv_cache_gpu`).
+ */
+#ifndef TRANSFORMER_ATTENTION_FLASH_AMD_ATTN_H
+#define TRANSFORMER_ATTENTION_FLASH_AMD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+    ATTN_ERR_INVALID_DIM = 2, /* a size, length or position is out of range */
+    ATTN_ERR_UNSUPPORTED = 3, /* head_dim not in {32, 64, 128}, or a pointer not 16-byte aligned */
+    ATTN_ERR_OVERFLOW = 4,    /* a size product does not fit the index types used */
+    ATTN_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than attn_decode_workspace_bytes() */
+    ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error for a launch */
+    ATTN_ERR_ALIAS = 7        /* an output buffer overlaps an input buffer */
+} attn_status;
+
+/* Largest number of sequences a decode or scatter call takes (the batched
+ * cache holds 1..32 sequences: realizar `init_batched_kv_cache_gpu`). */
+#define ATTN_MAX_SEQS 32
+
+/*
+ * Full-sequence multi-head attention (prefill).
+ *
+ * Defines: trueno-gpu `batched_multihead_attention` (softmax(Q K^T/sqrt(d_k)) V
+ * per head over interleaved [seq, n_heads * head_dim]) and trustformers-core
+ * `attention_prefill_gpu_to_gpu` (caller-chosen scale; causal mask "from an
+ * empty cache": query i sees keys 0..=i; masked probabilities are exactly 0).
+ * Batch elements are independent.
+ *
+ *   q, k, v  [batch, seq_len, n_heads * head_dim]  read
+ *   out      [batch, seq_len, n_heads * head_dim]  written, every element
+ *   out[b, i, h*d + l] = sum_j p_ij v[b, j, h*d + l],
+ *   p_ij = exp(s_ij - max_j s_ij) / sum_j exp(...),
+ *   s_ij = scale * sum_l q[b, i, h*d + l] k[b, j, h*d + l] over visible j.
+ *   scale    usually 1/sqrtf(head_dim); any finite value is accepted.
+ *   causal   0: every query sees all seq_len keys; 1: query i sees 0..i.
+ *
+ * Errors: NULL pointer; batch, seq_len, n_heads <= 0 or causal not 0/1
+ * (INVALID_DIM); head_dim not in {32, 64, 128} or misaligned (UNSUPPORTED);
+ * batch*seq_len*n_heads*head_dim >= 2^31 (OVERFLOW); scale not finite
+ * (INVALID_DIM); out overlapping q, k or v (ALIAS).
+ */
+int attn_prefill(const float *q, const float *k, const float *v, float *out,
+                 int32_t batch, int32_t seq_len, int32_t n_heads, int32_t head_dim,
+                 float scale, int32_t causal, void *stream);
+
+/*
+ * Bytes of device workspace attn_decode_gqa_batched needs for these sizes
+ * (per-split partial maxima, sums and unnormalised outputs).  Returns 0 when
+ * the sizes are invalid.  Pure host arithmetic; no HIP call.
+ */
+size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                   int32_t max_len);
+
+/*
+ * Batched grouped-query decode attention: one new query token per sequence.
+ *
+ * Defines: trueno-gpu `incremental_attention_gpu_with_stream` (one query per
+ * head against a head-first cache, empty sequence -> zeros, caller's stream,
+ * no sync) generalised to GQA and to M sequences as laid out by realizar
+ * `init_kv_cache_gpu` / `init_batched_kv_cache_gpu`.  Query head h reads KV
+ * head h / (num_heads / num_kv_heads) (contiguous groups).
+ *
+ *   q          [M, num_heads * head_dim]                       read
+ *   k_cache    [M, num_kv_heads, max_len, head_dim]             read, rows < seq_lens[m] only
+ *   v_cache    [M, num_kv_heads, max_len, head_dim]             read, rows < seq_lens[m] only
+ *   seq_lens   HOST [M] int32, keys attended by sequence m, 0 <= L <= max_len;
+ *              L = 0 gives zeros for that sequence
+ *   out        [M, num_heads * head_dim]                        written, every element
+ *   workspace  device scratch of >= attn_decode_workspace_bytes(M, num_heads,
+ *              head_dim, max_len) bytes, 16-byte aligned, owned by the caller,
+ *              contents on entry irrelevant; must not be used by other work
+ *              that can run concurrently with this call.
+ *
+ * Errors: NULL pointer; M not in [1, 32], num_heads/num_kv_heads/max_len <= 0,
+ * num_kv_heads > num_heads, num_heads % num_kv_heads != 0, a seq_lens value
+ * outside [0, max_len], scale not finite (INVALID_DIM); head_dim not in
+ * {32, 64, 128} or misaligned pointer (UNSUPPORTED); an element count >= 2^40
+ * (OVERFLOW); workspace too small (WORKSPACE); out overlapping an input or
+ * the workspace (ALIAS).
+ */
+int attn_decode_gqa_batched(const float *q, const float *k_cache, const float *v_cache,
+                            const int32_t *seq_lens, float *out, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_len, float scale, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * KV-cache append (scatter).
+ *
+ * Defines: trueno-gpu `kv_cache_scatter_gpu` (an interleaved [n_heads *
+ * head_dim] row goes to cache[head, pos, :]; pos must be < max_seq_len)
+ * generalised to n_new rows and M sequences of the batched cache (realizar
+ * `init_batched_kv_cache_gpu`, per-sequence stride num_kv_heads * max_len *
+ * head_dim).  Bytes are copied verbatim; nothing else in the caches changes.
+ *
+ *   k_new, v_new      [M, n_new, num_kv_heads * head_dim]   read
+ *   k_cache, v_cache  [M, num_kv_heads, max_len, head_dim]   rows written:
+ *       cache[m, kh, cache_lens[m] + r, :] = new[m, r, kh*d : (kh+1)*d]
+ *   cache_lens        HOST [M] int32, write start position of sequence m
+ *
+ * Errors: NULL pointer; M not in [1, 32], n_new/num_kv_heads/max_len <= 0, a
+ * cache_lens value < 0 or cache_lens[m] + n_new > max_len (INVALID_DIM);
+ * head_dim not in {32, 64, 128} or misaligned (UNSUPPORTED); an element count
+ * >= 2^40 (OVERFLOW); a cache overlapping a source or the other cache (ALIAS).
+ */
+int kv_cache_scatter(const float *k_new, const float *v_new, float *k_cache, float *v_cache,
+                     const int32_t *cache_lens, int32_t num_seqs, int32_t n_new,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t max_len, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRANSFORMER_ATTENTION_FLASH_AMD_ATTN_H */

@@ -1,0 +1,146 @@
+"""The C ABI on the CPU: the library loads, exports what include/attn.h declares,
+and rejects every invalid call with its documented status before touching HIP.
+
+No call here reaches a kernel launch: every argument set is invalid, and the
+library validates on the host before any HIP call (include/attn.h, conventions).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import transformer_attention_flash_amd as taf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, NULL, DIM, UNSUP, OVF, WS, HIP, ALIAS = range(8)
+A = 0x10000          # fake, 16-byte aligned "device" addresses, never dereferenced
+B_ = 0x20000000
+C_ = 0x40000000
+O_ = 0x60000000
+W_ = 0x80000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return taf.library()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "attn_prefill", "attn_decode_workspace_bytes", "attn_decode_gqa_batched",
+        "kv_cache_scatter", "attn_status_string"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", taf.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert taf.attn_status_string(s) and taf.attn_status_string(s) != "unknown status"
+    assert taf.attn_status_string(99) == "unknown status"
+
+
+def prefill(lib, q=A, k=B_, v=C_, out=O_, b=1, s=64, h=4, d=32, scale=0.125, causal=0):
+    return lib.attn_prefill(q, k, v, out, b, s, h, d, scale, causal, None)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, q=0) == NULL
+    assert prefill(lib, out=0) == NULL
+    assert prefill(lib, b=0) == DIM
+    assert prefill(lib, s=-1) == DIM
+    assert prefill(lib, h=0) == DIM
+    assert prefill(lib, causal=2) == DIM
+    assert prefill(lib, scale=float("nan")) == DIM
+    assert prefill(lib, scale=float("inf")) == DIM
+    assert prefill(lib, d=48) == UNSUP
+    assert prefill(lib, d=256) == UNSUP
+    assert prefill(lib, q=A + 4) == UNSUP
+    assert prefill(lib, b=64, s=65536, h=64, d=128) == OVF
+    assert prefill(lib, out=A + 64) == ALIAS      # out starts inside q
+    assert prefill(lib, out=C_ - 16) == ALIAS     # out runs into v
+
+
+def decode(lib, q=A, k=B_, v=C_, lens=None, out=O_, M=2, H=8, Hkv=2, d=64, max_len=100, scale=0.125,
+           ws=W_, ws_bytes=None):
+    if lens is None:
+        lens = [5, 100][:M] + [1] * max(0, M - 2)
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens) if lens != "null" else None
+    if ws_bytes is None:
+        ws_bytes = lib.attn_decode_workspace_bytes(max(1, min(M, 32)), max(1, H), d if d in (32, 64, 128) else 64,
+                                                   max(1, max_len))
+    return lib.attn_decode_gqa_batched(q, k, v, arr, out, M, H, Hkv, d, max_len, scale, ws, ws_bytes, None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, q=0) == NULL
+    assert decode(lib, lens="null") == NULL
+    assert decode(lib, ws=0) == NULL
+    assert decode(lib, M=0, lens=[1]) == DIM
+    assert decode(lib, M=33, lens=[1] * 33) == DIM
+    assert decode(lib, Hkv=3) == DIM           # 8 % 3 != 0
+    assert decode(lib, Hkv=16) == DIM          # more KV heads than query heads
+    assert decode(lib, lens=[101, 3]) == DIM   # longer than the cache
+    assert decode(lib, lens=[-1, 3]) == DIM
+    assert decode(lib, max_len=0, lens=[0, 0]) == DIM
+    assert decode(lib, scale=float("nan")) == DIM
+    assert decode(lib, d=96) == UNSUP
+    assert decode(lib, k=B_ + 8) == UNSUP
+    assert decode(lib, ws=W_ + 4) == UNSUP
+    assert decode(lib, ws_bytes=16) == WS
+    assert decode(lib, out=A) == ALIAS                       # out is q
+    assert decode(lib, ws=B_ + 1024) == ALIAS                # workspace inside the K cache
+
+
+def test_decode_workspace_bytes(lib):
+    # acc [M, H, splits, d] + (max, sum) [M, H, splits, 2] floats; the split
+    # length is at least 64 keys and grows so there are at most 256 splits.
+    assert lib.attn_decode_workspace_bytes(32, 32, 128, 4096) == 32 * 32 * 64 * 130 * 4
+    assert lib.attn_decode_workspace_bytes(16, 64, 128, 32768) == 16 * 64 * 256 * 130 * 4
+    assert lib.attn_decode_workspace_bytes(1, 1, 32, 1) == 1 * 1 * 1 * 34 * 4
+    assert lib.attn_decode_workspace_bytes(0, 8, 128, 16) == 0
+    assert lib.attn_decode_workspace_bytes(33, 8, 128, 16) == 0
+    assert lib.attn_decode_workspace_bytes(2, 8, 80, 16) == 0
+
+
+def scatter(lib, kn=A, vn=B_, kc=C_, vc=O_, lens=(0, 3), M=2, n_new=2, Hkv=2, d=64, max_len=8):
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens) if lens is not None else None
+    return lib.kv_cache_scatter(kn, vn, kc, vc, arr, M, n_new, Hkv, d, max_len, None)
+
+
+def test_scatter_validation(lib):
+    assert scatter(lib, kn=0) == NULL
+    assert scatter(lib, lens=None) == NULL
+    assert scatter(lib, M=0, lens=(0,)) == DIM
+    assert scatter(lib, M=33, lens=(0,) * 33) == DIM
+    assert scatter(lib, n_new=0) == DIM
+    assert scatter(lib, lens=(0, 7)) == DIM     # 7 + 2 > 8: the pages reject pos >= max_seq_len
+    assert scatter(lib, lens=(-1, 0)) == DIM
+    assert scatter(lib, d=16) == UNSUP
+    assert scatter(lib, vc=O_ + 8) == UNSUP
+    assert scatter(lib, n_new=2**20, Hkv=2**10, d=128, max_len=2**21, lens=(0, 0)) == OVF
+    assert scatter(lib, vc=C_ + 256) == ALIAS   # the two caches overlap
+    assert scatter(lib, kc=A) == ALIAS          # cache over the source
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4 * 32, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        taf.attn_prefill(x, x, x, x, 1, 1, 4, 32, 0.1, False)

@@ -1,0 +1,131 @@
+"""Batched GQA decode on the GPU against the fp64 oracle.
+
+Small cases cover every group size class (g = 1, 2, 3, 4, 8, 16, 32 -- the
+last needs two 16-head blocks), every head_dim, empty sequences, lengths on
+and around split/chunk boundaries, L = max_len, M = 32, and cache rows past
+L_m filled with NaN (they must never be read).  Full-size cases run the two
+decode workloads as one step: append the new row at L_m - 1, then attend
+over L_m keys.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import transformer_attention_flash_amd as taf
+from transformer_attention_flash_amd import workloads as wl
+from gpu_common import assert_attn_close, nan_like, note, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # M, H, Hkv, d, max_len, lens (None = random in [0, max_len])
+    (1, 1, 1, 32, 1, [1]),
+    (2, 4, 4, 64, 70, [0, 70]),
+    (4, 8, 2, 128, 300, [1, 31, 32, 33]),
+    (3, 16, 2, 128, 1000, [64, 65, 1000]),
+    (2, 32, 2, 64, 200, [199, 128]),
+    (2, 64, 2, 128, 130, [130, 7]),
+    (32, 8, 8, 32, 50, None),
+    (5, 12, 4, 64, 2000, [0, 511, 512, 513, 1999]),
+    (2, 6, 3, 128, 5000, [4097, 1024]),
+    (3, 16, 8, 128, 9000, [8999, 256, 257]),
+]
+
+
+def run_decode(q, kc, vc, lens, M, H, Hkv, d, max_len, scale):
+    ws = __import__("torch").empty(taf.attn_decode_workspace_bytes(M, H, d, max_len) // 4,
+                                   dtype=__import__("torch").float32, device=q.device)
+    out = nan_like((M, H * d))
+    taf.attn_decode_gqa_batched(q, kc, vc, lens, out, M, H, Hkv, d, max_len, scale, ws)
+    return to_host(out)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"M{c[0]}_H{c[1]}_Hkv{c[2]}_d{c[3]}_max{c[4]}" for c in SMALL])
+def test_decode_small(case):
+    M, H, Hkv, d, max_len, lens = case
+    rng = np.random.default_rng(100 + M * 7 + H)
+    if lens is None:
+        lens = rng.integers(0, max_len + 1, size=M)
+    lens = np.asarray(lens, np.int32)
+    q = rng.standard_normal((M, H * d), dtype=np.float32)
+    kc = rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32)
+    vc = rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32)
+    for m in range(M):  # rows past L_m are NaN: reading one would poison the output
+        kc[m, :, lens[m]:] = np.nan
+        vc[m, :, lens[m]:] = np.nan
+    scale = wl.scale_for(d)
+    note(f"decode M={M} H={H} Hkv={Hkv} d={d} max_len={max_len} lens={lens.tolist()}")
+    got = run_decode(to_dev(q), to_dev(kc), to_dev(vc), lens.tolist(), M, H, Hkv, d, max_len, scale)
+    want = oracle.default().decode(q, kc, vc, lens, M, H, Hkv, d, max_len, scale)
+    assert_attn_close(got, want, f"decode {case}")
+    for m in np.nonzero(lens == 0)[0]:
+        assert np.all(got[m] == 0.0), "an empty sequence must give zeros"
+
+
+def test_decode_large_scores():
+    """Scores in the hundreds: the split-local maxima differ widely, the merge must rescale."""
+    M, H, Hkv, d, max_len = 2, 8, 2, 128, 3000
+    rng = np.random.default_rng(5)
+    q = (rng.standard_normal((M, H * d), dtype=np.float32) * 8).astype(np.float32)
+    kc = rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32)
+    vc = rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32)
+    kc[:, :, 2500] *= 4  # one dominant key late in the sequence
+    lens = np.array([3000, 2600], np.int32)
+    scale = wl.scale_for(d)
+    note("decode large scores")
+    got = run_decode(to_dev(q), to_dev(kc), to_dev(vc), lens.tolist(), M, H, Hkv, d, max_len, scale)
+    want = oracle.default().decode(q, kc, vc, lens, M, H, Hkv, d, max_len, scale)
+    assert_attn_close(got, want, "decode large scores")
+
+
+def test_decode_equals_prefill_row_on_gpu():
+    """GPU decode at step t over a GPU-appended cache equals row t of the GPU causal prefill."""
+    import torch
+    B, S, H, d, max_len = 1, 160, 4, 64, 192
+    rng = np.random.default_rng(9)
+    q, k, v = (rng.standard_normal((B, S, H * d), dtype=np.float32) for _ in range(3))
+    scale = wl.scale_for(d)
+    note("decode == prefill row")
+    out = nan_like((B, S, H * d))
+    taf.attn_prefill(to_dev(q), to_dev(k), to_dev(v), out, B, S, H, d, scale, True)
+    pre = to_host(out)
+    kc = torch.full((1, H, max_len, d), float("nan"), device=out.device)
+    vc = torch.full((1, H, max_len, d), float("nan"), device=out.device)
+    taf.kv_cache_scatter(to_dev(k), to_dev(v), kc, vc, [0], 1, S, H, d, max_len)
+    want = oracle.default().prefill(q, k, v, B, S, H, d, scale, True)
+    for t in (0, 1, 31, 32, 63, 64, 100, S - 1):
+        got = run_decode(to_dev(np.ascontiguousarray(q[:, t])), kc, vc, [t + 1], 1, H, H, d, max_len, scale)
+        assert np.max(np.abs(got[0] - pre[0, t])) <= 2e-5, f"decode vs prefill row {t}"
+        assert_attn_close(got[0], want[0, t], f"decode step {t} vs oracle")
+
+
+@pytest.mark.parametrize("cid", [4, 5])
+def test_decode_step_full_size(cid):
+    """Append at L_m - 1 then decode over L_m, on the full decode workloads."""
+    import torch
+    cfg = wl.DECODE[cid]
+    inp = wl.decode_inputs(cfg)
+    lens = inp["lens"]
+    note(f"decode step full size cfg{cid} sum(L)={int(lens.sum())}")
+    kc, vc = to_dev(inp["k_cache"]), to_dev(inp["v_cache"])
+    taf.kv_cache_scatter(to_dev(inp["k_new"]), to_dev(inp["v_new"]), kc, vc, (lens - 1).tolist(),
+                         cfg.M, 1, cfg.Hkv, cfg.d, cfg.max_len)
+    got = run_decode(to_dev(inp["q"]), kc, vc, lens.tolist(), cfg.M, cfg.H, cfg.Hkv, cfg.d, cfg.max_len,
+                     cfg.scale)
+    del kc, vc
+    torch.cuda.empty_cache()
+    orc = oracle.default()
+    k_host, v_host = inp["k_cache"], inp["v_cache"]
+    orc.scatter(inp["k_new"], inp["v_new"], k_host, v_host, lens - 1, cfg.M, 1, cfg.Hkv, cfg.d, cfg.max_len)
+    if cid == 4:
+        want = orc.decode(inp["q"], k_host, v_host, lens, cfg.M, cfg.H, cfg.Hkv, cfg.d, cfg.max_len, cfg.scale)
+        assert_attn_close(got, want, "cfg4 decode (all heads)")
+    else:
+        # Every sequence, 8 heads each spread over the KV groups.
+        g = cfg.H // cfg.Hkv
+        sel = np.array([(m, kh * g + (m + kh) % g) for m in range(cfg.M) for kh in range(cfg.Hkv)], np.int64)
+        want = orc.decode_rows(inp["q"], k_host, v_host, lens, sel, cfg.M, cfg.H, cfg.Hkv, cfg.d,
+                               cfg.max_len, cfg.scale)
+        got_sel = np.stack([got[m, h * cfg.d:(h + 1) * cfg.d] for m, h in sel])
+        assert_attn_close(got_sel, want, "cfg5 decode (sampled heads)")
+        assert np.all(np.isfinite(got))

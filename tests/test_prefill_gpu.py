@@ -1,0 +1,90 @@
+"""Prefill (full-sequence attention) on the GPU against the fp64 oracle.
+
+Small cases span one to many 128-query and 32-key tiles with ragged tails
+(S = 1, 31, 33, 127, 129, 200, 500, 1500), every head_dim, batch > 1, head
+counts on and off the XCD-grouping path (B*H a multiple of 8 or not), causal
+and not, non-default scales and large scores.  Outputs start as NaN so an
+unwritten element fails.  The full-size cases are the three prefill
+workloads: all outputs for the two non-causal ones, sampled rows (first and
+last queries, tile edges, random) for the causal B=4, S=2048, H=32, d=128 one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import transformer_attention_flash_amd as taf
+from transformer_attention_flash_amd import workloads as wl
+from gpu_common import assert_attn_close, nan_like, note, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # B, S, H, d
+    (1, 1, 1, 32),
+    (1, 31, 2, 32),
+    (2, 33, 3, 64),
+    (1, 127, 1, 128),
+    (1, 128, 2, 128),
+    (1, 129, 1, 128),
+    (3, 200, 2, 64),
+    (2, 300, 4, 128),
+    (1, 500, 8, 128),
+    (1, 257, 16, 32),
+]
+
+
+def run_prefill(q, k, v, B, S, H, d, scale, causal):
+    out = nan_like((B, S, H * d))
+    taf.attn_prefill(to_dev(q), to_dev(k), to_dev(v), out, B, S, H, d, scale, causal)
+    return to_host(out)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}_S{c[1]}_H{c[2]}_d{c[3]}" for c in SMALL])
+def test_prefill_small(case, causal):
+    B, S, H, d = case
+    rng = np.random.default_rng(1 + S * 13 + H + d)
+    q, k, v = (rng.standard_normal((B, S, H * d), dtype=np.float32) for _ in range(3))
+    scale = wl.scale_for(d)
+    note(f"prefill B={B} S={S} H={H} d={d} causal={causal}")
+    got = run_prefill(q, k, v, B, S, H, d, scale, causal)
+    want = oracle.default().prefill(q, k, v, B, S, H, d, scale, causal)
+    assert_attn_close(got, want, f"prefill {case} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_prefill_large_scores_and_custom_scale(causal):
+    B, S, H, d = 1, 333, 2, 128
+    rng = np.random.default_rng(3)
+    q = (rng.standard_normal((B, S, H * d), dtype=np.float32) * 6).astype(np.float32)
+    k, v = (rng.standard_normal((B, S, H * d), dtype=np.float32) for _ in range(2))
+    scale = 0.3
+    note(f"prefill large scores causal={causal}")
+    got = run_prefill(q, k, v, B, S, H, d, scale, causal)
+    want = oracle.default().prefill(q, k, v, B, S, H, d, scale, causal)
+    assert_attn_close(got, want, "prefill large scores")
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_prefill_full_size_noncausal(cid):
+    cfg = wl.PREFILL[cid]
+    q, k, v = wl.prefill_inputs(cfg)
+    note(f"prefill full size {cfg.name}")
+    got = run_prefill(q, k, v, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, cfg.causal)
+    want = oracle.default().prefill(q, k, v, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, cfg.causal)
+    assert_attn_close(got, want, cfg.name)
+
+
+def test_prefill_full_size_causal_sampled():
+    cfg = wl.PREFILL[3]
+    q, k, v = wl.prefill_inputs(cfg)
+    note(f"prefill full size {cfg.name}")
+    got = run_prefill(q, k, v, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, cfg.causal)
+    assert np.all(np.isfinite(got)), "every output element is written"
+    rng = np.random.default_rng(33)
+    rows = [0, 1, 31, 32, 127, 128, 129, 1023, 1024, 2046, 2047] + rng.integers(0, cfg.S, 21).tolist()
+    sel = np.array([(b, i, h) for b in range(cfg.B) for i in rows for h in ((i + b) % cfg.H, (7 * i) % cfg.H)],
+                   np.int64)
+    want = oracle.default().prefill_rows(q, k, v, sel, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, True)
+    got_sel = np.stack([got[b, i, h * cfg.d:(h + 1) * cfg.d] for b, i, h in sel])
+    assert_attn_close(got_sel, want, "causal full-size sampled rows")

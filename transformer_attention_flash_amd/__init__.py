@@ -1,0 +1,176 @@
+"""GPU-resident scaled-dot-product attention for MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libattn.so`` (``include/attn.h``).
+Each function has the name of the C entry point it calls and only marshals
+arguments: it checks the torch tensors' device, dtype, contiguity and element
+counts (which the C layer cannot see behind raw pointers), passes their data
+pointers and the current HIP stream of their device, and turns a non-zero
+status into :class:`AttnError`.  All computation happens in the HIP kernels.
+
+The library is built ahead of time (``python -m
+transformer_attention_flash_amd.build`` or ``__graft_entry__.build()``); if it
+is missing, every call raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+__all__ = [
+    "AttnError",
+    "ATTN_MAX_SEQS",
+    "attn_prefill",
+    "attn_decode_workspace_bytes",
+    "attn_decode_gqa_batched",
+    "kv_cache_scatter",
+    "attn_status_string",
+    "library",
+    "library_path",
+]
+
+ATTN_MAX_SEQS = 32
+_STATUS = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_INVALID_DIM", 3: "ATTN_ERR_UNSUPPORTED",
+    4: "ATTN_ERR_OVERFLOW", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_ALIAS",
+}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libattn.so")
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-zero attn_status returned by libattn.so."""
+
+    def __init__(self, status: int, func: str):
+        self.status = status
+        super().__init__(f"{func}: {_STATUS.get(status, status)} ({attn_status_string(status)})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with `python -m transformer_attention_flash_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+        lib.attn_prefill.argtypes = [p, p, p, p, i32, i32, i32, i32, f32, i32, p]
+        lib.attn_prefill.restype = ctypes.c_int
+        lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        lib.attn_decode_workspace_bytes.restype = sz
+        lib.attn_decode_gqa_batched.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, p, sz, p]
+        lib.attn_decode_gqa_batched.restype = ctypes.c_int
+        lib.kv_cache_scatter.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, p]
+        lib.kv_cache_scatter.restype = ctypes.c_int
+        lib.attn_status_string.argtypes = [ctypes.c_int]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def attn_status_string(status: int) -> str:
+    return library().attn_status_string(int(status)).decode()
+
+
+# ----------------------------------------------------------------- marshalling
+
+
+def _check_tensor(name, t, numel, device=None):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live in GPU memory, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+def _host_ints(name, values, count) -> ctypes.Array:
+    vals = [int(x) for x in (values.tolist() if hasattr(values, "tolist") else values)]
+    if len(vals) != count:
+        raise ValueError(f"{name} has {len(vals)} entries, expected {count}")
+    for x in vals:
+        if not -(2**31) <= x < 2**31:
+            raise ValueError(f"{name} value {x} does not fit int32")
+    return (ctypes.c_int32 * count)(*vals)
+
+
+def _stream_ptr(device, stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _call(func_name, status):
+    if status != 0:
+        raise AttnError(status, func_name)
+
+
+# ----------------------------------------------------------------- entry points
+
+
+def attn_prefill(q, k, v, out, batch: int, seq_len: int, n_heads: int, head_dim: int,
+                 scale: float, causal: bool, stream=None) -> None:
+    """out[b, i, h*d:(h+1)*d] = softmax(scale q k^T [causal]) v for [batch, seq_len, n_heads*head_dim] f32."""
+    n = batch * seq_len * n_heads * head_dim
+    dev = q.device
+    ptrs = [_check_tensor(nm, t, n, dev) for nm, t in (("q", q), ("k", k), ("v", v), ("out", out))]
+    _call("attn_prefill", library().attn_prefill(*ptrs, batch, seq_len, n_heads, head_dim, scale,
+                                                 1 if causal else 0, _stream_ptr(dev, stream)))
+
+
+def attn_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_len: int) -> int:
+    return int(library().attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_len))
+
+
+def attn_decode_gqa_batched(q, k_cache, v_cache, seq_lens: Sequence[int], out, num_seqs: int,
+                            num_heads: int, num_kv_heads: int, head_dim: int, max_len: int,
+                            scale: float, workspace, stream=None) -> None:
+    """Batched GQA decode; ``seq_lens`` is a host sequence of M ints; ``workspace`` a device tensor."""
+    import torch
+
+    dev = q.device
+    qn = num_seqs * num_heads * head_dim
+    cn = num_seqs * num_kv_heads * max_len * head_dim
+    pq = _check_tensor("q", q, qn, dev)
+    pk = _check_tensor("k_cache", k_cache, cn, dev)
+    pv = _check_tensor("v_cache", v_cache, cn, dev)
+    po = _check_tensor("out", out, qn, dev)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same GPU")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    lens = _host_ints("seq_lens", seq_lens, num_seqs)
+    _call("attn_decode_gqa_batched",
+          library().attn_decode_gqa_batched(pq, pk, pv, lens, po, num_seqs, num_heads, num_kv_heads,
+                                            head_dim, max_len, scale, workspace.data_ptr(), ws_bytes,
+                                            _stream_ptr(dev, stream)))
+
+
+def kv_cache_scatter(k_new, v_new, k_cache, v_cache, cache_lens: Sequence[int], num_seqs: int,
+                     n_new: int, num_kv_heads: int, head_dim: int, max_len: int, stream=None) -> None:
+    """cache[m, kh, cache_lens[m] + r, :] = new[m, r, kh*d:(kh+1)*d] for K and V."""
+    dev = k_new.device
+    sn = num_seqs * n_new * num_kv_heads * head_dim
+    cn = num_seqs * num_kv_heads * max_len * head_dim
+    ptrs = [_check_tensor("k_new", k_new, sn, dev), _check_tensor("v_new", v_new, sn, dev),
+            _check_tensor("k_cache", k_cache, cn, dev), _check_tensor("v_cache", v_cache, cn, dev)]
+    lens = _host_ints("cache_lens", cache_lens, num_seqs)
+    _call("kv_cache_scatter", library().kv_cache_scatter(*ptrs, lens, num_seqs, n_new, num_kv_heads,
+                                                         head_dim, max_len, _stream_ptr(dev, stream)))

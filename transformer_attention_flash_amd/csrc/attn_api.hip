@@ -1,0 +1,167 @@
+// attn_api.hip -- the C ABI of libattn.so (declared in include/attn.h).
+//
+// Host-side validation comes first and is complete before anything is
+// enqueued, so an error return leaves every buffer untouched (the pages'
+// helpers likewise reject bad sizes before launching: trueno-gpu 0.4.11
+// src/memory/resident/attention.rs, `incremental_attention_gpu` /
+// `kv_cache_scatter_gpu`; trustformers-core 0.2.0
+// src/gpu_ops/cuda/oxicuda/attention.rs, `checked_len`).  Then exactly the
+// kernels of the operation are launched on the caller's stream; nothing is
+// allocated, copied or synchronised.
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+using attn::SeqInts;
+
+constexpr int64_t kMaxElems32 = (int64_t(1) << 31) - 1;  // prefill indexes tokens*H*D in int32-safe ranges
+constexpr int64_t kMaxElems = int64_t(1) << 40;          // decode/scatter element-count bound
+
+bool head_dim_ok(int32_t d) { return d == 32 || d == 64 || d == 128; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [p, p + n) and [q, q + m) (bytes) overlap?
+bool overlaps(const void *p, int64_t n, const void *q, int64_t m) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
+    return a0 < b0 + (uintptr_t)m && b0 < a0 + (uintptr_t)n;
+}
+
+// a * b * ... with an overflow check against `limit`.
+bool checked_mul(std::initializer_list<int64_t> xs, int64_t limit, int64_t *out) {
+    int64_t acc = 1;
+    for (int64_t x : xs) {
+        if (x < 0) return false;
+        if (x != 0 && acc > limit / x) return false;
+        acc *= x;
+    }
+    if (acc > limit) return false;
+    *out = acc;
+    return true;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_INVALID_DIM: return "a size, length or position is out of range";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported head_dim (32, 64, 128) or pointer not 16-byte aligned";
+        case ATTN_ERR_OVERFLOW: return "a size product overflows the supported range";
+        case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case ATTN_ERR_HIP: return "the HIP runtime reported an error";
+        case ATTN_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+        default: return "unknown status";
+    }
+}
+
+int attn_prefill(const float *q, const float *k, const float *v, float *out, int32_t batch,
+                 int32_t seq_len, int32_t n_heads, int32_t head_dim, float scale, int32_t causal,
+                 void *stream) {
+    if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+    if (batch <= 0 || seq_len <= 0 || n_heads <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_DIM;
+    if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID_DIM;
+    if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_UNSUPPORTED;
+    int64_t elems;
+    if (!checked_mul({batch, seq_len, n_heads, head_dim}, kMaxElems32, &elems)) return ATTN_ERR_OVERFLOW;
+    const int64_t bytes = elems * 4;
+    if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+        return ATTN_ERR_ALIAS;
+
+    attn::PrefillArgs a{q, k, v, out, batch, seq_len, n_heads, head_dim, scale, causal};
+    return from_hip(attn::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                   int32_t max_len) {
+    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS || num_heads <= 0 || max_len <= 0) return 0;
+    if (!head_dim_ok(head_dim)) return 0;
+    int64_t slots;
+    if (!checked_mul({num_seqs, num_heads, attn::decode_max_splits(max_len), head_dim + 2}, kMaxElems,
+                     &slots))
+        return 0;
+    return attn::decode_workspace_bytes(num_seqs, num_heads, head_dim, max_len);
+}
+
+int attn_decode_gqa_batched(const float *q, const float *k_cache, const float *v_cache,
+                            const int32_t *seq_lens, float *out, int32_t num_seqs, int32_t num_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t max_len, float scale,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    if (!q || !k_cache || !v_cache || !seq_lens || !out || !workspace) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS) return ATTN_ERR_INVALID_DIM;
+    if (num_heads <= 0 || num_kv_heads <= 0 || max_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_DIM;
+    if (num_kv_heads > num_heads || num_heads % num_kv_heads != 0) return ATTN_ERR_INVALID_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID_DIM;
+    SeqInts lens{};
+    for (int32_t m = 0; m < num_seqs; ++m) {
+        if (seq_lens[m] < 0 || seq_lens[m] > max_len) return ATTN_ERR_INVALID_DIM;
+        lens.v[m] = seq_lens[m];
+    }
+    if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        !aligned16(workspace))
+        return ATTN_ERR_UNSUPPORTED;
+    int64_t q_elems, cache_elems;
+    if (!checked_mul({num_seqs, num_heads, head_dim}, kMaxElems, &q_elems) ||
+        !checked_mul({num_seqs, num_kv_heads, max_len, head_dim}, kMaxElems, &cache_elems))
+        return ATTN_ERR_OVERFLOW;
+    int64_t units;  // upper bound on pass-1 work units and workspace slots
+    if (!checked_mul({num_seqs, num_heads, attn::decode_max_splits(max_len)}, kMaxElems32, &units))
+        return ATTN_ERR_OVERFLOW;
+    const size_t need = attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_len);
+    if (need == 0) return ATTN_ERR_OVERFLOW;
+    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    const int64_t qb = q_elems * 4, cb = cache_elems * 4;
+    if (overlaps(out, qb, q, qb) || overlaps(out, qb, k_cache, cb) || overlaps(out, qb, v_cache, cb) ||
+        overlaps(out, qb, workspace, (int64_t)need) || overlaps(workspace, (int64_t)need, q, qb) ||
+        overlaps(workspace, (int64_t)need, k_cache, cb) || overlaps(workspace, (int64_t)need, v_cache, cb))
+        return ATTN_ERR_ALIAS;
+
+    const int32_t max_splits = attn::decode_max_splits(max_len);
+    float *ws = static_cast<float *>(workspace);
+    float *ws_acc = ws;
+    float *ws_ml = ws + (size_t)num_seqs * num_heads * max_splits * head_dim;
+    attn::DecodeArgs a{q,   k_cache,      v_cache,   out,        ws_acc,  ws_ml,
+                       lens, num_seqs,    num_heads, num_kv_heads, head_dim, max_len,
+                       max_splits, scale};
+    return from_hip(attn::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int kv_cache_scatter(const float *k_new, const float *v_new, float *k_cache, float *v_cache,
+                     const int32_t *cache_lens, int32_t num_seqs, int32_t n_new, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t max_len, void *stream) {
+    if (!k_new || !v_new || !k_cache || !v_cache || !cache_lens) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS) return ATTN_ERR_INVALID_DIM;
+    if (n_new <= 0 || num_kv_heads <= 0 || max_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_DIM;
+    SeqInts pos{};
+    for (int32_t m = 0; m < num_seqs; ++m) {
+        if (cache_lens[m] < 0 || (int64_t)cache_lens[m] + n_new > max_len) return ATTN_ERR_INVALID_DIM;
+        pos.v[m] = cache_lens[m];
+    }
+    if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+        return ATTN_ERR_UNSUPPORTED;
+    int64_t src_elems, cache_elems, per_seq;
+    if (!checked_mul({num_seqs, n_new, num_kv_heads, head_dim}, kMaxElems, &src_elems) ||
+        !checked_mul({num_seqs, num_kv_heads, max_len, head_dim}, kMaxElems, &cache_elems) ||
+        !checked_mul({n_new, num_kv_heads, head_dim}, kMaxElems32, &per_seq))
+        return ATTN_ERR_OVERFLOW;
+    const int64_t sb = src_elems * 4, cb = cache_elems * 4;
+    if (overlaps(k_cache, cb, v_cache, cb) || overlaps(k_cache, cb, k_new, sb) ||
+        overlaps(k_cache, cb, v_new, sb) || overlaps(v_cache, cb, k_new, sb) || overlaps(v_cache, cb, v_new, sb))
+        return ATTN_ERR_ALIAS;
+
+    attn::ScatterArgs a{k_new, v_new, k_cache, v_cache, pos, num_seqs, n_new, num_kv_heads, head_dim, max_len};
+    return from_hip(attn::launch_kv_scatter(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

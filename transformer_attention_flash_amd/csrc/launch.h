@@ -1,0 +1,61 @@
+// launch.h -- internal interface between the C-ABI layer (attn_api.hip) and
+// the kernel translation units.  Arguments reaching these launchers have been
+// validated on the host already; each launcher only computes its grid and
+// enqueues on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+
+namespace attn {
+
+// Per-sequence host values travel in the kernel arguments (at most 32).
+struct SeqInts {
+    int32_t v[ATTN_MAX_SEQS];
+};
+
+struct ScatterArgs {
+    const float *k_new;
+    const float *v_new;
+    float *k_cache;
+    float *v_cache;
+    SeqInts pos;  // write start position per sequence
+    int32_t M, n_new, Hkv, D, max_len;
+};
+hipError_t launch_kv_scatter(const ScatterArgs &a, hipStream_t stream);
+
+struct PrefillArgs {
+    const float *q;
+    const float *k;
+    const float *v;
+    float *out;
+    int32_t B, S, H, D;
+    float scale;
+    int32_t causal;
+};
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+// Split-KV decode.  Workspace layout (floats):
+//   acc[M][H][max_splits][D]  unnormalised per-split outputs
+//   ml [M][H][max_splits][2]  per-split (running max in log2 units, sum)
+struct DecodeArgs {
+    const float *q;
+    const float *k_cache;
+    const float *v_cache;
+    float *out;
+    float *ws_acc;
+    float *ws_ml;
+    SeqInts lens;
+    int32_t M, H, Hkv, D, max_len;
+    int32_t max_splits;  // capacity of the workspace's split axis
+    float scale;
+};
+// Number of split slots per (sequence, head) the workspace must hold.
+int32_t decode_max_splits(int32_t max_len);
+// Bytes of workspace for (M, H, D, max_len); 0 if it overflows.
+size_t decode_workspace_bytes(int64_t M, int64_t H, int64_t D, int64_t max_len);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace attn
