@@ -7,19 +7,22 @@
 // (`init_kv_cache_gpu`: [num_kv_heads, max_len, head_dim];
 // `init_batched_kv_cache_gpu`: [M, num_kv_heads, max_len, head_dim]).
 //
-// Pass 1 (decode_split_kernel): one wavefront per work unit (sequence m, KV
-// head kh, block of up to 16 query heads of that KV head's group, key split
-// s).  The wave streams the split's K rows once and V rows once straight from
-// HBM and serves every query head of the group from each load: the g query
-// heads sharing a KV head make the scores a dense [16 x d] x [d x 16]
-// contraction per 16 keys (heads padded to 16), which runs on
-// v_mfma_f32_16x16x4_f32 and leaves the VALU free for the softmax.  The
-// split's running max m_s (log2 units), sum l_s and unnormalised output
-// acc_s are written to the workspace.
+// Pass 1 (decode_split_kernel): one workgroup per work unit (sequence m, KV
+// head kh, block of up to 16 query heads of that KV head's group, key block).
+// Its four waves stream adjacent 32-key chunks of the block side by side, each
+// K row and V row read once straight from HBM, and every query head of the
+// group is served from each load: the g query heads sharing a KV head make the
+// scores a dense [16 x d] x [d x 16] contraction per 16 keys (heads padded to
+// 16), which runs on v_mfma_f32_16x16x4_f32 and leaves the VALU free for the
+// softmax.  Each wave's running max m_s (log2 units), sum l_s and
+// unnormalised output acc_s over its chunks form one split, written to the
+// workspace.
 //
-// Pass 2 (decode_combine_kernel): one wavefront per (m, h) merges the splits
-// in index order: M* = max_s m_s, w_s = 2^(m_s - M*), out = sum_s w_s acc_s /
-// sum_s w_s l_s, or zeros when the sequence is empty.
+// Pass 2 (decode_combine_kernel): one workgroup per (m, h) merges the splits:
+// M* = max_s m_s, w_s = 2^(m_s - M*), out = sum_s w_s acc_s / sum_s w_s l_s,
+// or zeros when the sequence is empty.  Each of its 4 waves sums every 4th
+// split and the 4 partial sums are added in a fixed order, so the result is
+// the same on every run.
 //
 // Register layouts of v_mfma_f32_16x16x4_f32 (lane l, i = l % 16, k = l / 16):
 // operand A supplies A[i][k], operand B supplies B[k][i], and output register
@@ -57,8 +60,21 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Cache rows are read exactly once per call: stream them past the caches.
+#ifndef ATTN_DECODE_NT_LOADS
+#define ATTN_DECODE_NT_LOADS 1
+#endif
+template <typename T>
+__device__ __forceinline__ T load_stream(const T *p) {
+#if ATTN_DECODE_NT_LOADS
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, UnitMap map,
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a, UnitMap map,
                                                                 int32_t T, int32_t n_hblk) {
     constexpr int NT = D / 16;     // 16-column tiles of O^T
     constexpr int KV4 = D / 16;    // 16-byte K vectors per lane per 16-key tile
@@ -67,19 +83,24 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, Un
     typedef typename VecN<VW>::type vvec;
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int unit = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (unit >= map.start[a.M]) return;  // whole wave leaves; no block barrier below
+    const int wave = threadIdx.x >> 6;
+    const int unit = blockIdx.x;  // the grid has exactly map.start[M] blocks
 
-    // unit -> (m, kh, head block hb, split s)
+    // unit -> (m, kh, head block hb, key block kblk).  A key block spans
+    // kWavesPerBlock * T keys; wave w of the workgroup takes its chunks
+    // w, w + 4, w + 8, ... so the four waves stream adjacent 32-key chunks of
+    // K (and of V) side by side, and it owns split slot 4 * kblk + w.
     int m = 0;
     while (unit >= map.start[m + 1]) ++m;
     const int L = a.lens.v[m];
-    const int nsplit = (L + T - 1) / T;
+    const int span = kWavesPerBlock * T;
+    const int nkblk = (L + span - 1) / span;
     int rem = unit - map.start[m];
-    const int s = rem % nsplit;
-    rem /= nsplit;
+    const int kblk = rem % nkblk;
+    rem /= nkblk;
     const int hb = rem % n_hblk;
     const int kh = rem / n_hblk;
+    const int s = kblk * kWavesPerBlock + wave;
 
     const int g = a.H / a.Hkv;
     const int hi = lane & 15;  // head column / key row within a tile
@@ -88,8 +109,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, Un
     const bool head_ok = head_in_group < g;
     const int h = kh * g + head_in_group;
 
-    const int k0 = s * T;
-    const int k1 = min(k0 + T, L);
+    const int k0 = kblk * span;        // the workgroup's keys are [k0, k1)
+    const int k1 = min(k0 + span, L);
+    const int kfirst = k0 + kChunk * wave;
+    constexpr int kStep = kChunk * kWavesPerBlock;
 
     // q^T operand, pre-scaled so scores come out in log2 units.
     const float qs = a.scale * kLog2e;
@@ -114,18 +137,38 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, Un
     float m_run = kNegBig;
     float l_run = 0.f;
 
-    for (int kb = k0; kb < k1; kb += kChunk) {
-        // Issue every load of the chunk first: K rows (lane = key row, k-slot
-        // picks 16-byte columns) and V rows (16 lanes cover a row).
-        f32x4 kf[2][KV4];
-        vvec vf[2][4][NVV];
+    // K goes global -> registers -> LDS -> MFMA operand registers.  The MFMA
+    // operand layout puts only four lanes on a key row (64 bytes per row per
+    // instruction), which would make the memory pipeline carry every K line
+    // as two half-line requests; instead each global load instruction reads
+    // two whole rows (1 KiB, fully coalesced) and the operand is gathered from
+    // this wave's LDS tile.  Rows are padded by 4 floats so the 16 keys of an
+    // operand read fall in distinct banks.  V is read straight into operand
+    // registers: 16 lanes cover a row, 256 contiguous bytes per row.  Rows
+    // past the key block's end are clamped to its last row (in bounds) and
+    // masked below.
+    constexpr int KROW = D + 4;                      // LDS pitch of a K row (floats)
+    constexpr int KST = kChunk * D / 4 / kWave;      // 16-byte K vectors per lane per chunk
+    __shared__ __attribute__((aligned(16))) float k_lds[kWavesPerBlock][kChunk * KROW];
+    float *kl = k_lds[wave];
+    f32x4 kst[KST];
+    vvec vf[2][4][NVV];
+    auto load_k = [&](int kb) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int krow = min(kb + 16 * t + hi, k1 - 1);
-#pragma unroll
-            for (int j = 0; j < KV4; ++j)
-                kf[t][j] = *reinterpret_cast<const f32x4 *>(kc + (size_t)krow * D + 16 * j + 4 * kq);
+        for (int u = 0; u < KST; ++u) {
+            const int idx = lane + kWave * u;
+            const int krow = min(kb + idx / (D / 4), k1 - 1);
+            kst[u] = load_stream(reinterpret_cast<const f32x4 *>(kc + (size_t)krow * D + 4 * (idx % (D / 4))));
         }
+    };
+    auto stage_k = [&]() {
+#pragma unroll
+        for (int u = 0; u < KST; ++u) {
+            const int idx = lane + kWave * u;
+            *reinterpret_cast<f32x4 *>(kl + (idx / (D / 4)) * KROW + 4 * (idx % (D / 4))) = kst[u];
+        }
+    };
+    auto load_v = [&](int kb) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -133,21 +176,46 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, Un
                 const int vrow = min(kb + 16 * t + 4 * kq + r, k1 - 1);
 #pragma unroll
                 for (int c = 0; c < NVV; ++c)
-                    vf[t][r][c] = *reinterpret_cast<const vvec *>(vc + (size_t)vrow * D + 64 * c + VW * hi);
+                    vf[t][r][c] = load_stream(reinterpret_cast<const vvec *>(vc + (size_t)vrow * D + 64 * c + VW * hi));
             }
         }
+    };
+
+    // Software pipeline: chunk c+1's K loads are issued as soon as chunk c's
+    // scores no longer need the K registers, and its V loads as soon as the
+    // P.V products of chunk c are issued, so every wave keeps a chunk's worth
+    // of HBM reads in flight while it computes.  The scheduling barriers stop
+    // the compiler from sinking the loads next to their uses.  The loads are
+    // unconditional (exact wait counts across the loop back-edge): after the
+    // last chunk every lane's row clamps to k1 - 1, one row already in cache.
+    load_k(kfirst);
+    __builtin_amdgcn_sched_barrier(0);  // K before V, the order the loop keeps
+    load_v(kfirst);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int kb = kfirst; kb < k1; kb += kStep) {
+
+        // Chunk kb's K rows into this wave's LDS tile (a wave's LDS accesses
+        // are processed in order, so the reads below see these writes and the
+        // previous chunk's reads completed before they are overwritten).
+        stage_k();
 
         // S^T tiles: rows = keys kb + 16t + 4kq + r, columns = heads.
         f32x4 sc[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             f32x4 acc = {0, 0, 0, 0};
+            const float *krow = kl + (16 * t + hi) * KROW + 4 * kq;
 #pragma unroll
-            for (int j = 0; j < KV4; ++j)
+            for (int j = 0; j < KV4; ++j) {
+                const f32x4 kv = *reinterpret_cast<const f32x4 *>(krow + 16 * j);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) acc = mfma16(kf[t][j][c], qreg[j][c], acc);
+                for (int c = 0; c < 4; ++c) acc = mfma16(kv[c], qreg[j][c], acc);
+            }
             sc[t] = acc;
         }
+        __builtin_amdgcn_sched_barrier(0);
+        load_k(kb + kStep);
+        __builtin_amdgcn_sched_barrier(0);
 
         // Online softmax over the chunk; keys >= k1 are masked.
         float mx = -INFINITY;
@@ -188,9 +256,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a, Un
                     o[n] = mfma16(vv, sc[t][r], o[n]);
                 }
             }
+        __builtin_amdgcn_sched_barrier(0);
+        load_v(kb + kStep);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Each k-slot group summed its own keys; combine them.
+    // Each k-slot group summed its own keys; combine them.  A wave whose key
+    // block had no chunk for it still writes its (empty) partial: max kNegBig,
+    // sum 0, output 0, which the merge weighs by 2^(kNegBig - M*) = 0.
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
 
@@ -219,22 +292,26 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a, 
     constexpr int PER = D >= 64 ? D / 64 : 1;  // floats per lane
     constexpr int LANES = D / PER;             // lanes holding output columns
     typedef typename VecN<PER>::type pvec;
+    __shared__ __attribute__((aligned(16))) float part_acc[kWavesPerBlock][D];
+    __shared__ float part_l[kWavesPerBlock];
 
+    // One workgroup per (m, h); its 4 waves take every 4th split.
+    const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    if (w >= a.M * a.H) return;
+    const int w = blockIdx.x;
     const int m = w / a.H;
     const int L = a.lens.v[m];
-    const int nsplit = (L + T - 1) / T;
+    const int nsplit = kWavesPerBlock * ((L + kWavesPerBlock * T - 1) / (kWavesPerBlock * T));
     float *dst = a.out + (size_t)w * D;
 
-    if (nsplit == 0) {
-        if (lane < LANES) *reinterpret_cast<pvec *>(dst + PER * lane) = pvec{};
+    if (nsplit == 0) {  // empty sequence: zeros (uniform over the block)
+        if (wave == 0 && lane < LANES) *reinterpret_cast<pvec *>(dst + PER * lane) = pvec{};
         return;
     }
     const size_t slot0 = (size_t)w * a.max_splits;
     const float *ml = a.ws_ml + 2 * slot0;
 
+    // Every wave finds the global max itself (no barrier needed for it).
     float mstar = -INFINITY;
     for (int s = lane; s < nsplit; s += kWave) mstar = fmaxf(mstar, ml[2 * s]);
 #pragma unroll
@@ -243,28 +320,41 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a, 
     float lsum = 0.f;
     pvec acc{};
     const float *accp = a.ws_acc + slot0 * D + PER * lane;
-    for (int s = 0; s < nsplit; ++s) {
+#pragma unroll 4
+    for (int s = wave; s < nsplit; s += kWavesPerBlock) {
         const float wgt = fast_exp2(ml[2 * s] - mstar);
         lsum += wgt * ml[2 * s + 1];
         if (lane < LANES) acc += wgt * *reinterpret_cast<const pvec *>(accp + (size_t)s * D);
     }
-    if (lane < LANES) *reinterpret_cast<pvec *>(dst + PER * lane) = acc * (1.0f / lsum);
+    if (lane < LANES) *reinterpret_cast<pvec *>(&part_acc[wave][PER * lane]) = acc;
+    if (lane == 0) part_l[wave] = lsum;
+    __syncthreads();
+    if (wave == 0 && lane < LANES) {
+        pvec tot = *reinterpret_cast<const pvec *>(&part_acc[0][PER * lane]);
+        float ltot = part_l[0];
+#pragma unroll
+        for (int i = 1; i < kWavesPerBlock; ++i) {
+            tot += *reinterpret_cast<const pvec *>(&part_acc[i][PER * lane]);
+            ltot += part_l[i];
+        }
+        *reinterpret_cast<pvec *>(dst + PER * lane) = tot * (1.0f / ltot);
+    }
 }
 
-// Smallest split length (keys per work unit) for a cache of max_len rows: a
-// multiple of the chunk that keeps the workspace's split axis at <= 256 slots.
+// Smallest split length (keys per wave) for a cache of max_len rows: a
+// power of two >= 64 that keeps the workspace's split axis at <= 256 slots.
 int32_t min_split(int32_t max_len) {
     int32_t t = 64;
     while ((int64_t)t * 256 < max_len) t *= 2;
     return t;
 }
 
+// Key blocks of sequence length L for a split length T.
+int32_t key_blocks(int32_t L, int32_t T) { return (L + kWavesPerBlock * T - 1) / (kWavesPerBlock * T); }
+
 }  // namespace
 
-int32_t decode_max_splits(int32_t max_len) {
-    const int32_t t = min_split(max_len);
-    return (max_len + t - 1) / t;
-}
+int32_t decode_max_splits(int32_t max_len) { return kWavesPerBlock * key_blocks(max_len, min_split(max_len)); }
 
 size_t decode_workspace_bytes(int64_t M, int64_t H, int64_t D, int64_t max_len) {
     const int64_t slots = M * H * (int64_t)decode_max_splits((int32_t)max_len);
@@ -278,26 +368,29 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     // while the grid would still have at least kMinUnits waves, so long
     // sequences get long splits (less partial traffic) and short batches still
     // fill the 256 compute units.
-    constexpr int64_t kMinUnits = 4096;
-    auto units_for = [&](int32_t t) {
+#ifndef ATTN_DECODE_MIN_UNITS
+#define ATTN_DECODE_MIN_UNITS 4096
+#endif
+    constexpr int64_t kMinUnits = ATTN_DECODE_MIN_UNITS;
+    auto waves_for = [&](int32_t t) {
         int64_t u = 0;
-        for (int i = 0; i < a.M; ++i) u += (a.lens.v[i] + t - 1) / t;
-        return u * a.Hkv * n_hblk;
+        for (int i = 0; i < a.M; ++i) u += key_blocks(a.lens.v[i], t);
+        return u * a.Hkv * n_hblk * kWavesPerBlock;
     };
     int32_t T = min_split(a.max_len);
-    while (T < a.max_len && units_for(2 * T) >= kMinUnits) T *= 2;
+    while (T < a.max_len && waves_for(2 * T) >= kMinUnits) T *= 2;
 
     UnitMap map;
     int32_t acc = 0;
     for (int i = 0; i < a.M; ++i) {
         map.start[i] = acc;
-        acc += ((a.lens.v[i] + T - 1) / T) * a.Hkv * n_hblk;
+        acc += key_blocks(a.lens.v[i], T) * a.Hkv * n_hblk;
     }
     for (int i = a.M; i <= ATTN_MAX_SEQS; ++i) map.start[i] = acc;
 
     dim3 block(kThreads);
     if (acc > 0) {
-        dim3 grid((acc + kWavesPerBlock - 1) / kWavesPerBlock);
+        dim3 grid(acc);
         switch (a.D) {
             case 32: decode_split_kernel<32><<<grid, block, 0, stream>>>(a, map, T, n_hblk); break;
             case 64: decode_split_kernel<64><<<grid, block, 0, stream>>>(a, map, T, n_hblk); break;
@@ -307,7 +400,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    dim3 grid2((a.M * a.H + kWavesPerBlock - 1) / kWavesPerBlock);
+    dim3 grid2(a.M * a.H);
     switch (a.D) {
         case 32: decode_combine_kernel<32><<<grid2, block, 0, stream>>>(a, T); break;
         case 64: decode_combine_kernel<64><<<grid2, block, 0, stream>>>(a, T); break;
