@@ -19,10 +19,11 @@
 // workspace.
 //
 // Pass 2 (decode_combine_kernel): one workgroup per (m, h) merges the splits:
-// M* = max_s m_s, w_s = 2^(m_s - M*), out = sum_s w_s acc_s / sum_s w_s l_s,
-// or zeros when the sequence is empty.  Each of its 4 waves sums every 4th
-// split and the 4 partial sums are added in a fixed order, so the result is
-// the same on every run.
+// with M* = max_s m_s and w_s = 2^(m_s - M*), out = sum_s w_s acc_s /
+// sum_s w_s l_s, or zeros when the sequence is empty.  Each of its 4 waves
+// folds every 4th split in with a running max (the same identity applied
+// incrementally) and the 4 results are merged in a fixed order, so the
+// result is the same on every run.
 //
 // Register layouts of v_mfma_f32_16x16x4_f32 (lane l, i = l % 16, k = l / 16):
 // operand A supplies A[i][k], operand B supplies B[k][i], and output register
@@ -30,6 +31,8 @@
 // keys, columns = heads), so that output register r of a lane is exactly the
 // operand-B value that lane supplies at key step r of the P.V contraction
 // O^T = V^T P^T: no data moves between the two products.
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -52,8 +55,14 @@ __host__ __device__ constexpr int ocol(int n, int i) {
     }
 }
 
+// Work decomposition of one call, computed on the host from the lengths.
+// Every (kh, head block) of sequence m is cut into nkblk[m] key blocks of
+// span[m] keys (a multiple of 4 waves x 32 keys; the last block may be
+// shorter); workgroup start[m] + (kh * n_hblk + hb) * nkblk[m] + kblk runs one.
 struct UnitMap {
-    int32_t start[ATTN_MAX_SEQS + 1];  // first unit of each sequence; start[M] = total
+    int32_t start[ATTN_MAX_SEQS + 1];  // first workgroup of each sequence; start[M] = grid size
+    int32_t nkblk[ATTN_MAX_SEQS];
+    int32_t span[ATTN_MAX_SEQS];
 };
 
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
@@ -75,7 +84,7 @@ __device__ __forceinline__ T load_stream(const T *p) {
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a, UnitMap map,
-                                                                int32_t T, int32_t n_hblk) {
+                                                                int32_t n_hblk) {
     constexpr int NT = D / 16;     // 16-column tiles of O^T
     constexpr int KV4 = D / 16;    // 16-byte K vectors per lane per 16-key tile
     constexpr int VW = D >= 64 ? 4 : 2;  // floats per V vector
@@ -86,15 +95,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     const int wave = threadIdx.x >> 6;
     const int unit = blockIdx.x;  // the grid has exactly map.start[M] blocks
 
-    // unit -> (m, kh, head block hb, key block kblk).  A key block spans
-    // kWavesPerBlock * T keys; wave w of the workgroup takes its chunks
-    // w, w + 4, w + 8, ... so the four waves stream adjacent 32-key chunks of
-    // K (and of V) side by side, and it owns split slot 4 * kblk + w.
+    // unit -> (m, kh, head block hb, key block kblk).  Wave w of the
+    // workgroup takes chunks w, w + 4, w + 8, ... of the key block, so the
+    // four waves stream adjacent 32-key chunks of K (and of V) side by side,
+    // and it owns split slot 4 * kblk + w.
     int m = 0;
     while (unit >= map.start[m + 1]) ++m;
     const int L = a.lens.v[m];
-    const int span = kWavesPerBlock * T;
-    const int nkblk = (L + span - 1) / span;
+    const int span = map.span[m];
+    const int nkblk = map.nkblk[m];
     int rem = unit - map.start[m];
     const int kblk = rem % nkblk;
     rem /= nkblk;
@@ -182,9 +191,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     };
 
     // Software pipeline: chunk c+1's K loads are issued as soon as chunk c's
-    // scores no longer need the K registers, and its V loads as soon as the
-    // P.V products of chunk c are issued, so every wave keeps a chunk's worth
-    // of HBM reads in flight while it computes.  The scheduling barriers stop
+    // K rows are staged in LDS, and its V loads as soon as the P.V products of
+    // chunk c are issued, so every wave keeps about a chunk's worth of HBM
+    // reads in flight while it computes.  The scheduling barriers stop
     // the compiler from sinking the loads next to their uses.  The loads are
     // unconditional (exact wait counts across the loop back-edge): after the
     // last chunk every lane's row clamps to k1 - 1, one row already in cache.
@@ -198,6 +207,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
         // are processed in order, so the reads below see these writes and the
         // previous chunk's reads completed before they are overwritten).
         stage_k();
+        __builtin_amdgcn_sched_barrier(0);
+        // The staging registers are free again: chunk c+1's K loads go out now
+        // and have this chunk's scores, softmax and P.V to arrive.
+        load_k(kb + kStep);
+        __builtin_amdgcn_sched_barrier(0);
 
         // S^T tiles: rows = keys kb + 16t + 4kq + r, columns = heads.
         f32x4 sc[2];
@@ -213,9 +227,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
             }
             sc[t] = acc;
         }
-        __builtin_amdgcn_sched_barrier(0);
-        load_k(kb + kStep);
-        __builtin_amdgcn_sched_barrier(0);
 
         // Online softmax over the chunk; keys >= k1 are masked.
         float mx = -INFINITY;
@@ -288,20 +299,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a, int32_t T) {
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a, UnitMap map) {
     constexpr int PER = D >= 64 ? D / 64 : 1;  // floats per lane
     constexpr int LANES = D / PER;             // lanes holding output columns
+    constexpr int BATCH = 8;                   // splits whose loads are in flight together
     typedef typename VecN<PER>::type pvec;
     __shared__ __attribute__((aligned(16))) float part_acc[kWavesPerBlock][D];
-    __shared__ float part_l[kWavesPerBlock];
+    __shared__ float part_m[kWavesPerBlock], part_l[kWavesPerBlock];
 
-    // One workgroup per (m, h); its 4 waves take every 4th split.
+    // One workgroup per (m, h); wave w merges splits w, w + 4, ... with a
+    // running max, then wave 0 merges the four results.  The order is fixed,
+    // so the output is identical from run to run.
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = blockIdx.x;
     const int m = w / a.H;
-    const int L = a.lens.v[m];
-    const int nsplit = kWavesPerBlock * ((L + kWavesPerBlock * T - 1) / (kWavesPerBlock * T));
+    const int nsplit = kWavesPerBlock * map.nkblk[m];
     float *dst = a.out + (size_t)w * D;
 
     if (nsplit == 0) {  // empty sequence: zeros (uniform over the block)
@@ -310,51 +323,102 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a, 
     }
     const size_t slot0 = (size_t)w * a.max_splits;
     const float *ml = a.ws_ml + 2 * slot0;
-
-    // Every wave finds the global max itself (no barrier needed for it).
-    float mstar = -INFINITY;
-    for (int s = lane; s < nsplit; s += kWave) mstar = fmaxf(mstar, ml[2 * s]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, off));
-
-    float lsum = 0.f;
-    pvec acc{};
     const float *accp = a.ws_acc + slot0 * D + PER * lane;
-#pragma unroll 4
-    for (int s = wave; s < nsplit; s += kWavesPerBlock) {
-        const float wgt = fast_exp2(ml[2 * s] - mstar);
-        lsum += wgt * ml[2 * s + 1];
-        if (lane < LANES) acc += wgt * *reinterpret_cast<const pvec *>(accp + (size_t)s * D);
+
+    float m_run = kNegBig, l_run = 0.f;
+    pvec acc{};
+    for (int s0 = wave; s0 < nsplit; s0 += kWavesPerBlock * BATCH) {
+        float mv[BATCH], lv[BATCH];
+        pvec av[BATCH];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const int s = s0 + kWavesPerBlock * b;
+            const bool ok = s < nsplit;
+            mv[b] = ok ? ml[2 * s] : kNegBig;
+            lv[b] = ok ? ml[2 * s + 1] : 0.f;
+            av[b] = (ok && lane < LANES) ? *reinterpret_cast<const pvec *>(accp + (size_t)s * D) : pvec{};
+        }
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const float m_new = fmaxf(m_run, mv[b]);
+            const float keep = fast_exp2(m_run - m_new), take = fast_exp2(mv[b] - m_new);
+            l_run = l_run * keep + lv[b] * take;
+            acc = acc * keep + av[b] * take;
+            m_run = m_new;
+        }
     }
     if (lane < LANES) *reinterpret_cast<pvec *>(&part_acc[wave][PER * lane]) = acc;
-    if (lane == 0) part_l[wave] = lsum;
+    if (lane == 0) {
+        part_m[wave] = m_run;
+        part_l[wave] = l_run;
+    }
     __syncthreads();
     if (wave == 0 && lane < LANES) {
-        pvec tot = *reinterpret_cast<const pvec *>(&part_acc[0][PER * lane]);
-        float ltot = part_l[0];
+        float mstar = part_m[0];
 #pragma unroll
-        for (int i = 1; i < kWavesPerBlock; ++i) {
-            tot += *reinterpret_cast<const pvec *>(&part_acc[i][PER * lane]);
-            ltot += part_l[i];
+        for (int i = 1; i < kWavesPerBlock; ++i) mstar = fmaxf(mstar, part_m[i]);
+        pvec tot{};
+        float ltot = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWavesPerBlock; ++i) {
+            const float wgt = fast_exp2(part_m[i] - mstar);
+            tot += wgt * *reinterpret_cast<const pvec *>(&part_acc[i][PER * lane]);
+            ltot += wgt * part_l[i];
         }
         *reinterpret_cast<pvec *>(dst + PER * lane) = tot * (1.0f / ltot);
     }
 }
 
-// Smallest split length (keys per wave) for a cache of max_len rows: a
-// power of two >= 64 that keeps the workspace's split axis at <= 256 slots.
-int32_t min_split(int32_t max_len) {
-    int32_t t = 64;
-    while ((int64_t)t * 256 < max_len) t *= 2;
-    return t;
+constexpr int32_t kSpanQuantum = kWavesPerBlock * kChunk;  // keys: one chunk per wave
+constexpr int32_t kMaxKeyBlocks = 64;                        // per (sequence, head): workspace bound
+
+// Smallest key-block span for a cache of max_len rows: a power-of-two multiple
+// of the quantum that keeps a sequence at <= kMaxKeyBlocks key blocks.
+int32_t span_floor(int32_t max_len) {
+    int32_t s = kSpanQuantum;
+    while ((max_len + s - 1) / s > kMaxKeyBlocks) s *= 2;
+    return s;
 }
 
-// Key blocks of sequence length L for a split length T.
-int32_t key_blocks(int32_t L, int32_t T) { return (L + kWavesPerBlock * T - 1) / (kWavesPerBlock * T); }
+// Workgroups of decode_split_kernel<D> that fit on the device at once (CUs x
+// resident blocks per CU), queried once per device and head_dim.
+#ifndef ATTN_DECODE_ROUNDS
+#define ATTN_DECODE_ROUNDS 2
+#endif
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_capacity[kMaxDevices][3];
+
+template <int D>
+int32_t query_capacity() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 512;
+    const int slot = D == 32 ? 0 : D == 64 ? 1 : 2;
+    int32_t cap = g_capacity[dev][slot].load(std::memory_order_relaxed);
+    if (cap > 0) return cap;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0 ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D>, kThreads, 0) != hipSuccess ||
+        per_cu <= 0)
+        return 512;
+    cap = cus * per_cu;
+    g_capacity[dev][slot].store(cap, std::memory_order_relaxed);
+    return cap;
+}
+
+int32_t capacity_for(int32_t D) {
+    switch (D) {
+        case 32: return query_capacity<32>();
+        case 64: return query_capacity<64>();
+        default: return query_capacity<128>();
+    }
+}
 
 }  // namespace
 
-int32_t decode_max_splits(int32_t max_len) { return kWavesPerBlock * key_blocks(max_len, min_split(max_len)); }
+int32_t decode_max_splits(int32_t max_len) {
+    const int32_t sf = span_floor(max_len);
+    return kWavesPerBlock * ((max_len + sf - 1) / sf);
+}
 
 size_t decode_workspace_bytes(int64_t M, int64_t H, int64_t D, int64_t max_len) {
     const int64_t slots = M * H * (int64_t)decode_max_splits((int32_t)max_len);
@@ -364,37 +428,49 @@ size_t decode_workspace_bytes(int64_t M, int64_t H, int64_t D, int64_t max_len) 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     const int32_t g = a.H / a.Hkv;
     const int32_t n_hblk = (g + 15) / 16;
-    // Split length: the smallest workspace-compatible power of two is doubled
-    // while the grid would still have at least kMinUnits waves, so long
-    // sequences get long splits (less partial traffic) and short batches still
-    // fill the 256 compute units.
-#ifndef ATTN_DECODE_MIN_UNITS
-#define ATTN_DECODE_MIN_UNITS 4096
-#endif
-    constexpr int64_t kMinUnits = ATTN_DECODE_MIN_UNITS;
-    auto waves_for = [&](int32_t t) {
-        int64_t u = 0;
-        for (int i = 0; i < a.M; ++i) u += key_blocks(a.lens.v[i], t);
-        return u * a.Hkv * n_hblk * kWavesPerBlock;
-    };
-    int32_t T = min_split(a.max_len);
-    while (T < a.max_len && waves_for(2 * T) >= kMinUnits) T *= 2;
+    const int64_t units_per_seq = (int64_t)a.Hkv * n_hblk;
+
+    // Balance: cut every sequence's keys into key blocks of (nearly) equal
+    // size, sized so the whole grid is ATTN_DECODE_ROUNDS times what the device
+    // holds at once.  Equal blocks finish together, so no lone partial round
+    // runs at the end.  Spans are multiples of 4 x 32 keys and at least
+    // span_floor(max_len), which bounds the workspace.
+    int64_t total = 0;
+    for (int i = 0; i < a.M; ++i) total += a.lens.v[i];
+    total *= units_per_seq;
+    const double target = (double)capacity_for(a.D) * ATTN_DECODE_ROUNDS;
+    const int32_t sf = span_floor(a.max_len);
 
     UnitMap map;
     int32_t acc = 0;
     for (int i = 0; i < a.M; ++i) {
+        const int32_t L = a.lens.v[i];
         map.start[i] = acc;
-        acc += key_blocks(a.lens.v[i], T) * a.Hkv * n_hblk;
+        map.nkblk[i] = 0;
+        map.span[i] = sf;
+        if (L == 0) continue;
+        const double want = (double)L * target / (double)total;  // key blocks per (kh, hb) unit
+        const int32_t nb = want < 1.0 ? 1 : (int32_t)(want + 0.5);
+        int32_t span = (L + nb - 1) / nb;
+        span = ((span + kSpanQuantum - 1) / kSpanQuantum) * kSpanQuantum;
+        if (span < sf) span = sf;
+        map.span[i] = span;
+        map.nkblk[i] = (L + span - 1) / span;
+        acc += map.nkblk[i] * (int32_t)units_per_seq;
     }
     for (int i = a.M; i <= ATTN_MAX_SEQS; ++i) map.start[i] = acc;
+    for (int i = a.M; i < ATTN_MAX_SEQS; ++i) {
+        map.nkblk[i] = 0;
+        map.span[i] = sf;
+    }
 
     dim3 block(kThreads);
     if (acc > 0) {
         dim3 grid(acc);
         switch (a.D) {
-            case 32: decode_split_kernel<32><<<grid, block, 0, stream>>>(a, map, T, n_hblk); break;
-            case 64: decode_split_kernel<64><<<grid, block, 0, stream>>>(a, map, T, n_hblk); break;
-            case 128: decode_split_kernel<128><<<grid, block, 0, stream>>>(a, map, T, n_hblk); break;
+            case 32: decode_split_kernel<32><<<grid, block, 0, stream>>>(a, map, n_hblk); break;
+            case 64: decode_split_kernel<64><<<grid, block, 0, stream>>>(a, map, n_hblk); break;
+            case 128: decode_split_kernel<128><<<grid, block, 0, stream>>>(a, map, n_hblk); break;
             default: return hipErrorInvalidValue;
         }
         hipError_t e = hipGetLastError();
@@ -402,9 +478,9 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     }
     dim3 grid2(a.M * a.H);
     switch (a.D) {
-        case 32: decode_combine_kernel<32><<<grid2, block, 0, stream>>>(a, T); break;
-        case 64: decode_combine_kernel<64><<<grid2, block, 0, stream>>>(a, T); break;
-        case 128: decode_combine_kernel<128><<<grid2, block, 0, stream>>>(a, T); break;
+        case 32: decode_combine_kernel<32><<<grid2, block, 0, stream>>>(a, map); break;
+        case 64: decode_combine_kernel<64><<<grid2, block, 0, stream>>>(a, map); break;
+        case 128: decode_combine_kernel<128><<<grid2, block, 0, stream>>>(a, map); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

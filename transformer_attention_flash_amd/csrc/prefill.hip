@@ -193,8 +193,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int
                 psum += s[v];
             }
             l_run = l_run * alpha + psum;
+            // Once the running maxima settle, alpha is 1 in every lane: skip the
+            // 16*NT multiplies then (a wave-uniform branch).
+#ifndef ATTN_PREFILL_SKIP_RESCALE
+#define ATTN_PREFILL_SKIP_RESCALE 1
+#endif
+            if (!ATTN_PREFILL_SKIP_RESCALE || __any(alpha != 1.0f)) {
 #pragma unroll
-            for (int n = 0; n < NT; ++n) o[n] *= alpha;
+                for (int n = 0; n < NT; ++n) o[n] *= alpha;
+            }
 
             // O^T += V^T P^T: at key step v this lane supplies V[key][NT*li + n]
             // for n-tile n and P^T[key][my_q] = s[v].
