@@ -14,9 +14,10 @@
 //
 // Work decomposition: a workgroup owns BM = 128 queries of one (b, h); each
 // of its 4 wavefronts owns 32 of them and keeps its Q slice in VGPRs and its
-// 32 x D output accumulator in registers.  K and V tiles of BN = 32 keys are
-// staged through LDS, the next tile's global loads in flight (in registers)
-// while the current tile is consumed.  Both products run on v_mfma_f32_32x32x2_f32.
+// 32 x D output accumulator in registers.  K and V tiles of BN = 32 keys go
+// from HBM straight into a double-buffered LDS tile (global_load_lds, no
+// register staging); the next tile's transfer is in flight while the current
+// one is consumed, with one workgroup barrier per tile.  Both products run on v_mfma_f32_32x32x2_f32.
 //
 // Register layouts of v_mfma_f32_32x32x2_f32 (lane l, i = l % 32, k = l / 32):
 // operand A supplies A[i][k], operand B supplies B[k][i], and output register
@@ -35,8 +36,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int BM = 32 * kWaves;  // queries per workgroup
-constexpr int BN = 32;           // keys per LDS tile
-constexpr int kPad = 4;          // floats of padding per K row in LDS (bank spread)
+constexpr int BN = 32;           // keys per LDS tile (one 32-key MFMA sub-tile)
 
 __device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -45,18 +45,42 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16 &c) {
 // Key row (within a 32-key sub-tile) / output row of register v in lane-half k.
 __device__ __forceinline__ int mrow(int v, int k) { return 8 * (v >> 2) + 4 * k + (v & 3); }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One 16-byte global -> LDS transfer per lane (global_load_lds_dwordx4): lane l's
+// 16 bytes land at lds_base + 16 l, lds_base being uniform over the wave.
+__device__ __forceinline__ void dma16(const float *src, float *lds_base) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), (lds_void_t *)lds_base, 16, 0, 0);
+}
+
+// Wait until this wave has no global loads (including LDS transfers) in flight.
+__device__ __forceinline__ void wait_vmem_all() {
+    // s_waitcnt vmcnt(0), expcnt/lgkmcnt unconstrained (7 and 15).
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int32_t n_qtiles,
                                                               int32_t xcd_remap) {
-    constexpr int NT = D / 32;         // 32-row tiles of O^T; also floats per lane per V row
-    constexpr int QV = D / 8;          // 16-byte Q/K vectors per lane
-    constexpr int KROW = D + kPad;     // LDS row pitch of K (floats)
-    constexpr int TILE_VEC = BN * D / 4;              // 16-byte vectors per K (or V) tile
-    constexpr int LD_PER_THREAD = TILE_VEC / kThreads;  // per tensor
+    constexpr int NT = D / 32;          // 32-row tiles of O^T; also floats per lane per V row
+    constexpr int QV = D / 8;           // 16-byte Q/K vectors per lane
+    constexpr int CPR = D / 4;          // 16-byte chunks per K/V row
+    constexpr int RPI = kWave / CPR;    // rows moved by one wave-wide 1 KiB transfer
+    constexpr int XPW = BN / RPI / kWaves;  // transfers per wave per tensor per tile
+    constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;  // K chunk swizzle mask
     typedef typename VecN<NT>::type vrow_t;
+    static_assert(XPW >= 1 && XPW * RPI * kWaves == BN, "tile must split evenly over the waves");
 
-    __shared__ __attribute__((aligned(16))) float Ks[BN * KROW];
-    __shared__ __attribute__((aligned(16))) float Vs[BN * D];
+    // Double-buffered K/V tiles.  K chunk c of row r sits at chunk position
+    // c ^ (r & SWZ), so the 16 rows of one half-wave operand read hit distinct
+    // banks; V rows are read contiguously and are stored as they are.
+    // Separate objects (not one [2][..] array) so the compiler can see that a
+    // transfer into one buffer does not alias reads of the other and does not
+    // make those reads wait for it.
+    __shared__ __attribute__((aligned(16))) float Ks0[BN * D];
+    __shared__ __attribute__((aligned(16))) float Vs0[BN * D];
+    __shared__ __attribute__((aligned(16))) float Ks1[BN * D];
+    __shared__ __attribute__((aligned(16))) float Vs1[BN * D];
 
     // ---- block -> (b, h, query tile); heavy causal tiles first, and with
     // xcd_remap the query tiles of one (b, h) stay on one XCD (blocks are
@@ -118,106 +142,90 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int
     const int n_ktiles_all = (S + BN - 1) / BN;
     const int n_ktiles = CAUSAL ? min(n_ktiles_all, (min(q0 + BM, S) - 1) / BN + 1) : n_ktiles_all;
 
-    // Cooperative global -> register loads of one K/V tile.
-    f32x4 kbuf[LD_PER_THREAD], vbuf[LD_PER_THREAD];
-    auto load_tile = [&](int kt) {
+    // Each wave moves XPW 1 KiB pieces of the K tile and of the V tile straight
+    // into LDS.  Keys past S read row S - 1 (in bounds); their scores are masked
+    // and their probabilities are exactly 0, so the values never matter.
+    auto issue_tile = [&](int kt, float *kdst, float *vdst) {
 #pragma unroll
-        for (int u = 0; u < LD_PER_THREAD; ++u) {
-            const int idx = tid + u * kThreads;
-            const int r = idx / (D / 4), c4 = idx % (D / 4);
-            const int key = kt * BN + r;
-            if (key < S) {
-                kbuf[u] = *reinterpret_cast<const f32x4 *>(kg + (size_t)key * row_stride + 4 * c4);
-                vbuf[u] = *reinterpret_cast<const f32x4 *>(vg + (size_t)key * row_stride + 4 * c4);
-            } else {
-                kbuf[u] = f32x4{0, 0, 0, 0};
-                vbuf[u] = f32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int u = 0; u < LD_PER_THREAD; ++u) {
-            const int idx = tid + u * kThreads;
-            const int r = idx / (D / 4), c4 = idx % (D / 4);
-            *reinterpret_cast<f32x4 *>(&Ks[r * KROW + 4 * c4]) = kbuf[u];
-            *reinterpret_cast<f32x4 *>(&Vs[r * D + 4 * c4]) = vbuf[u];
+        for (int u = 0; u < XPW; ++u) {
+            const int piece = wave * XPW + u;
+            const int row = piece * RPI + lane / CPR;
+            const int chunk = lane % CPR;
+            const size_t key = (size_t)min(kt * BN + row, S - 1);
+            dma16(kg + key * row_stride + 4 * (chunk ^ (row & SWZ)), kdst + piece * 256);
+            dma16(vg + key * row_stride + 4 * chunk, vdst + piece * 256);
         }
     };
 
-    load_tile(0);
-    store_tile();
-    __syncthreads();
+    // One tile: wait for it, barrier, start the next tile's transfer into the
+    // other buffer, consume this one.
+    auto step = [&](int kt, const float *Kt, const float *Vt, float *Kn, float *Vn) {
+        wait_vmem_all();  // this wave's share of tile kt has landed
+        __syncthreads();  // ... and every other wave's; all are done with tile kt-1
+        if (kt + 1 < n_ktiles) issue_tile(kt + 1, Kn, Vn);
 
-    for (int kt = 0; kt < n_ktiles; ++kt) {
-        if (kt + 1 < n_ktiles) load_tile(kt + 1);
+        const int ks0 = kt * BN;  // first key of the tile
+        if (CAUSAL && ks0 > qw0 + 31) return;  // whole tile above this wave's diagonal
 
+        // S^T = K Q^T over D (k-slot lk of step (j, c) is column 8j + 4lk + c).
+        f32x16 s = f32x16{};
+        const float *kbase = Kt + li * D;
 #pragma unroll
-        for (int st = 0; st < BN / 32; ++st) {
-            const int ks0 = kt * BN + st * 32;  // first key of the sub-tile
-            if (ks0 >= S) break;
-            if (CAUSAL && ks0 > qw0 + 31) break;  // whole sub-tile above this wave's diagonal
+        for (int j = 0; j < QV; ++j) {
+            const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + 4 * ((2 * j + lk) ^ (li & SWZ)));
+#pragma unroll
+            for (int c = 0; c < 4; ++c) s = mfma32(kv[c], qreg[j][c], s);
+        }
 
-            // S^T = K Q^T over D (k-slot lk of step (j, c) is column 8j + 4lk + c).
-            f32x16 s = f32x16{};
-            const float *krow = &Ks[(st * 32 + li) * KROW + 4 * lk];
-#pragma unroll
-            for (int j = 0; j < QV; ++j) {
-                const f32x4 kv = *reinterpret_cast<const f32x4 *>(krow + 8 * j);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) s = mfma32(kv[c], qreg[j][c], s);
-            }
-
-            // Mask: keys past S, and (causal) keys after the query.
-            const bool need_mask = (ks0 + 32 > S) || (CAUSAL && ks0 + 31 > qw0);
-            if (need_mask) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int key = ks0 + mrow(v, lk);
-                    const bool dead = key >= S || (CAUSAL && key > my_q);
-                    s[v] = dead ? -INFINITY : s[v];
-                }
-            }
-
-            float mx = s[0];
-#pragma unroll
-            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - m_new);
-            m_run = m_new;
-            float psum = 0.f;
+        // Mask: keys past S, and (causal) keys after the query.
+        const bool need_mask = (ks0 + 32 > S) || (CAUSAL && ks0 + 31 > qw0);
+        if (need_mask) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                s[v] = fast_exp2(s[v] - m_new);
-                psum += s[v];
-            }
-            l_run = l_run * alpha + psum;
-            // Once the running maxima settle, alpha is 1 in every lane: skip the
-            // 16*NT multiplies then (a wave-uniform branch).
-#ifndef ATTN_PREFILL_SKIP_RESCALE
-#define ATTN_PREFILL_SKIP_RESCALE 1
-#endif
-            if (!ATTN_PREFILL_SKIP_RESCALE || __any(alpha != 1.0f)) {
-#pragma unroll
-                for (int n = 0; n < NT; ++n) o[n] *= alpha;
-            }
-
-            // O^T += V^T P^T: at key step v this lane supplies V[key][NT*li + n]
-            // for n-tile n and P^T[key][my_q] = s[v].
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const vrow_t vv = *reinterpret_cast<const vrow_t *>(&Vs[(st * 32 + mrow(v, lk)) * D + NT * li]);
-#pragma unroll
-                for (int n = 0; n < NT; ++n) o[n] = mfma32(vget<NT>(vv, n), s[v], o[n]);
+                const int key = ks0 + mrow(v, lk);
+                const bool dead = key >= S || (CAUSAL && key > my_q);
+                s[v] = dead ? -INFINITY : s[v];
             }
         }
 
-        if (kt + 1 < n_ktiles) {
-            __syncthreads();
-            store_tile();
-            __syncthreads();
+        float mx = s[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            s[v] = fast_exp2(s[v] - m_new);
+            psum += s[v];
         }
+        l_run = l_run * alpha + psum;
+        // Once the running maxima settle, alpha is 1 in every lane: skip the
+        // 16*NT multiplies then (a wave-uniform branch).
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) o[n] *= alpha;
+        }
+
+        // O^T += V^T P^T: at key step v this lane supplies V[key][NT*li + n]
+        // for n-tile n and P^T[key][my_q] = s[v].
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const vrow_t vv = *reinterpret_cast<const vrow_t *>(Vt + mrow(v, lk) * D + NT * li);
+#pragma unroll
+            for (int n = 0; n < NT; ++n) o[n] = mfma32(vget<NT>(vv, n), s[v], o[n]);
+        }
+    };
+
+    // Two-stage pipeline with one barrier per tile: after a tile's barrier every
+    // wave has finished the previous tile, so the next tile can be transferred
+    // into the buffer the previous one used while this one is consumed.
+    issue_tile(0, Ks0, Vs0);
+    for (int kt = 0; kt < n_ktiles; kt += 2) {
+        step(kt, Ks0, Vs0, Ks1, Vs1);
+        if (kt + 1 < n_ktiles) step(kt + 1, Ks1, Vs1, Ks0, Vs0);
     }
 
     // ---- normalise and store: lane holds query my_q, columns NT*row + n.
