@@ -15,7 +15,9 @@ and follows the definitions cited there:
 * decode -- trueno-gpu ``incremental_attention_gpu``; realizar 0.8.5
   ``src/cuda/executor/cache_from_cache_from_kv_cache.rs``,
   ``init_kv_cache_gpu`` / ``init_batched_kv_cache_gpu`` (GQA cache layout);
-* scatter -- trueno-gpu ``kv_cache_scatter_gpu``.
+* scatter -- trueno-gpu ``kv_cache_scatter_gpu``;
+* chunked prefill behind a cache -- trustformers-core ``attention_prefill_gpu_to_gpu``
+  (the offset mask its from-empty-cache mask leaves to other paths).
 
 ``brute.py`` is a second, independent numpy fp64 formulation used only to
 cross-check this one on tiny shapes.
@@ -55,6 +57,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_decode_rows.restype = ctypes.c_int
     lib.oracle_scatter.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64]
     lib.oracle_scatter.restype = ctypes.c_int
+    lib.oracle_prefill_cached.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, ctypes.c_float]
+    lib.oracle_prefill_cached.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -151,6 +155,22 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_scatter rejected its arguments")
         return k_cache, v_cache
+
+    def prefill_cached(self, q, k_new, v_new, k_cache, v_cache, cache_lens, M, n_new, H, Hkv, d, max_len,
+                       scale):
+        """Chunk of n_new tokens behind cache_lens[m] cached rows; out is [M, n_new, H*d]."""
+        q, k_new, v_new = _f32(q), _f32(k_new), _f32(v_new)
+        k_cache, v_cache = _f32(k_cache), _f32(v_cache)
+        cache_lens = np.ascontiguousarray(cache_lens, dtype=np.int32)
+        assert q.size == M * n_new * H * d and k_new.size == M * n_new * Hkv * d == v_new.size
+        assert k_cache.size == M * Hkv * max_len * d == v_cache.size and cache_lens.size == M
+        out = np.empty(M * n_new * H * d, dtype=np.float64)
+        rc = self.lib.oracle_prefill_cached(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                            _ptr(cache_lens), _ptr(out), M, n_new, H, Hkv, d, max_len,
+                                            float(np.float32(scale)))
+        if rc != 0:
+            raise ValueError("oracle_prefill_cached rejected its arguments")
+        return out.reshape(M, n_new, H * d)
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())

@@ -67,3 +67,25 @@ def scatter(k_new, v_new, k_cache, v_cache, cache_lens, M, n_new, Hkv, d, max_le
         kc[m][:, pos, :] = kn[m].transpose(1, 0, 2)
         vc[m][:, pos, :] = vn[m].transpose(1, 0, 2)
     return kc.view(np.float32), vc.view(np.float32)
+
+
+def prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens, M, n_new, H, Hkv, d, max_len, scale):
+    """Concatenate cached rows 0..P-1 and the new rows, then a causal mask shifted by P."""
+    g = H // Hkv
+    qm = np.asarray(q, dtype=np.float64).reshape(M, n_new, H, d)
+    kn = np.asarray(k_new, dtype=np.float64).reshape(M, n_new, Hkv, d)
+    vn = np.asarray(v_new, dtype=np.float64).reshape(M, n_new, Hkv, d)
+    kc = np.asarray(k_cache, dtype=np.float64).reshape(M, Hkv, max_len, d)
+    vc = np.asarray(v_cache, dtype=np.float64).reshape(M, Hkv, max_len, d)
+    out = np.zeros((M, n_new, H, d))
+    for m in range(M):
+        P = int(cache_lens[m])
+        keys = np.concatenate([kc[m, :, :P, :], kn[m].transpose(1, 0, 2)], axis=1)   # [Hkv, P+n, d]
+        vals = np.concatenate([vc[m, :, :P, :], vn[m].transpose(1, 0, 2)], axis=1)
+        keys = np.repeat(keys, g, axis=0)
+        vals = np.repeat(vals, g, axis=0)                                           # [H, P+n, d]
+        s = float(np.float32(scale)) * np.einsum("rhd,hjd->hrj", qm[m], keys)      # [H, n, P+n]
+        visible = np.arange(P + n_new)[None, :] <= (P + np.arange(n_new))[:, None]
+        p = _softmax_rows(s, visible[None])
+        out[m] = np.einsum("hrj,hjd->rhd", p, vals)
+    return out.reshape(M, n_new, H * d)

@@ -226,6 +226,65 @@ int oracle_scatter(const float *k_new, const float *v_new, float *k_cache,
     return 0;
 }
 
+/* Chunked prefill behind an existing cache (the offset causal mask:
+ * trustformers-core 0.2.0 ..., `attention_prefill_gpu_to_gpu` names prefills
+ * "appended behind an existing cache" as the case its from-empty mask does not
+ * cover).  Sequence m holds cache_lens[m] = P rows already; its n_new new
+ * tokens sit at absolute positions P .. P+n_new-1.  Query r (position P + r)
+ * of head h attends to keys 0 .. P + r of KV head h / (H/Hkv), where key j is
+ * cache row j when j < P and new row j - P otherwise.
+ *   q: [M, n_new, H*d]; k_new, v_new: [M, n_new, Hkv*d];
+ *   k_cache, v_cache: [M, Hkv, max_len, d] (only rows < P are read);
+ *   out: [M, n_new, H*d] f64.
+ * The keys of one (m, kh) are gathered into a contiguous scratch first, so the
+ * row function above applies unchanged. */
+int oracle_prefill_cached(const float *q, const float *k_new, const float *v_new,
+                          const float *k_cache, const float *v_cache,
+                          const int32_t *cache_lens, double *out, int64_t M,
+                          int64_t n_new, int64_t H, int64_t Hkv, int64_t d,
+                          int64_t max_len, float scale)
+{
+    int64_t unit, n_units, m;
+    int failed = 0;
+    if (M <= 0 || n_new <= 0 || H <= 0 || Hkv <= 0 || d <= 0 || max_len <= 0) return -1;
+    if (H % Hkv != 0) return -1;
+    for (m = 0; m < M; ++m)
+        if (cache_lens[m] < 0 || (int64_t)cache_lens[m] + n_new > max_len) return -1;
+    n_units = M * H;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (unit = 0; unit < n_units; ++unit) {
+        int64_t mm = unit / H, h = unit % H, kh = h / (H / Hkv), r, j, l;
+        int64_t P = cache_lens[mm], total = P + n_new;
+        float *keys = (float *)malloc(sizeof(float) * (size_t)(total * d));
+        float *vals = (float *)malloc(sizeof(float) * (size_t)(total * d));
+        double *scores = (double *)malloc(sizeof(double) * (size_t)total);
+        if (!keys || !vals || !scores) {
+            free(keys); free(vals); free(scores);
+            failed |= 1;
+            continue;
+        }
+        for (j = 0; j < total; ++j)
+            for (l = 0; l < d; ++l) {
+                if (j < P) {
+                    int64_t c = ((mm * Hkv + kh) * max_len + j) * d + l;
+                    keys[j * d + l] = k_cache[c];
+                    vals[j * d + l] = v_cache[c];
+                } else {
+                    int64_t c = (mm * n_new + (j - P)) * Hkv * d + kh * d + l;
+                    keys[j * d + l] = k_new[c];
+                    vals[j * d + l] = v_new[c];
+                }
+            }
+        for (r = 0; r < n_new; ++r)
+            attend_row(q + (mm * n_new + r) * H * d + h * d, keys, d, vals, d, P + r + 1, d,
+                       (double)scale, scores, out + (mm * n_new + r) * H * d + h * d);
+        free(keys);
+        free(vals);
+        free(scores);
+    }
+    return failed ? -1 : 0;
+}
+
 /* Number of OpenMP threads a parallel region would use (for reporting). */
 int oracle_num_threads(void)
 {

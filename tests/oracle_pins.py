@@ -308,6 +308,73 @@ def pin_decode_rows_match(orc):
     _close(rows, np.stack([full[m, h * d:(h + 1) * d] for m, h in sel]), 0.0, "decode_rows")
 
 
+# --------------------------------------------------------------------------- chunked prefill behind a cache
+
+
+def _cached_case(r, M, n_new, H, Hkv, d, max_len, lens):
+    q = r.standard_normal((M, n_new, H * d)).astype(np.float32)
+    kn = r.standard_normal((M, n_new, Hkv * d)).astype(np.float32)
+    vn = r.standard_normal((M, n_new, Hkv * d)).astype(np.float32)
+    kc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    vc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    for m in range(M):  # rows at or past P are not part of the cache yet
+        kc[m, :, lens[m]:] = np.nan
+        vc[m, :, lens[m]:] = np.nan
+    return q, kn, vn, kc, vc
+
+
+def pin_cached_from_empty_is_causal_prefill(orc):
+    """With nothing cached (P = 0) and Hkv = H, a chunk is a plain causal prefill."""
+    r = _rng("cached-empty")
+    M, n, H, d, max_len = 2, 7, 3, 4, 9
+    lens = np.zeros(M, np.int32)
+    q, kn, vn, kc, vc = _cached_case(r, M, n, H, H, d, max_len, lens)
+    got = orc.prefill_cached(q, kn, vn, kc, vc, lens, M, n, H, H, d, max_len, _scale(d))
+    _close(got, orc.prefill(q, kn, vn, M, n, H, d, _scale(d), True), 1e-13, "P=0 chunk vs causal prefill")
+
+
+def pin_cached_single_token_is_decode(orc):
+    """A one-token chunk behind P cached rows is a decode over the appended cache (L = P + 1)."""
+    r = _rng("cached-one")
+    M, H, Hkv, d, max_len = 3, 8, 2, 4, 10
+    lens = np.array([0, 4, 9], np.int32)
+    q, kn, vn, kc, vc = _cached_case(r, M, 1, H, Hkv, d, max_len, lens)
+    got = orc.prefill_cached(q, kn, vn, kc, vc, lens, M, 1, H, Hkv, d, max_len, _scale(d))
+    kc2, vc2 = kc.copy(), vc.copy()
+    orc.scatter(kn, vn, kc2, vc2, lens, M, 1, Hkv, d, max_len)
+    want = orc.decode(q.reshape(M, H * d), kc2, vc2, lens + 1, M, H, Hkv, d, max_len, _scale(d))
+    _close(got.reshape(M, H * d), want, 1e-13, "one-token chunk vs decode")
+
+
+def pin_cached_chunks_compose(orc):
+    """Prefilling S tokens in two chunks (the second behind the first's appended rows) equals one causal prefill."""
+    r = _rng("cached-compose")
+    M, S, s1, H, Hkv, d, max_len = 2, 9, 4, 6, 3, 4, 12
+    zero = np.zeros(M, np.int32)
+    q, kn, vn, kc, vc = _cached_case(r, M, S, H, Hkv, d, max_len, zero)
+    whole = orc.prefill_cached(q, kn, vn, kc, vc, zero, M, S, H, Hkv, d, max_len, _scale(d))
+    first = orc.prefill_cached(np.ascontiguousarray(q[:, :s1]), np.ascontiguousarray(kn[:, :s1]),
+                               np.ascontiguousarray(vn[:, :s1]), kc, vc, zero, M, s1, H, Hkv, d, max_len, _scale(d))
+    kc2, vc2 = kc.copy(), vc.copy()
+    orc.scatter(np.ascontiguousarray(kn[:, :s1]), np.ascontiguousarray(vn[:, :s1]), kc2, vc2, zero, M, s1, Hkv, d,
+                max_len)
+    second = orc.prefill_cached(np.ascontiguousarray(q[:, s1:]), np.ascontiguousarray(kn[:, s1:]),
+                                np.ascontiguousarray(vn[:, s1:]), kc2, vc2, np.full(M, s1, np.int32), M, S - s1, H,
+                                Hkv, d, max_len, _scale(d))
+    _close(np.concatenate([first, second], axis=1), whole, 1e-13, "two chunks vs one")
+
+
+def pin_cached_brute_force(orc):
+    """C oracle == numpy concatenate-and-mask formulation on ragged cache lengths and GQA groups."""
+    r = _rng("cached-brute")
+    for M, n, H, Hkv, d, max_len in [(3, 5, 4, 2, 3, 9), (2, 1, 6, 3, 4, 6), (4, 3, 2, 1, 2, 7), (1, 6, 3, 3, 5, 6)]:
+        lens = r.integers(0, max_len - n + 1, size=M).astype(np.int32)
+        q, kn, vn, kc, vc = _cached_case(r, M, n, H, Hkv, d, max_len, lens)
+        _close(orc.prefill_cached(q, kn, vn, kc, vc, lens, M, n, H, Hkv, d, max_len, _scale(d)),
+               brute.prefill_cached(q, kn, vn, np.nan_to_num(kc), np.nan_to_num(vc), lens, M, n, H, Hkv, d, max_len,
+                                    _scale(d)), 1e-12, f"cached brute {M, n, H, Hkv, d}")
+
+
 # --------------------------------------------------------------------------- brute force
 
 

@@ -45,6 +45,10 @@ MUTANTS = [
     ("scatter_v_from_k", "memcpy(&bits, &v_new[src + l], 4);", "memcpy(&bits, &k_new[src + l], 4);"),
     ("empty_sequence_not_zero", "for (l = 0; l < d; ++l) out[l] = 0.0;", "for (l = 0; l < d; ++l) out[l] = 1.0;"),
     ("rows_entry_ignores_causal", "row, causal ? i + 1 : S, d,", "row, S, d,"),
+    ("cached_offset_dropped", "vals, d, P + r + 1, d,", "vals, d, r + 1, d,"),
+    ("cached_reads_cache_row_P", "                if (j < P) {", "                if (j <= P) {"),
+    ("cached_new_rows_shifted", "(mm * n_new + (j - P)) * Hkv * d", "(mm * n_new + (j - P + 1 < n_new ? j - P + 1 : j - P)) * Hkv * d"),
+    ("cached_modulo_head_map", "kh = h / (H / Hkv), r, j, l;", "kh = h % Hkv, r, j, l;"),
 ]
 
 
