@@ -64,6 +64,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10, help="untimed steps (also let the clocks settle)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-next-rows", action="store_true",
+                   help="skip the separately timed chunked-prefill-behind-cache measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 3 times (counter calibration) and exit")
     return p.parse_args()
@@ -242,7 +244,38 @@ def main():
                             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic("decode")},
         "cpu_baseline": None,
+        "next_rows": None,
     }
+
+    if not args.no_next_rows:
+        # Chunked prefill behind the cache the bulk append filled (rows 0..2047 of
+        # each sequence): the next 2048 tokens, timed on their own, outside the step.
+        ccfg = wl.CHUNK_BEHIND_CACHE
+        rng = np.random.default_rng(4096)
+        shape = (ccfg.M, ccfg.n_new, ccfg.H * ccfg.d)
+        cq, ck, cv = (up(wl.normal(rng, shape, pcfg.std)) for _ in range(3))
+        cout = torch.empty_like(cq)
+        cached = [scfg.n_new] * ccfg.M
+        run = lambda: taf.attn_prefill_cached(cq, ck, cv, bk, bv, cached, cout, ccfg.M, ccfg.n_new, ccfg.H,
+                                              ccfg.Hkv, ccfg.d, ccfg.max_len, ccfg.scale)
+        for _ in range(5):
+            run()
+        torch.cuda.synchronize()
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for e0, e1 in cev:
+            e0.record()
+            run()
+            e1.record()
+        torch.cuda.synchronize()
+        c_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in cev]))
+        c_tflops = ccfg.flops(cached) / (c_ms * 1e-3) / 1e12
+        result["next_rows"] = {"prefill_cached": {
+            "workload": ccfg.name, "us": round(c_ms * 1e3, 2), "tflops": round(c_tflops, 3),
+            "frac_mfma": round(c_tflops / FP32_MFMA_PEAK_TFLOPS, 4), "algorithmic_flops": ccfg.flops(cached),
+            "note": "append of the chunk's K/V plus attention over 2048 cached + the chunk's own keys; "
+                    "timed separately, not part of ms_per_step"}}
+        log(f"prefill_cached: {c_ms * 1e3:.1f} us, {c_tflops:.1f} TFLOP/s")
+        del cq, ck, cv, cout
 
     # Free the GPU copies before the host-side leg.
     del pq, pk, pv, pout, bk, bv, dq, dkn, dvn, dkc, dvc, dout, ws

@@ -4,7 +4,7 @@
  *
  *   out = softmax(scale * Q K^T [+ causal mask]) V
  *
- * Three operations, each enqueued on a caller-supplied HIP stream:
+ * Four operations, each enqueued on a caller-supplied HIP stream:
  *   attn_prefill             full-sequence attention over interleaved
  *                            [batch, seq, n_heads * head_dim] activations,
  *                            optionally causal;
@@ -12,7 +12,10 @@
  *                            sequences against a preallocated GQA KV cache,
  *                            each sequence with its own length;
  *   kv_cache_scatter         append rows of new keys/values into that cache
- *                            at each sequence's current length.
+ *                            at each sequence's current length;
+ *   attn_prefill_cached      a chunk of new tokens behind an existing cache:
+ *                            append, then attend with the causal mask offset
+ *                            by each sequence's cached length.
  *
  * Conventions shared by every entry point
  *   - Tensors are f32, row-major, contiguous, in DEVICE memory owned by the
@@ -68,8 +71,9 @@ typedef enum {
  *
  * Defines: trueno-gpu `batched_multihead_attention` (softmax(Q K^T/sqrt(d_k)) V
  * per head over interleaved [seq, n_heads * head_dim]) and trustformers-core
- * `attention_prefill_gpu_to_gpu` (caller-chosen scale; causal mask "from an
- * empty cache": query i sees keys 0..=i; masked probabilities are exactly 0).
+ * `attention_prefill_gpu_to_gpu` (caller-chosen scale; the causal mask assumes
+ * nothing is cached yet, so query i sees keys 0..=i; masked probabilities are
+ * exactly 0).
  * Batch elements are independent.
  *
  *   q, k, v  [batch, seq_len, n_heads * head_dim]  read
@@ -88,6 +92,45 @@ typedef enum {
 int attn_prefill(const float *q, const float *k, const float *v, float *out,
                  int32_t batch, int32_t seq_len, int32_t n_heads, int32_t head_dim,
                  float scale, int32_t causal, void *stream);
+
+/*
+ * Chunked prefill behind an existing KV cache: append the keys and values of a
+ * chunk of n_new tokens to each sequence's cache and attend the chunk's queries
+ * causally over everything cached so far.
+ *
+ * Defines: trustformers-core `attention_prefill_gpu_to_gpu` restricts its causal
+ * mask to a prefill with nothing cached and sends a prefill that follows cached
+ * tokens to the decode path one token at a time; this entry point covers that
+ * case in one call.  Sequence m
+ * holds P = cache_lens[m] rows; its new tokens sit at positions P .. P+n_new-1,
+ * and query r (position P + r) of head h sees keys 0 .. P + r of KV head
+ * h / (num_heads / num_kv_heads), laid out as realizar `init_batched_kv_cache_gpu`.
+ *
+ *   q                 [M, n_new, num_heads * head_dim]       read
+ *   k_new, v_new      [M, n_new, num_kv_heads * head_dim]    read
+ *   k_cache, v_cache  [M, num_kv_heads, max_len, head_dim]   rows P .. P+n_new-1
+ *                     written exactly as kv_cache_scatter would; rows < P read
+ *   cache_lens        HOST [M] int32, P per sequence (not updated: lengths are
+ *                     caller state; the new length is P + n_new)
+ *   out               [M, n_new, num_heads * head_dim]       written, every element
+ *   With cache_lens all 0 and num_kv_heads == num_heads this equals
+ *   kv_cache_scatter followed by attn_prefill(causal = 1); with n_new == 1 it
+ *   equals kv_cache_scatter followed by attn_decode_gqa_batched with
+ *   seq_lens = P + 1.
+ *
+ * Errors: NULL pointer; M not in [1, 32], n_new/num_heads/num_kv_heads/max_len
+ * <= 0, num_heads % num_kv_heads != 0, num_kv_heads > num_heads, a cache_lens
+ * value < 0 or cache_lens[m] + n_new > max_len, scale not finite
+ * (INVALID_DIM); head_dim not in {32, 64, 128} or a misaligned pointer
+ * (UNSUPPORTED); M*n_new*num_heads*head_dim >= 2^31 or a cache element count
+ * >= 2^40 (OVERFLOW); out or a cache overlapping an input, or the caches
+ * overlapping each other or out (ALIAS).  Two launches (append, attention)
+ * are enqueued on `stream`.
+ */
+int attn_prefill_cached(const float *q, const float *k_new, const float *v_new, float *k_cache,
+                        float *v_cache, const int32_t *cache_lens, float *out, int32_t num_seqs,
+                        int32_t n_new, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t max_len, float scale, void *stream);
 
 /*
  * Bytes of device workspace attn_decode_gqa_batched needs for these sizes

@@ -59,6 +59,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_scatter.restype = ctypes.c_int
     lib.oracle_prefill_cached.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, ctypes.c_float]
     lib.oracle_prefill_cached.restype = ctypes.c_int
+    lib.oracle_prefill_cached_rows.argtypes = [p, p, p, p, p, p, p, i64, p, i64, i64, i64, i64, i64, i64,
+                                               ctypes.c_float]
+    lib.oracle_prefill_cached_rows.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -171,6 +174,21 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_prefill_cached rejected its arguments")
         return out.reshape(M, n_new, H * d)
+
+    def prefill_cached_rows(self, q, k_new, v_new, k_cache, v_cache, cache_lens, sel, M, n_new, H, Hkv, d,
+                            max_len, scale):
+        """Selected rows of prefill_cached; ``sel`` is an (n, 3) int array of (m, r, h)."""
+        q, k_new, v_new = _f32(q), _f32(k_new), _f32(v_new)
+        k_cache, v_cache = _f32(k_cache), _f32(v_cache)
+        cache_lens = np.ascontiguousarray(cache_lens, dtype=np.int32)
+        sel = np.ascontiguousarray(sel, dtype=np.int64).reshape(-1, 3)
+        out = np.empty((sel.shape[0], d), dtype=np.float64)
+        rc = self.lib.oracle_prefill_cached_rows(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                                 _ptr(cache_lens), _ptr(sel), sel.shape[0], _ptr(out), M, n_new,
+                                                 H, Hkv, d, max_len, float(np.float32(scale)))
+        if rc != 0:
+            raise ValueError("oracle_prefill_cached_rows rejected its arguments")
+        return out
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())

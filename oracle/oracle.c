@@ -18,8 +18,8 @@
  *    `batched_multihead_attention`: output = softmax(Q K^T / sqrt(d_k)) V over
  *    interleaved [seq, n_heads * head_dim] activations, one head at a time.
  *  - trustformers-core 0.2.0 src/gpu_ops/cuda/oxicuda/attention.rs,
- *    `attention_prefill_gpu_to_gpu` (causal mask "from empty cache": query i
- *    sees keys 0..=i), `softmax_causal_gpu_to_gpu` (masked cells are exactly
+ *    `attention_prefill_gpu_to_gpu` (causal mask for a prefill with nothing
+ *    cached: query i sees keys 0..=i), `softmax_causal_gpu_to_gpu` (masked cells are exactly
  *    zero) and the test helper `prefill_reference` (max-subtracted softmax,
  *    then (p / sum) * v).
  *  - trueno-gpu ..., `incremental_attention_gpu`: one query token per head
@@ -227,9 +227,9 @@ int oracle_scatter(const float *k_new, const float *v_new, float *k_cache,
 }
 
 /* Chunked prefill behind an existing cache (the offset causal mask:
- * trustformers-core 0.2.0 ..., `attention_prefill_gpu_to_gpu` names prefills
- * "appended behind an existing cache" as the case its from-empty mask does not
- * cover).  Sequence m holds cache_lens[m] = P rows already; its n_new new
+ * trustformers-core 0.2.0 ..., `attention_prefill_gpu_to_gpu` leaves a prefill
+ * that follows cached tokens to the per-token decode path; this is that case in
+ * one call).  Sequence m holds cache_lens[m] = P rows already; its n_new new
  * tokens sit at absolute positions P .. P+n_new-1.  Query r (position P + r)
  * of head h attends to keys 0 .. P + r of KV head h / (H/Hkv), where key j is
  * cache row j when j < P and new row j - P otherwise.
@@ -278,6 +278,53 @@ int oracle_prefill_cached(const float *q, const float *k_new, const float *v_new
         for (r = 0; r < n_new; ++r)
             attend_row(q + (mm * n_new + r) * H * d + h * d, keys, d, vals, d, P + r + 1, d,
                        (double)scale, scores, out + (mm * n_new + r) * H * d + h * d);
+        free(keys);
+        free(vals);
+        free(scores);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Selected rows of oracle_prefill_cached.  sel: n_sel triples (m, r, h);
+ * out: n_sel x d f64, row t = out[m, r, h*d : (h+1)*d] of the full call. */
+int oracle_prefill_cached_rows(const float *q, const float *k_new, const float *v_new,
+                               const float *k_cache, const float *v_cache,
+                               const int32_t *cache_lens, const int64_t *sel, int64_t n_sel,
+                               double *out, int64_t M, int64_t n_new, int64_t H, int64_t Hkv,
+                               int64_t d, int64_t max_len, float scale)
+{
+    int64_t t, m;
+    int failed = 0;
+    if (M <= 0 || n_new <= 0 || H <= 0 || Hkv <= 0 || d <= 0 || max_len <= 0 || n_sel < 0) return -1;
+    if (H % Hkv != 0) return -1;
+    for (m = 0; m < M; ++m)
+        if (cache_lens[m] < 0 || (int64_t)cache_lens[m] + n_new > max_len) return -1;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (t = 0; t < n_sel; ++t) {
+        int64_t mm = sel[3 * t], r = sel[3 * t + 1], h = sel[3 * t + 2], kh, P, n, j, l;
+        float *keys, *vals;
+        double *scores;
+        if (mm < 0 || mm >= M || r < 0 || r >= n_new || h < 0 || h >= H) { failed |= 1; continue; }
+        kh = h / (H / Hkv);
+        P = cache_lens[mm];
+        n = P + r + 1; /* keys visible to this query */
+        keys = (float *)malloc(sizeof(float) * (size_t)(n * d));
+        vals = (float *)malloc(sizeof(float) * (size_t)(n * d));
+        scores = (double *)malloc(sizeof(double) * (size_t)n);
+        if (!keys || !vals || !scores) {
+            free(keys); free(vals); free(scores);
+            failed |= 1;
+            continue;
+        }
+        for (j = 0; j < n; ++j)
+            for (l = 0; l < d; ++l) {
+                int64_t c = j < P ? ((mm * Hkv + kh) * max_len + j) * d + l
+                                  : (mm * n_new + (j - P)) * Hkv * d + kh * d + l;
+                keys[j * d + l] = j < P ? k_cache[c] : k_new[c];
+                vals[j * d + l] = j < P ? v_cache[c] : v_new[c];
+            }
+        attend_row(q + (mm * n_new + r) * H * d + h * d, keys, d, vals, d, n, d, (double)scale, scores,
+                   out + t * d);
         free(keys);
         free(vals);
         free(scores);

@@ -375,6 +375,18 @@ def pin_cached_brute_force(orc):
                                     _scale(d)), 1e-12, f"cached brute {M, n, H, Hkv, d}")
 
 
+def pin_cached_rows_match(orc):
+    """The sampled-row entry point of the chunked prefill equals the full computation."""
+    r = _rng("cached-rows")
+    M, n, H, Hkv, d, max_len = 3, 6, 4, 2, 4, 12
+    lens = np.array([0, 5, 6], np.int32)
+    q, kn, vn, kc, vc = _cached_case(r, M, n, H, Hkv, d, max_len, lens)
+    full = orc.prefill_cached(q, kn, vn, kc, vc, lens, M, n, H, Hkv, d, max_len, _scale(d))
+    sel = np.array([[0, 0, 0], [2, 5, 3], [1, 2, 1], [1, 5, 2]], np.int64)
+    rows = orc.prefill_cached_rows(q, kn, vn, kc, vc, lens, sel, M, n, H, Hkv, d, max_len, _scale(d))
+    _close(rows, np.stack([full[m, i, h * d:(h + 1) * d] for m, i, h in sel]), 0.0, "prefill_cached_rows")
+
+
 # --------------------------------------------------------------------------- brute force
 
 

@@ -37,7 +37,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "attn_prefill", "attn_decode_workspace_bytes", "attn_decode_gqa_batched",
+        "attn_prefill", "attn_prefill_cached", "attn_decode_workspace_bytes", "attn_decode_gqa_batched",
         "kv_cache_scatter", "attn_status_string"])
 
 
@@ -139,6 +139,30 @@ def test_scatter_validation(lib):
     assert scatter(lib, n_new=2**20, Hkv=2**10, d=128, max_len=2**21, lens=(0, 0)) == OVF
     assert scatter(lib, vc=C_ + 256) == ALIAS   # the two caches overlap
     assert scatter(lib, kc=A) == ALIAS          # cache over the source
+
+
+def cached(lib, q=A, kn=B_, vn=B_ + 0x1000000, kc=C_, vc=C_ + 0x8000000, lens=(0, 3), out=O_, M=2, n=4,
+           H=8, Hkv=2, d=64, max_len=64, scale=0.125):
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens) if lens is not None else None
+    return lib.attn_prefill_cached(q, kn, vn, kc, vc, arr, out, M, n, H, Hkv, d, max_len, scale, None)
+
+
+def test_prefill_cached_validation(lib):
+    assert cached(lib, q=0) == NULL
+    assert cached(lib, lens=None) == NULL
+    assert cached(lib, M=0, lens=(0,)) == DIM
+    assert cached(lib, M=33, lens=(0,) * 33) == DIM
+    assert cached(lib, n=0) == DIM
+    assert cached(lib, Hkv=3) == DIM                 # 8 % 3 != 0
+    assert cached(lib, lens=(0, 61)) == DIM          # 61 + 4 > 64
+    assert cached(lib, lens=(-2, 0)) == DIM
+    assert cached(lib, scale=float("inf")) == DIM
+    assert cached(lib, d=48) == UNSUP
+    assert cached(lib, kc=C_ + 4) == UNSUP
+    assert cached(lib, n=2**16, H=2**10, Hkv=2**10, d=128, max_len=2**17, lens=(0, 0)) == OVF
+    assert cached(lib, out=A + 64) == ALIAS          # out over q
+    assert cached(lib, vc=C_ + 1024) == ALIAS        # the caches overlap
+    assert cached(lib, kc=B_) == ALIAS               # cache over k_new
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -47,7 +47,10 @@ MUTANTS = [
     ("rows_entry_ignores_causal", "row, causal ? i + 1 : S, d,", "row, S, d,"),
     ("cached_offset_dropped", "vals, d, P + r + 1, d,", "vals, d, r + 1, d,"),
     ("cached_reads_cache_row_P", "                if (j < P) {", "                if (j <= P) {"),
-    ("cached_new_rows_shifted", "(mm * n_new + (j - P)) * Hkv * d", "(mm * n_new + (j - P + 1 < n_new ? j - P + 1 : j - P)) * Hkv * d"),
+    ("cached_new_rows_shifted", "int64_t c = (mm * n_new + (j - P)) * Hkv * d",
+     "int64_t c = (mm * n_new + (j - P + 1 < n_new ? j - P + 1 : j - P)) * Hkv * d"),
+    ("cached_rows_offset_dropped", "        n = P + r + 1; /* keys visible to this query */",
+     "        n = r + 1; /* keys visible to this query */"),
     ("cached_modulo_head_map", "kh = h / (H / Hkv), r, j, l;", "kh = h % Hkv, r, j, l;"),
 ]
 

@@ -21,6 +21,7 @@ __all__ = [
     "AttnError",
     "ATTN_MAX_SEQS",
     "attn_prefill",
+    "attn_prefill_cached",
     "attn_decode_workspace_bytes",
     "attn_decode_gqa_batched",
     "kv_cache_scatter",
@@ -63,6 +64,8 @@ def library() -> ctypes.CDLL:
         p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
         lib.attn_prefill.argtypes = [p, p, p, p, i32, i32, i32, i32, f32, i32, p]
         lib.attn_prefill.restype = ctypes.c_int
+        lib.attn_prefill_cached.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p]
+        lib.attn_prefill_cached.restype = ctypes.c_int
         lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.attn_decode_workspace_bytes.restype = sz
         lib.attn_decode_gqa_batched.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, p, sz, p]
@@ -134,6 +137,24 @@ def attn_prefill(q, k, v, out, batch: int, seq_len: int, n_heads: int, head_dim:
     ptrs = [_check_tensor(nm, t, n, dev) for nm, t in (("q", q), ("k", k), ("v", v), ("out", out))]
     _call("attn_prefill", library().attn_prefill(*ptrs, batch, seq_len, n_heads, head_dim, scale,
                                                  1 if causal else 0, _stream_ptr(dev, stream)))
+
+
+def attn_prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens: Sequence[int], out, num_seqs: int,
+                        n_new: int, num_heads: int, num_kv_heads: int, head_dim: int, max_len: int,
+                        scale: float, stream=None) -> None:
+    """Append a chunk's K/V at cache_lens[m] and attend its queries over cache rows 0..cache_lens[m]+r."""
+    dev = q.device
+    qn = num_seqs * n_new * num_heads * head_dim
+    nn = num_seqs * n_new * num_kv_heads * head_dim
+    cn = num_seqs * num_kv_heads * max_len * head_dim
+    ptrs = [_check_tensor("q", q, qn, dev), _check_tensor("k_new", k_new, nn, dev),
+            _check_tensor("v_new", v_new, nn, dev), _check_tensor("k_cache", k_cache, cn, dev),
+            _check_tensor("v_cache", v_cache, cn, dev)]
+    lens = _host_ints("cache_lens", cache_lens, num_seqs)
+    po = _check_tensor("out", out, qn, dev)
+    _call("attn_prefill_cached",
+          library().attn_prefill_cached(*ptrs, lens, po, num_seqs, n_new, num_heads, num_kv_heads, head_dim,
+                                        max_len, scale, _stream_ptr(dev, stream)))
 
 
 def attn_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_len: int) -> int:

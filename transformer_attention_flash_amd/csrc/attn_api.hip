@@ -77,8 +77,80 @@ int attn_prefill(const float *q, const float *k, const float *v, float *out, int
     if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
         return ATTN_ERR_ALIAS;
 
-    attn::PrefillArgs a{q, k, v, out, batch, seq_len, n_heads, head_dim, scale, causal};
+    attn::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.B = batch;
+    a.S = seq_len;
+    a.H = n_heads;
+    a.D = head_dim;
+    a.scale = scale;
+    a.causal = causal;
+    a.cached = 0;
+    a.Hkv = n_heads;
+    a.max_len = seq_len;
     return from_hip(attn::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+int attn_prefill_cached(const float *q, const float *k_new, const float *v_new, float *k_cache,
+                        float *v_cache, const int32_t *cache_lens, float *out, int32_t num_seqs,
+                        int32_t n_new, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t max_len, float scale, void *stream) {
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_lens || !out) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS) return ATTN_ERR_INVALID_DIM;
+    if (n_new <= 0 || num_heads <= 0 || num_kv_heads <= 0 || max_len <= 0 || head_dim <= 0)
+        return ATTN_ERR_INVALID_DIM;
+    if (num_kv_heads > num_heads || num_heads % num_kv_heads != 0) return ATTN_ERR_INVALID_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID_DIM;
+    SeqInts pos{};
+    for (int32_t m = 0; m < num_seqs; ++m) {
+        if (cache_lens[m] < 0 || (int64_t)cache_lens[m] + n_new > max_len) return ATTN_ERR_INVALID_DIM;
+        pos.v[m] = cache_lens[m];
+    }
+    if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(out))
+        return ATTN_ERR_UNSUPPORTED;
+    int64_t q_elems, new_elems, cache_elems, per_seq;
+    if (!checked_mul({num_seqs, n_new, num_heads, head_dim}, kMaxElems32, &q_elems) ||
+        !checked_mul({num_seqs, n_new, num_kv_heads, head_dim}, kMaxElems32, &new_elems) ||
+        !checked_mul({num_seqs, num_kv_heads, max_len, head_dim}, kMaxElems, &cache_elems) ||
+        !checked_mul({n_new, num_kv_heads, head_dim}, kMaxElems32, &per_seq))
+        return ATTN_ERR_OVERFLOW;
+    const int64_t qb = q_elems * 4, nb = new_elems * 4, cb = cache_elems * 4;
+    const void *ins[] = {q, k_new, v_new};
+    const int64_t in_bytes[] = {qb, nb, nb};
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(out, qb, ins[i], in_bytes[i]) || overlaps(k_cache, cb, ins[i], in_bytes[i]) ||
+            overlaps(v_cache, cb, ins[i], in_bytes[i]))
+            return ATTN_ERR_ALIAS;
+    if (overlaps(out, qb, k_cache, cb) || overlaps(out, qb, v_cache, cb) || overlaps(k_cache, cb, v_cache, cb))
+        return ATTN_ERR_ALIAS;
+
+    // Append the chunk's K/V rows at each sequence's length, then attend over
+    // the cache; both launches go on the same stream, in that order.
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    attn::ScatterArgs sa{k_new, v_new, k_cache, v_cache, pos, num_seqs, n_new, num_kv_heads, head_dim, max_len};
+    hipError_t e = attn::launch_kv_scatter(sa, st);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+    attn::PrefillArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.B = num_seqs;
+    a.S = n_new;
+    a.H = num_heads;
+    a.D = head_dim;
+    a.scale = scale;
+    a.causal = 1;
+    a.cached = 1;
+    a.Hkv = num_kv_heads;
+    a.max_len = max_len;
+    a.pos = pos;
+    return from_hip(attn::launch_prefill(a, st));
 }
 
 size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,

@@ -26,6 +26,11 @@ struct ScatterArgs {
 };
 hipError_t launch_kv_scatter(const ScatterArgs &a, hipStream_t stream);
 
+// Full-sequence attention.  q and out are [B, S, H * D] (S queries per batch
+// element).  With cached == 0, k and v are [B, S, H * D] too (prefill from an
+// empty cache).  With cached == 1, k and v are the caches [B, Hkv, max_len, D]:
+// element b's queries sit at absolute positions pos[b] .. pos[b] + S - 1 and
+// query i attends to cache rows 0 .. pos[b] + i (causal must be 1).
 struct PrefillArgs {
     const float *q;
     const float *k;
@@ -34,6 +39,9 @@ struct PrefillArgs {
     int32_t B, S, H, D;
     float scale;
     int32_t causal;
+    int32_t cached;
+    int32_t Hkv, max_len;
+    SeqInts pos;
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 

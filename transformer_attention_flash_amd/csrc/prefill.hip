@@ -6,7 +6,10 @@
 // interleaved in the row) and trustformers-core 0.2.0
 // src/gpu_ops/cuda/oxicuda/attention.rs, `attention_prefill_gpu_to_gpu`
 // (caller-chosen scale, causal mask from an empty cache: query i sees keys
-// 0..=i, masked probabilities exactly zero).  Instead of the pages' per-head
+// 0..=i, masked probabilities exactly zero).  The same kernel also runs a
+// chunk of queries behind an existing KV cache (the case that page leaves to
+// other paths): keys then come from the GQA cache slab [max_len, D] of the
+// query head's KV head and query i of the chunk sees cache rows 0..P+i.  Instead of the pages' per-head
 // extract / transpose / GEMM / softmax / GEMM chain, one kernel reads the
 // head's columns straight out of the interleaved rows and never materialises
 // scores: an online softmax (running row max and sum, output rescaled when
@@ -103,12 +106,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int
     }
     const int b = bh / a.H;
     const int h = bh % a.H;
-    const int S = a.S;
+    const int S = a.S;                           // queries of this batch element
     const size_t row_stride = (size_t)a.H * D;  // floats between consecutive tokens
     const size_t head_base = (size_t)b * S * row_stride + (size_t)h * D;
     const float *__restrict__ qg = a.q + head_base;
-    const float *__restrict__ kg = a.k + head_base;
-    const float *__restrict__ vg = a.v + head_base;
+    // Keys: the interleaved activations (key j = token j), or the cache slab of
+    // KV head h / (H / Hkv) (key j = cache row j, queries offset by P).
+    const int P = a.cached ? a.pos.v[b] : 0;    // key index of query 0
+    const int Sk = P + S;                        // keys a query can reach at most
+    size_t kv_stride, kv_base;
+    if (a.cached) {
+        kv_stride = D;
+        kv_base = ((size_t)b * a.Hkv + h / (a.H / a.Hkv)) * (size_t)a.max_len * D;
+    } else {
+        kv_stride = row_stride;
+        kv_base = head_base;
+    }
+    const float *__restrict__ kg = a.k + kv_base;
+    const float *__restrict__ vg = a.v + kv_base;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -139,21 +154,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int
     float m_run = kNegBig;
     float l_run = 0.f;
 
-    const int n_ktiles_all = (S + BN - 1) / BN;
-    const int n_ktiles = CAUSAL ? min(n_ktiles_all, (min(q0 + BM, S) - 1) / BN + 1) : n_ktiles_all;
+    const int n_ktiles_all = (Sk + BN - 1) / BN;
+    const int n_ktiles = CAUSAL ? min(n_ktiles_all, (P + min(q0 + BM, S) - 1) / BN + 1) : n_ktiles_all;
 
     // Each wave moves XPW 1 KiB pieces of the K tile and of the V tile straight
-    // into LDS.  Keys past S read row S - 1 (in bounds); their scores are masked
-    // and their probabilities are exactly 0, so the values never matter.
+    // into LDS.  Keys past Sk read row Sk - 1 (in bounds); their scores are
+    // masked and their probabilities are exactly 0, so the values never matter.
     auto issue_tile = [&](int kt, float *kdst, float *vdst) {
 #pragma unroll
         for (int u = 0; u < XPW; ++u) {
             const int piece = wave * XPW + u;
             const int row = piece * RPI + lane / CPR;
             const int chunk = lane % CPR;
-            const size_t key = (size_t)min(kt * BN + row, S - 1);
-            dma16(kg + key * row_stride + 4 * (chunk ^ (row & SWZ)), kdst + piece * 256);
-            dma16(vg + key * row_stride + 4 * chunk, vdst + piece * 256);
+            const size_t key = (size_t)min(kt * BN + row, Sk - 1);
+            dma16(kg + key * kv_stride + 4 * (chunk ^ (row & SWZ)), kdst + piece * 256);
+            dma16(vg + key * kv_stride + 4 * chunk, vdst + piece * 256);
         }
     };
 
@@ -165,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int
         if (kt + 1 < n_ktiles) issue_tile(kt + 1, Kn, Vn);
 
         const int ks0 = kt * BN;  // first key of the tile
-        if (CAUSAL && ks0 > qw0 + 31) return;  // whole tile above this wave's diagonal
+        if (CAUSAL && ks0 > P + qw0 + 31) return;  // whole tile above this wave's diagonal
 
         // S^T = K Q^T over D (k-slot lk of step (j, c) is column 8j + 4lk + c).
         f32x16 s = f32x16{};
@@ -177,13 +192,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int
             for (int c = 0; c < 4; ++c) s = mfma32(kv[c], qreg[j][c], s);
         }
 
-        // Mask: keys past S, and (causal) keys after the query.
-        const bool need_mask = (ks0 + 32 > S) || (CAUSAL && ks0 + 31 > qw0);
+        // Mask: keys past Sk, and (causal) keys after the query's position.
+        const bool need_mask = (ks0 + 32 > Sk) || (CAUSAL && ks0 + 31 > P + qw0);
         if (need_mask) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int key = ks0 + mrow(v, lk);
-                const bool dead = key >= S || (CAUSAL && key > my_q);
+                const bool dead = key >= Sk || (CAUSAL && key > P + my_q);
                 s[v] = dead ? -INFINITY : s[v];
             }
         }

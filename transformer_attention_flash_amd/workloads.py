@@ -106,6 +106,27 @@ class ScatterConfig:
         return 2 * 2 * self.M * self.n_new * self.Hkv * self.d * 4
 
 
+@dataclasses.dataclass(frozen=True)
+class ChunkConfig:
+    """A chunk of n_new tokens prefilled behind cached[m] rows of each sequence."""
+    name: str
+    M: int
+    n_new: int
+    H: int
+    Hkv: int
+    d: int
+    max_len: int
+
+    @property
+    def scale(self) -> float:
+        return scale_for(self.d)
+
+    def flops(self, cached) -> int:
+        """4*d per visible (query, key) pair per head: query r of sequence m sees cached[m] + r + 1 keys."""
+        pairs = sum(int(c) * self.n_new + self.n_new * (self.n_new + 1) // 2 for c in cached)
+        return 4 * self.d * self.H * pairs
+
+
 PREFILL = {
     1: PrefillConfig(1, "mha_s64_h4_d32", B=1, S=64, H=4, d=32, causal=False),
     2: PrefillConfig(2, "whisper_base_encoder_s1500_h8_d64", B=1, S=1500, H=8, d=64, causal=False),
@@ -114,6 +135,9 @@ PREFILL = {
 # The bulk append of the causal prefill's K/V into a [4, 32, 4096, 128] cache from position 0.
 BULK_SCATTER = ScatterConfig(3, "bulk_append_m4_n2048_hkv32_d128_max4096", M=4, n_new=2048, Hkv=32,
                              d=128, max_len=4096)
+# The second half of the causal prefill workload's sequences prefilled behind the first half.
+CHUNK_BEHIND_CACHE = ChunkConfig("chunk_m4_n2048_behind_2048_h32_d128_max4096", M=4, n_new=2048, H=32, Hkv=32,
+                                 d=128, max_len=4096)
 DECODE = {
     4: DecodeConfig(4, "gqa_decode_m32_h32_hkv8_d128_max4096", M=32, H=32, Hkv=8, d=128,
                     max_len=4096, len_lo=1, len_hi=4096),
