@@ -17,7 +17,9 @@ and follows the definitions cited there:
   ``init_kv_cache_gpu`` / ``init_batched_kv_cache_gpu`` (GQA cache layout);
 * scatter -- trueno-gpu ``kv_cache_scatter_gpu``;
 * chunked prefill behind a cache -- trustformers-core ``attention_prefill_gpu_to_gpu``
-  (the offset mask its from-empty-cache mask leaves to other paths).
+  (the offset mask its nothing-cached mask leaves to other paths);
+* rotary position embedding -- trustformers-core ``rope_neox_gpu_to_gpu`` /
+  ``rope_reference``; realizar ``apply_rope_to_buffer``.
 
 ``brute.py`` is a second, independent numpy fp64 formulation used only to
 cross-check this one on tiny shapes.
@@ -62,6 +64,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_prefill_cached_rows.argtypes = [p, p, p, p, p, p, p, i64, p, i64, i64, i64, i64, i64, i64,
                                                ctypes.c_float]
     lib.oracle_prefill_cached_rows.restype = ctypes.c_int
+    lib.oracle_rope.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_double]
+    lib.oracle_rope.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -189,6 +193,18 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_prefill_cached_rows rejected its arguments")
         return out
+
+    def rope(self, x, pos, H, d, rotary_ndims, base):
+        """NeoX half-split partial RoPE of rows [n, H*d] at positions pos[n]; returns f64 [n, H*d]."""
+        x = _f32(x)
+        pos = np.ascontiguousarray(pos, dtype=np.int32).reshape(-1)
+        n = pos.size
+        assert x.size == n * H * d
+        out = np.empty(n * H * d, dtype=np.float64)
+        rc = self.lib.oracle_rope(_ptr(x), _ptr(pos), _ptr(out), n, H, d, rotary_ndims, float(base))
+        if rc != 0:
+            raise ValueError("oracle_rope rejected its arguments")
+        return out.reshape(n, H * d)
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())

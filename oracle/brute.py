@@ -89,3 +89,17 @@ def prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens, M, n_new, H, H
         p = _softmax_rows(s, visible[None])
         out[m] = np.einsum("hrj,hjd->rhd", p, vals)
     return out.reshape(M, n_new, H * d)
+
+
+def rope(x, pos, H, d, rotary_ndims, base):
+    """Each pair (x_i, x_{i+half}) as the complex number x_i + 1j x_{i+half}, multiplied by e^{1j a}."""
+    x = np.asarray(x, dtype=np.float64).reshape(len(pos), H, d).copy()
+    half = rotary_ndims // 2
+    if half == 0:
+        return x.reshape(len(pos), H * d)
+    i = np.arange(half, dtype=np.float64)
+    a = np.asarray(pos, dtype=np.float64)[:, None] * np.float64(base) ** (-2.0 * i / rotary_ndims)  # [n, half]
+    z = (x[:, :, :half] + 1j * x[:, :, half:2 * half]) * np.exp(1j * a)[:, None, :]
+    x[:, :, :half] = z.real
+    x[:, :, half:2 * half] = z.imag
+    return x.reshape(len(pos), H * d)

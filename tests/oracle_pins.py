@@ -12,7 +12,10 @@ raises AssertionError when the oracle disagrees with:
   gpu_tests ``oxicuda_resident_decode_attention_parity``; an empty sequence
   gives zeros -- trueno-gpu 0.4.11 src/memory/resident/attention.rs,
   ``incremental_attention_gpu``),
-* printed offsets (tests/golden/), and
+* printed offsets (tests/golden/),
+* the rotary embedding's closed forms (identity at position 0, unit-vector
+  images, the frequency ladder, pair lengths, composition, dependence of
+  scores on relative position only), and
 * an independent numpy fp64 brute force on every tiny shape.
 """
 from __future__ import annotations
@@ -505,6 +508,165 @@ def pin_scatter_rejects_overflow(orc):
     else:
         raise AssertionError("append past max_len accepted")
     assert not kc.any() and not vc.any()
+
+
+# --------------------------------------------------------------------------- rope
+#
+# GPT-NeoX half-split partial rotary embedding: trustformers-core 0.2.0
+# src/gpu_ops/cuda/oxicuda/attention.rs, ``rope_neox_gpu_to_gpu`` and its CPU
+# helper ``rope_reference``; realizar 0.8.5 ...cache_from_kv_cache.rs,
+# ``apply_rope_to_buffer`` (the rotary_ndims = head_dim case, base = theta).
+
+
+def pin_rope_position_zero_is_identity(orc):
+    """At position 0 every angle is 0, so the rotation is exactly the identity."""
+    r = _rng("rope0")
+    n, H, d = 3, 2, 8
+    x = r.standard_normal((n, H * d)).astype(np.float32)
+    for rot in (0, 2, 4, 8):
+        y = orc.rope(x, np.zeros(n, np.int32), H, d, rot, 10000.0)
+        assert np.array_equal(y, x.astype(np.float64)), f"position 0, rotary {rot}"
+
+
+def pin_rope_untouched_dims(orc):
+    """Dims at or past rotary_ndims pass through unchanged; rotary_ndims = 0 is the identity."""
+    r = _rng("ropetail")
+    n, H, d = 4, 3, 10
+    x = r.standard_normal((n, H * d)).astype(np.float32)
+    pos = np.array([1, 7, 100, 12345], np.int32)
+    assert np.array_equal(orc.rope(x, pos, H, d, 0, 500.0), x.astype(np.float64)), "rotary 0"
+    for rot in (2, 4, 6):
+        y = orc.rope(x, pos, H, d, rot, 500.0).reshape(n, H, d)
+        assert np.array_equal(y[:, :, rot:], x.reshape(n, H, d)[:, :, rot:].astype(np.float64)), f"tail rot={rot}"
+        assert not np.allclose(y[:, :, :rot], x.reshape(n, H, d)[:, :, :rot]), f"head rot={rot} not rotated"
+
+
+def pin_rope_basis_vectors(orc):
+    """Pair 0 turns at base^0 = 1 radian per position, counter-clockwise, pairing dim 0 with dim half.
+
+    e_0 at position p goes to cos(p) e_0 + sin(p) e_half and e_half to
+    -sin(p) e_0 + cos(p) e_half; no other dim is touched.
+    """
+    H, d, rot = 1, 8, 8
+    half = rot // 2
+    for p in (1, 2, 5, 33):
+        for src, want in ((0, {0: math.cos(p), half: math.sin(p)}), (half, {0: -math.sin(p), half: math.cos(p)})):
+            x = np.zeros((1, d), np.float32)
+            x[0, src] = 1.0
+            y = orc.rope(x, np.array([p], np.int32), H, d, rot, 10000.0)[0]
+            exp = np.zeros(d)
+            for k, val in want.items():
+                exp[k] = val
+            _close(y, exp, 1e-15, f"basis e_{src} at position {p}")
+
+
+def pin_rope_frequency_ladder(orc):
+    """Pair i turns at base^(-2i/rotary_ndims) radians per position.
+
+    With base 10000 and rotary 4 (the sizes of the pages' RoPE parity test,
+    head_dim 6) pair 1 turns at 10000^(-1/2) = 1/100, so position 100 turns
+    e_1 by exactly one radian; with base 10000 and rotary 8 the four pairs turn
+    at 1, 1/10, 1/100, 1/1000: position 1000 turns pair i by 1000 / 10^i.
+    """
+    x = np.zeros((1, 6), np.float32)
+    x[0, 1] = 1.0
+    y = orc.rope(x, np.array([100], np.int32), 1, 6, 4, 10000.0)[0]
+    _close(y, [0, math.cos(1.0), 0, math.sin(1.0), 0, 0], 1e-14, "rotary 4 of head_dim 6, pair 1")
+    for i, turns in enumerate((1000.0, 100.0, 10.0, 1.0)):
+        x = np.zeros((1, 8), np.float32)
+        x[0, i] = 1.0
+        y = orc.rope(x, np.array([1000], np.int32), 1, 8, 8, 10000.0)[0]
+        exp = np.zeros(8)
+        exp[i], exp[i + 4] = math.cos(turns), math.sin(turns)
+        _close(y, exp, 1e-12, f"rotary 8 pair {i}")
+
+
+def pin_rope_pair_norms_preserved(orc):
+    """Each rotated pair keeps its length."""
+    r = _rng("ropenorm")
+    n, H, d, rot = 5, 2, 16, 12
+    x = r.standard_normal((n, H * d)).astype(np.float32)
+    pos = r.integers(0, 40000, size=n).astype(np.int32)
+    y = orc.rope(x, pos, H, d, rot, 1e6).reshape(n, H, d)
+    xs = x.reshape(n, H, d).astype(np.float64)
+    h = rot // 2
+    _close(np.hypot(y[:, :, :h], y[:, :, h:rot]), np.hypot(xs[:, :, :h], xs[:, :, h:rot]), 1e-12, "pair norms")
+
+
+def pin_rope_composes(orc):
+    """Rotating to p1 and then by p2 equals rotating to p1 + p2 (up to the f32 hand-over)."""
+    r = _rng("ropecomp")
+    n, H, d, rot = 4, 2, 8, 8
+    x = r.standard_normal((n, H * d)).astype(np.float32)
+    p1 = np.array([3, 50, 700, 9000], np.int32)
+    p2 = np.array([4, 1, 300, 11], np.int32)
+    two = orc.rope(orc.rope(x, p1, H, d, rot, 10000.0).astype(np.float32), p2, H, d, rot, 10000.0)
+    _close(two, orc.rope(x, p1 + p2, H, d, rot, 10000.0), 2e-6, "R(p2) R(p1) = R(p1 + p2)")
+
+
+def pin_rope_relative_position(orc):
+    """q at position p and k at position p' score the same for every equal offset p - p'."""
+    r = _rng("roperel")
+    H, d, rot = 2, 8, 8
+    q = r.standard_normal((1, H * d)).astype(np.float32)
+    k = r.standard_normal((1, H * d)).astype(np.float32)
+    for off in (0, 1, 7, 250):
+        scores = []
+        for base_pos in (0, 13, 1000, 31000):
+            rq = orc.rope(q, np.array([base_pos + off], np.int32), H, d, rot, 10000.0).reshape(H, d)
+            rk = orc.rope(k, np.array([base_pos], np.int32), H, d, rot, 10000.0).reshape(H, d)
+            scores.append((rq * rk).sum(axis=1))
+        for sc in scores[1:]:
+            _close(sc, scores[0], 1e-9, f"offset {off}")
+
+
+def pin_rope_brute(orc):
+    """Complex-number formulation (oracle/brute.py) on random rows, partial rotary and several bases."""
+    r = _rng("ropebrute")
+    for n, H, d, rot, base in [(5, 3, 8, 8, 10000.0), (3, 2, 12, 4, 10000.0), (6, 4, 32, 16, 1e6),
+                               (2, 1, 6, 2, 500.0), (4, 2, 128, 128, 10000.0), (4, 2, 128, 32, 10000.0)]:
+        x = r.standard_normal((n, H * d)).astype(np.float32)
+        pos = r.integers(0, 33000, size=n).astype(np.int32)
+        _close(orc.rope(x, pos, H, d, rot, base), brute.rope(x, pos, H, d, rot, base), 1e-9,
+               f"rope brute n={n} H={H} d={d} rot={rot}")
+
+
+def pin_rope_pages_case(orc):
+    """The sizes and inputs of the pages' RoPE parity test, at position offsets 0 and 3.
+
+    trustformers-core 0.2.0 ..., gpu_tests ``oxicuda_resident_rope_parity_with_offset``:
+    seq 2, 2 heads, head_dim 6, rotary 4, base 10000, element t of the input
+    = 0.31 t - 1.5 (f32).  No expected values are printed; pair 0 turns by the
+    position and pair 1 by a hundredth of it, so each output is written out here.
+    """
+    seq, H, d, rot = 2, 2, 6, 4
+    x = (np.arange(seq * H * d, dtype=np.float32) * np.float32(0.31) - np.float32(1.5)).reshape(seq, H * d)
+    for offset in (0, 3):
+        pos = np.arange(seq, dtype=np.int32) + offset
+        y = orc.rope(x, pos, H, d, rot, 10000.0).reshape(seq, H, d)
+        xs = x.reshape(seq, H, d).astype(np.float64)
+        for t in range(seq):
+            p = float(pos[t])
+            for h in range(H):
+                a0, a1 = p, p / 100.0
+                e = [xs[t, h, 0] * math.cos(a0) - xs[t, h, 2] * math.sin(a0),
+                     xs[t, h, 1] * math.cos(a1) - xs[t, h, 3] * math.sin(a1),
+                     xs[t, h, 0] * math.sin(a0) + xs[t, h, 2] * math.cos(a0),
+                     xs[t, h, 1] * math.sin(a1) + xs[t, h, 3] * math.cos(a1),
+                     xs[t, h, 4], xs[t, h, 5]]
+                _close(y[t, h], e, 1e-12, f"offset {offset} row {t} head {h}")
+        _close(y.reshape(seq, H * d), brute.rope(x, pos, H, d, rot, 10000.0), 1e-12, f"brute offset {offset}")
+
+
+def pin_rope_rejects_bad_sizes(orc):
+    """Odd rotary_ndims, rotary_ndims > head_dim and a non-positive base are refused."""
+    x = np.ones((1, 8), np.float32)
+    for rot, base in ((3, 10000.0), (10, 10000.0), (8, 0.0), (-2, 10000.0)):
+        try:
+            orc.rope(x, np.array([1], np.int32), 1, 8, rot, base)
+        except ValueError:
+            continue
+        raise AssertionError(f"rotary {rot} base {base} accepted")
 
 
 ALL_PINS = [(name, fn) for name, fn in sorted(globals().items()) if name.startswith("pin_")]

@@ -52,6 +52,15 @@ MUTANTS = [
     ("cached_rows_offset_dropped", "        n = P + r + 1; /* keys visible to this query */",
      "        n = r + 1; /* keys visible to this query */"),
     ("cached_modulo_head_map", "kh = h / (H / Hkv), r, j, l;", "kh = h % Hkv, r, j, l;"),
+    ("rope_sign_flip", "yr[i] = x1 * c - x2 * sn;", "yr[i] = x1 * c + x2 * sn;"),
+    ("rope_sin_cos_swapped", "yr[i + half] = x1 * sn + x2 * c;", "yr[i + half] = x1 * c + x2 * sn;"),
+    ("rope_exponent_uses_head_dim", "-2.0 * (double)i / (double)rotary_ndims", "-2.0 * (double)i / (double)d"),
+    ("rope_exponent_off_by_one", "-2.0 * (double)i / (double)rotary_ndims", "-2.0 * (double)(i + 1) / (double)rotary_ndims"),
+    ("rope_adjacent_pairs", "double x1 = (double)xr[i], x2 = (double)xr[i + half];",
+     "double x1 = (double)xr[2 * i], x2 = (double)xr[2 * i + 1];"),
+    ("rope_row_index_as_position", "double a = (double)pos[t] * freq;", "double a = (double)t * freq;"),
+    ("rope_tail_zeroed", "for (l = 0; l < d; ++l) yr[l] = (double)xr[l];",
+     "for (l = 0; l < d; ++l) yr[l] = l < rotary_ndims ? (double)xr[l] : 0.0;"),
 ]
 
 
