@@ -110,6 +110,27 @@ def cpu_baseline(inp, cfg, target_s):
     }
 
 
+def time_call(torch, run, filler=None, warm=5, reps=10):
+    """Mean milliseconds of `run` over `reps` calls, each bracketed by events on the current stream.
+
+    `filler` (a long call) is enqueued first, so that the GPU is still busy with it
+    while the host enqueues the timed calls: the events then see GPU time only,
+    not the host's launch latency between two short calls.
+    """
+    for _ in range(warm):
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    if filler is not None:
+        filler()
+    for e0, e1 in ev:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -258,16 +279,7 @@ def main():
         cached = [scfg.n_new] * ccfg.M
         run = lambda: taf.attn_prefill_cached(cq, ck, cv, bk, bv, cached, cout, ccfg.M, ccfg.n_new, ccfg.H,
                                               ccfg.Hkv, ccfg.d, ccfg.max_len, ccfg.scale)
-        for _ in range(5):
-            run()
-        torch.cuda.synchronize()
-        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-        for e0, e1 in cev:
-            e0.record()
-            run()
-            e1.record()
-        torch.cuda.synchronize()
-        c_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in cev]))
+        c_ms = time_call(torch, run, calls["prefill"])
         c_tflops = ccfg.flops(cached) / (c_ms * 1e-3) / 1e12
         result["next_rows"] = {"prefill_cached": {
             "workload": ccfg.name, "us": round(c_ms * 1e3, 2), "tflops": round(c_tflops, 3),
@@ -276,6 +288,33 @@ def main():
                     "timed separately, not part of ms_per_step"}}
         log(f"prefill_cached: {c_ms * 1e3:.1f} us, {c_tflops:.1f} TFLOP/s")
         del cq, ck, cv, cout
+
+        # Rotary embedding fused into the append and the decode: the bulk append
+        # with every key rotated (base 10000), and the decode step with the new
+        # key rotated into the cache and the query rotated (base 1e6, as Qwen).
+        rot = pcfg.d
+        fill = calls["prefill"]
+        r_bulk = time_call(torch, lambda: taf.kv_cache_scatter_rope(pk, pv, bk, bv, [0] * scfg.M, scfg.M, scfg.n_new,
+                                                                    scfg.Hkv, scfg.d, scfg.max_len, rot, 1e4), fill)
+        r_app = time_call(torch, lambda: taf.kv_cache_scatter_rope(dkn, dvn, dkc, dvc, append_pos, dcfg.M, 1,
+                                                                   dcfg.Hkv, dcfg.d, dcfg.max_len, rot, 1e6), fill)
+        r_dec = time_call(torch, lambda: taf.attn_decode_gqa_batched_rope(dq, dkc, dvc, lens_list, dout, dcfg.M,
+                                                                          dcfg.H, dcfg.Hkv, dcfg.d, dcfg.max_len,
+                                                                          dcfg.scale, rot, 1e6, ws), fill)
+        r_blk_gbs = scfg.bytes / (r_bulk * 1e-3) / 1e9
+        r_dec_gbs = dec_bytes / (r_dec * 1e-3) / 1e9
+        result["next_rows"]["rope"] = {
+            "bulk_scatter_rope": {"us": round(r_bulk * 1e3, 2), "gbs": round(r_blk_gbs, 2),
+                                  "frac_hbm": round(r_blk_gbs / HBM_PEAK_GBS, 4), "rotary_ndims": rot,
+                                  "theta": 1e4, "plain_us": round(per["bulk_scatter"] * 1e3, 2)},
+            "append_rope": {"us": round(r_app * 1e3, 2), "plain_us": round(per["append"] * 1e3, 2)},
+            "decode_rope": {"us": round(r_dec * 1e3, 2), "gbs": round(r_dec_gbs, 2),
+                            "frac_hbm": round(r_dec_gbs / HBM_PEAK_GBS, 4), "rotary_ndims": rot, "theta": 1e6,
+                            "plain_us": round(per["decode"] * 1e3, 2)},
+            "note": "timed separately (10 calls after 5 warm-up calls each, queued behind a prefill), "
+                    "not part of ms_per_step"}
+        log(f"rope: bulk append {r_bulk * 1e3:.1f} us ({r_blk_gbs:.0f} GB/s), append {r_app * 1e3:.1f} us, "
+            f"decode {r_dec * 1e3:.1f} us ({r_dec_gbs:.0f} GB/s)")
 
     # Free the GPU copies before the host-side leg.
     del pq, pk, pv, pout, bk, bv, dq, dkn, dvn, dkc, dvc, dout, ws

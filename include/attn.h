@@ -16,6 +16,8 @@
  *   attn_prefill_cached      a chunk of new tokens behind an existing cache:
  *                            append, then attend with the causal mask offset
  *                            by each sequence's cached length.
+ * The append and the decode also come with a rotary position embedding fused
+ * in (kv_cache_scatter_rope, attn_decode_gqa_batched_rope).
  *
  * Conventions shared by every entry point
  *   - Tensors are f32, row-major, contiguous, in DEVICE memory owned by the
@@ -37,7 +39,7 @@
  * `incremental_attention_gpu_with_stream`, `kv_cache_scatter_gpu`);
  * trustformers-core 0.2.0 src/gpu_ops/cuda/oxicuda/attention.rs
  * (`attention_prefill_gpu_to_gpu`, `attention_decode_gpu_to_gpu`,
- * `checked_len`); realizar 0.8.5
+ * `checked_len`, `rope_neox_gpu_to_gpu`, `rope_reference`); realizar 0.8.5
  * src/cuda/executor/cache_from_cache_from_kv_cache.rs (`init_kv_cache_gpu`,
  * `init_batched_kv_cache_gpu`).
  */
@@ -195,6 +197,55 @@ int attn_decode_gqa_batched(const float *q, const float *k_cache, const float *v
 int kv_cache_scatter(const float *k_new, const float *v_new, float *k_cache, float *v_cache,
                      const int32_t *cache_lens, int32_t num_seqs, int32_t n_new,
                      int32_t num_kv_heads, int32_t head_dim, int32_t max_len, void *stream);
+
+/*
+ * Rotary position embedding (used by the *_rope entry points).
+ *
+ * Defines: trustformers-core `rope_neox_gpu_to_gpu` (GPT-NeoX half-split
+ * partial rotation of [seq, heads, head_dim] rows at an absolute position
+ * offset: 0 for a prefill, the cached length during decode) and its CPU
+ * helper `rope_reference`; realizar `set_rope_theta` / `apply_rope_to_buffer`
+ * (the same rotation over the whole head, base = rope theta, e.g. 10000 or
+ * 1000000).  In every head of a row at position p, dim i < half =
+ * rotary_ndims / 2 is paired with dim i + half and the pair is turned by
+ * a = p * rope_theta^(-2 i / rotary_ndims) radians:
+ *   y_i = x_i cos a - x_{i+half} sin a,   y_{i+half} = x_i sin a + x_{i+half} cos a;
+ * dims >= rotary_ndims are unchanged.
+ *   rotary_ndims  0 (no rotation) or a multiple of 8 up to head_dim
+ *   rope_theta    the base; finite and > 0
+ * Accuracy: angles are reduced to a fraction of a turn in double before the
+ * single-precision sin/cos, so a rotated element is within a few f32 ulps of
+ * the exact rotation at every int32 position (a single-precision angle
+ * p * freq would be off by up to ~2e-3 rad near p = 32768).
+ * Extra errors: rotary_ndims < 0 or > head_dim, rope_theta not finite or <= 0
+ * (INVALID_DIM); rotary_ndims not a multiple of 8 (UNSUPPORTED).  They are
+ * checked after the arguments the plain entry point checks.
+ */
+
+/*
+ * kv_cache_scatter with the keys rotated to their cache positions: key row r
+ * of sequence m is stored rotated to position cache_lens[m] + r.  Values are
+ * copied verbatim, as are the key dims >= rotary_ndims.  Same arguments,
+ * layout and errors as kv_cache_scatter, plus rotary_ndims and rope_theta.
+ */
+int kv_cache_scatter_rope(const float *k_new, const float *v_new, float *k_cache, float *v_cache,
+                          const int32_t *cache_lens, int32_t num_seqs, int32_t n_new,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t max_len,
+                          int32_t rotary_ndims, float rope_theta, void *stream);
+
+/*
+ * attn_decode_gqa_batched with the query rotated: sequence m's query is the
+ * newest token, at position seq_lens[m] - 1, and is rotated to that position
+ * before it is scored; the cached keys are used as stored (already rotated,
+ * e.g. by kv_cache_scatter_rope).  Same arguments, layout, workspace and errors
+ * as attn_decode_gqa_batched, plus rotary_ndims and rope_theta.
+ */
+int attn_decode_gqa_batched_rope(const float *q, const float *k_cache, const float *v_cache,
+                                 const int32_t *seq_lens, float *out, int32_t num_seqs,
+                                 int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_len, float scale, int32_t rotary_ndims,
+                                 float rope_theta, void *workspace, size_t workspace_bytes,
+                                 void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *attn_status_string(int status);

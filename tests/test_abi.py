@@ -38,7 +38,7 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "attn_prefill", "attn_prefill_cached", "attn_decode_workspace_bytes", "attn_decode_gqa_batched",
-        "kv_cache_scatter", "attn_status_string"])
+        "kv_cache_scatter", "attn_status_string", "kv_cache_scatter_rope", "attn_decode_gqa_batched_rope"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -163,6 +163,51 @@ def test_prefill_cached_validation(lib):
     assert cached(lib, out=A + 64) == ALIAS          # out over q
     assert cached(lib, vc=C_ + 1024) == ALIAS        # the caches overlap
     assert cached(lib, kc=B_) == ALIAS               # cache over k_new
+
+
+def test_scatter_rope_validation(lib):
+    def call(rot=64, theta=10000.0, d=64, **kw):
+        lens = kw.pop("lens", (0, 3))
+        arr = (ctypes.c_int32 * len(lens))(*lens)
+        args = dict(kn=A, vn=B_, kc=C_, vc=O_, M=2, n_new=2, Hkv=2, max_len=8)
+        args.update(kw)
+        return lib.kv_cache_scatter_rope(args["kn"], args["vn"], args["kc"], args["vc"], arr, args["M"],
+                                         args["n_new"], args["Hkv"], d, args["max_len"], rot, theta, None)
+    assert call(kn=0) == NULL
+    assert call(lens=(0, 7)) == DIM              # the plain append's checks come first
+    assert call(d=48) == UNSUP
+    assert call(rot=-8) == DIM
+    assert call(rot=72) == DIM                   # wider than head_dim 64
+    assert call(theta=0.0) == DIM
+    assert call(theta=-10000.0) == DIM
+    assert call(theta=float("inf")) == DIM
+    assert call(theta=float("nan")) == DIM
+    assert call(rot=12) == UNSUP                 # not a multiple of 8
+    assert call(rot=6) == UNSUP
+    assert call(kc=A) == ALIAS
+
+
+def test_decode_rope_validation(lib):
+    def call(rot=128, theta=1e6, d=128, lens=(5, 100), ws_bytes=None, **kw):
+        arr = (ctypes.c_int32 * len(lens))(*lens)
+        M, H, Hkv, max_len = 2, 8, 2, 100
+        if ws_bytes is None:
+            ws_bytes = lib.attn_decode_workspace_bytes(M, H, 128, max_len)
+        args = dict(q=A, k=B_, v=C_, out=O_, ws=W_)
+        args.update(kw)
+        return lib.attn_decode_gqa_batched_rope(args["q"], args["k"], args["v"], arr, args["out"], M, H, Hkv, d,
+                                                max_len, 0.088, rot, theta, args["ws"], ws_bytes, None)
+    assert call(q=0) == NULL
+    assert call(lens=(101, 3)) == DIM
+    assert call(d=96) == UNSUP
+    assert call(ws_bytes=16) == WS
+    assert call(out=A) == ALIAS
+    assert call(rot=136) == DIM
+    assert call(rot=-1) == DIM
+    assert call(theta=0.0) == DIM
+    assert call(theta=float("nan")) == DIM
+    assert call(rot=4) == UNSUP
+    assert call(rot=100) == UNSUP
 
 
 def test_python_binding_rejects_cpu_tensors():

@@ -25,6 +25,8 @@ __all__ = [
     "attn_decode_workspace_bytes",
     "attn_decode_gqa_batched",
     "kv_cache_scatter",
+    "kv_cache_scatter_rope",
+    "attn_decode_gqa_batched_rope",
     "attn_status_string",
     "library",
     "library_path",
@@ -72,6 +74,11 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_gqa_batched.restype = ctypes.c_int
         lib.kv_cache_scatter.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, p]
         lib.kv_cache_scatter.restype = ctypes.c_int
+        lib.kv_cache_scatter_rope.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p]
+        lib.kv_cache_scatter_rope.restype = ctypes.c_int
+        lib.attn_decode_gqa_batched_rope.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, f32, p,
+                                                     sz, p]
+        lib.attn_decode_gqa_batched_rope.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -161,37 +168,69 @@ def attn_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, ma
     return int(library().attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_len))
 
 
-def attn_decode_gqa_batched(q, k_cache, v_cache, seq_lens: Sequence[int], out, num_seqs: int,
-                            num_heads: int, num_kv_heads: int, head_dim: int, max_len: int,
-                            scale: float, workspace, stream=None) -> None:
-    """Batched GQA decode; ``seq_lens`` is a host sequence of M ints; ``workspace`` a device tensor."""
+def _decode_ptrs(q, k_cache, v_cache, out, workspace, num_seqs, num_heads, num_kv_heads, head_dim, max_len):
     import torch
 
     dev = q.device
     qn = num_seqs * num_heads * head_dim
     cn = num_seqs * num_kv_heads * max_len * head_dim
-    pq = _check_tensor("q", q, qn, dev)
-    pk = _check_tensor("k_cache", k_cache, cn, dev)
-    pv = _check_tensor("v_cache", v_cache, cn, dev)
+    ptrs = [_check_tensor("q", q, qn, dev), _check_tensor("k_cache", k_cache, cn, dev),
+            _check_tensor("v_cache", v_cache, cn, dev)]
     po = _check_tensor("out", out, qn, dev)
     if not isinstance(workspace, torch.Tensor) or workspace.device != dev or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the same GPU")
-    ws_bytes = workspace.numel() * workspace.element_size()
+    return dev, ptrs, po, workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def attn_decode_gqa_batched(q, k_cache, v_cache, seq_lens: Sequence[int], out, num_seqs: int,
+                            num_heads: int, num_kv_heads: int, head_dim: int, max_len: int,
+                            scale: float, workspace, stream=None) -> None:
+    """Batched GQA decode; ``seq_lens`` is a host sequence of M ints; ``workspace`` a device tensor."""
+    dev, ptrs, po, pw, ws_bytes = _decode_ptrs(q, k_cache, v_cache, out, workspace, num_seqs, num_heads,
+                                               num_kv_heads, head_dim, max_len)
     lens = _host_ints("seq_lens", seq_lens, num_seqs)
     _call("attn_decode_gqa_batched",
-          library().attn_decode_gqa_batched(pq, pk, pv, lens, po, num_seqs, num_heads, num_kv_heads,
-                                            head_dim, max_len, scale, workspace.data_ptr(), ws_bytes,
-                                            _stream_ptr(dev, stream)))
+          library().attn_decode_gqa_batched(*ptrs, lens, po, num_seqs, num_heads, num_kv_heads, head_dim,
+                                            max_len, scale, pw, ws_bytes, _stream_ptr(dev, stream)))
+
+
+def attn_decode_gqa_batched_rope(q, k_cache, v_cache, seq_lens: Sequence[int], out, num_seqs: int,
+                                 num_heads: int, num_kv_heads: int, head_dim: int, max_len: int,
+                                 scale: float, rotary_ndims: int, rope_theta: float, workspace,
+                                 stream=None) -> None:
+    """attn_decode_gqa_batched with each query rotated to position seq_lens[m] - 1 first."""
+    dev, ptrs, po, pw, ws_bytes = _decode_ptrs(q, k_cache, v_cache, out, workspace, num_seqs, num_heads,
+                                               num_kv_heads, head_dim, max_len)
+    lens = _host_ints("seq_lens", seq_lens, num_seqs)
+    _call("attn_decode_gqa_batched_rope",
+          library().attn_decode_gqa_batched_rope(*ptrs, lens, po, num_seqs, num_heads, num_kv_heads, head_dim,
+                                                 max_len, scale, rotary_ndims, rope_theta, pw, ws_bytes,
+                                                 _stream_ptr(dev, stream)))
+
+
+def _scatter_ptrs(k_new, v_new, k_cache, v_cache, num_seqs, n_new, num_kv_heads, head_dim, max_len):
+    dev = k_new.device
+    sn = num_seqs * n_new * num_kv_heads * head_dim
+    cn = num_seqs * num_kv_heads * max_len * head_dim
+    return dev, [_check_tensor("k_new", k_new, sn, dev), _check_tensor("v_new", v_new, sn, dev),
+                 _check_tensor("k_cache", k_cache, cn, dev), _check_tensor("v_cache", v_cache, cn, dev)]
 
 
 def kv_cache_scatter(k_new, v_new, k_cache, v_cache, cache_lens: Sequence[int], num_seqs: int,
                      n_new: int, num_kv_heads: int, head_dim: int, max_len: int, stream=None) -> None:
     """cache[m, kh, cache_lens[m] + r, :] = new[m, r, kh*d:(kh+1)*d] for K and V."""
-    dev = k_new.device
-    sn = num_seqs * n_new * num_kv_heads * head_dim
-    cn = num_seqs * num_kv_heads * max_len * head_dim
-    ptrs = [_check_tensor("k_new", k_new, sn, dev), _check_tensor("v_new", v_new, sn, dev),
-            _check_tensor("k_cache", k_cache, cn, dev), _check_tensor("v_cache", v_cache, cn, dev)]
+    dev, ptrs = _scatter_ptrs(k_new, v_new, k_cache, v_cache, num_seqs, n_new, num_kv_heads, head_dim, max_len)
     lens = _host_ints("cache_lens", cache_lens, num_seqs)
     _call("kv_cache_scatter", library().kv_cache_scatter(*ptrs, lens, num_seqs, n_new, num_kv_heads,
                                                          head_dim, max_len, _stream_ptr(dev, stream)))
+
+
+def kv_cache_scatter_rope(k_new, v_new, k_cache, v_cache, cache_lens: Sequence[int], num_seqs: int,
+                          n_new: int, num_kv_heads: int, head_dim: int, max_len: int, rotary_ndims: int,
+                          rope_theta: float, stream=None) -> None:
+    """kv_cache_scatter with key row r rotated to position cache_lens[m] + r."""
+    dev, ptrs = _scatter_ptrs(k_new, v_new, k_cache, v_cache, num_seqs, n_new, num_kv_heads, head_dim, max_len)
+    lens = _host_ints("cache_lens", cache_lens, num_seqs)
+    _call("kv_cache_scatter_rope",
+          library().kv_cache_scatter_rope(*ptrs, lens, num_seqs, n_new, num_kv_heads, head_dim, max_len,
+                                          rotary_ndims, rope_theta, _stream_ptr(dev, stream)))

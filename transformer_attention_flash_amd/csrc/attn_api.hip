@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include "launch.h"
+#include "rope.h"
 
 namespace {
 
@@ -43,6 +44,91 @@ bool checked_mul(std::initializer_list<int64_t> xs, int64_t limit, int64_t *out)
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+// Rotary embedding arguments: 0 <= rotary_ndims <= head_dim, a multiple of 8
+// (so a 16-byte vector never straddles the rotated and unrotated dims), and a
+// finite positive base.
+int check_rope(int32_t rotary_ndims, int32_t head_dim, float rope_theta) {
+    if (rotary_ndims < 0 || rotary_ndims > head_dim) return ATTN_ERR_INVALID_DIM;
+    if (!isfinite(rope_theta) || !(rope_theta > 0.0f)) return ATTN_ERR_INVALID_DIM;
+    if (rotary_ndims % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+// Validation shared by the plain and rotary variants of decode and append;
+// on success *args is filled and nothing has been enqueued.
+int prepare_decode(const float *q, const float *k_cache, const float *v_cache, const int32_t *seq_lens,
+                   float *out, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t max_len, float scale, void *workspace, size_t workspace_bytes,
+                   attn::DecodeArgs *args) {
+    if (!q || !k_cache || !v_cache || !seq_lens || !out || !workspace) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS) return ATTN_ERR_INVALID_DIM;
+    if (num_heads <= 0 || num_kv_heads <= 0 || max_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_DIM;
+    if (num_kv_heads > num_heads || num_heads % num_kv_heads != 0) return ATTN_ERR_INVALID_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID_DIM;
+    SeqInts lens{};
+    for (int32_t m = 0; m < num_seqs; ++m) {
+        if (seq_lens[m] < 0 || seq_lens[m] > max_len) return ATTN_ERR_INVALID_DIM;
+        lens.v[m] = seq_lens[m];
+    }
+    if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+        !aligned16(workspace))
+        return ATTN_ERR_UNSUPPORTED;
+    int64_t q_elems, cache_elems;
+    if (!checked_mul({num_seqs, num_heads, head_dim}, kMaxElems, &q_elems) ||
+        !checked_mul({num_seqs, num_kv_heads, max_len, head_dim}, kMaxElems, &cache_elems))
+        return ATTN_ERR_OVERFLOW;
+    int64_t units;  // upper bound on pass-1 work units and workspace slots
+    if (!checked_mul({num_seqs, num_heads, attn::decode_max_splits(max_len)}, kMaxElems32, &units))
+        return ATTN_ERR_OVERFLOW;
+    const size_t need = attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_len);
+    if (need == 0) return ATTN_ERR_OVERFLOW;
+    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    const int64_t qb = q_elems * 4, cb = cache_elems * 4;
+    if (overlaps(out, qb, q, qb) || overlaps(out, qb, k_cache, cb) || overlaps(out, qb, v_cache, cb) ||
+        overlaps(out, qb, workspace, (int64_t)need) || overlaps(workspace, (int64_t)need, q, qb) ||
+        overlaps(workspace, (int64_t)need, k_cache, cb) || overlaps(workspace, (int64_t)need, v_cache, cb))
+        return ATTN_ERR_ALIAS;
+
+    const int32_t max_splits = attn::decode_max_splits(max_len);
+    float *ws = static_cast<float *>(workspace);
+    float *ws_acc = ws;
+    float *ws_ml = ws + (size_t)num_seqs * num_heads * max_splits * head_dim;
+    *args = attn::DecodeArgs{q,   k_cache,      v_cache,   out,        ws_acc,  ws_ml,
+                             lens, num_seqs,    num_heads, num_kv_heads, head_dim, max_len,
+                             max_splits, scale};
+    return ATTN_OK;
+}
+
+int prepare_scatter(const float *k_new, const float *v_new, float *k_cache, float *v_cache,
+                    const int32_t *cache_lens, int32_t num_seqs, int32_t n_new, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t max_len, attn::ScatterArgs *args) {
+    if (!k_new || !v_new || !k_cache || !v_cache || !cache_lens) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS) return ATTN_ERR_INVALID_DIM;
+    if (n_new <= 0 || num_kv_heads <= 0 || max_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_DIM;
+    SeqInts pos{};
+    for (int32_t m = 0; m < num_seqs; ++m) {
+        if (cache_lens[m] < 0 || (int64_t)cache_lens[m] + n_new > max_len) return ATTN_ERR_INVALID_DIM;
+        pos.v[m] = cache_lens[m];
+    }
+    if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+        return ATTN_ERR_UNSUPPORTED;
+    int64_t src_elems, cache_elems, per_seq;
+    if (!checked_mul({num_seqs, n_new, num_kv_heads, head_dim}, kMaxElems, &src_elems) ||
+        !checked_mul({num_seqs, num_kv_heads, max_len, head_dim}, kMaxElems, &cache_elems) ||
+        !checked_mul({n_new, num_kv_heads, head_dim}, kMaxElems32, &per_seq))
+        return ATTN_ERR_OVERFLOW;
+    const int64_t sb = src_elems * 4, cb = cache_elems * 4;
+    if (overlaps(k_cache, cb, v_cache, cb) || overlaps(k_cache, cb, k_new, sb) ||
+        overlaps(k_cache, cb, v_new, sb) || overlaps(v_cache, cb, k_new, sb) || overlaps(v_cache, cb, v_new, sb))
+        return ATTN_ERR_ALIAS;
+
+    *args = attn::ScatterArgs{k_new, v_new, k_cache, v_cache, pos, num_seqs, n_new, num_kv_heads, head_dim,
+                              max_len};
+    return ATTN_OK;
+}
 
 }  // namespace
 
@@ -168,72 +254,48 @@ int attn_decode_gqa_batched(const float *q, const float *k_cache, const float *v
                             const int32_t *seq_lens, float *out, int32_t num_seqs, int32_t num_heads,
                             int32_t num_kv_heads, int32_t head_dim, int32_t max_len, float scale,
                             void *workspace, size_t workspace_bytes, void *stream) {
-    if (!q || !k_cache || !v_cache || !seq_lens || !out || !workspace) return ATTN_ERR_NULL;
-    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS) return ATTN_ERR_INVALID_DIM;
-    if (num_heads <= 0 || num_kv_heads <= 0 || max_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_DIM;
-    if (num_kv_heads > num_heads || num_heads % num_kv_heads != 0) return ATTN_ERR_INVALID_DIM;
-    if (!isfinite(scale)) return ATTN_ERR_INVALID_DIM;
-    SeqInts lens{};
-    for (int32_t m = 0; m < num_seqs; ++m) {
-        if (seq_lens[m] < 0 || seq_lens[m] > max_len) return ATTN_ERR_INVALID_DIM;
-        lens.v[m] = seq_lens[m];
-    }
-    if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-        !aligned16(workspace))
-        return ATTN_ERR_UNSUPPORTED;
-    int64_t q_elems, cache_elems;
-    if (!checked_mul({num_seqs, num_heads, head_dim}, kMaxElems, &q_elems) ||
-        !checked_mul({num_seqs, num_kv_heads, max_len, head_dim}, kMaxElems, &cache_elems))
-        return ATTN_ERR_OVERFLOW;
-    int64_t units;  // upper bound on pass-1 work units and workspace slots
-    if (!checked_mul({num_seqs, num_heads, attn::decode_max_splits(max_len)}, kMaxElems32, &units))
-        return ATTN_ERR_OVERFLOW;
-    const size_t need = attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_len);
-    if (need == 0) return ATTN_ERR_OVERFLOW;
-    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-    const int64_t qb = q_elems * 4, cb = cache_elems * 4;
-    if (overlaps(out, qb, q, qb) || overlaps(out, qb, k_cache, cb) || overlaps(out, qb, v_cache, cb) ||
-        overlaps(out, qb, workspace, (int64_t)need) || overlaps(workspace, (int64_t)need, q, qb) ||
-        overlaps(workspace, (int64_t)need, k_cache, cb) || overlaps(workspace, (int64_t)need, v_cache, cb))
-        return ATTN_ERR_ALIAS;
-
-    const int32_t max_splits = attn::decode_max_splits(max_len);
-    float *ws = static_cast<float *>(workspace);
-    float *ws_acc = ws;
-    float *ws_ml = ws + (size_t)num_seqs * num_heads * max_splits * head_dim;
-    attn::DecodeArgs a{q,   k_cache,      v_cache,   out,        ws_acc,  ws_ml,
-                       lens, num_seqs,    num_heads, num_kv_heads, head_dim, max_len,
-                       max_splits, scale};
+    attn::DecodeArgs a;
+    const int st = prepare_decode(q, k_cache, v_cache, seq_lens, out, num_seqs, num_heads, num_kv_heads,
+                                  head_dim, max_len, scale, workspace, workspace_bytes, &a);
+    if (st != ATTN_OK) return st;
     return from_hip(attn::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int attn_decode_gqa_batched_rope(const float *q, const float *k_cache, const float *v_cache,
+                                 const int32_t *seq_lens, float *out, int32_t num_seqs, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_len, float scale,
+                                 int32_t rotary_ndims, float rope_theta, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    attn::DecodeArgs a;
+    int st = prepare_decode(q, k_cache, v_cache, seq_lens, out, num_seqs, num_heads, num_kv_heads, head_dim,
+                            max_len, scale, workspace, workspace_bytes, &a);
+    if (st != ATTN_OK) return st;
+    if ((st = check_rope(rotary_ndims, head_dim, rope_theta)) != ATTN_OK) return st;
+    const attn::RopeParams rp = attn::make_rope(rotary_ndims, rope_theta);
+    return from_hip(attn::launch_decode(a, static_cast<hipStream_t>(stream), &rp));
 }
 
 int kv_cache_scatter(const float *k_new, const float *v_new, float *k_cache, float *v_cache,
                      const int32_t *cache_lens, int32_t num_seqs, int32_t n_new, int32_t num_kv_heads,
                      int32_t head_dim, int32_t max_len, void *stream) {
-    if (!k_new || !v_new || !k_cache || !v_cache || !cache_lens) return ATTN_ERR_NULL;
-    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS) return ATTN_ERR_INVALID_DIM;
-    if (n_new <= 0 || num_kv_heads <= 0 || max_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_DIM;
-    SeqInts pos{};
-    for (int32_t m = 0; m < num_seqs; ++m) {
-        if (cache_lens[m] < 0 || (int64_t)cache_lens[m] + n_new > max_len) return ATTN_ERR_INVALID_DIM;
-        pos.v[m] = cache_lens[m];
-    }
-    if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
-    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
-        return ATTN_ERR_UNSUPPORTED;
-    int64_t src_elems, cache_elems, per_seq;
-    if (!checked_mul({num_seqs, n_new, num_kv_heads, head_dim}, kMaxElems, &src_elems) ||
-        !checked_mul({num_seqs, num_kv_heads, max_len, head_dim}, kMaxElems, &cache_elems) ||
-        !checked_mul({n_new, num_kv_heads, head_dim}, kMaxElems32, &per_seq))
-        return ATTN_ERR_OVERFLOW;
-    const int64_t sb = src_elems * 4, cb = cache_elems * 4;
-    if (overlaps(k_cache, cb, v_cache, cb) || overlaps(k_cache, cb, k_new, sb) ||
-        overlaps(k_cache, cb, v_new, sb) || overlaps(v_cache, cb, k_new, sb) || overlaps(v_cache, cb, v_new, sb))
-        return ATTN_ERR_ALIAS;
-
-    attn::ScatterArgs a{k_new, v_new, k_cache, v_cache, pos, num_seqs, n_new, num_kv_heads, head_dim, max_len};
+    attn::ScatterArgs a;
+    const int st = prepare_scatter(k_new, v_new, k_cache, v_cache, cache_lens, num_seqs, n_new, num_kv_heads,
+                                   head_dim, max_len, &a);
+    if (st != ATTN_OK) return st;
     return from_hip(attn::launch_kv_scatter(a, static_cast<hipStream_t>(stream)));
+}
+
+int kv_cache_scatter_rope(const float *k_new, const float *v_new, float *k_cache, float *v_cache,
+                          const int32_t *cache_lens, int32_t num_seqs, int32_t n_new, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t max_len, int32_t rotary_ndims, float rope_theta,
+                          void *stream) {
+    attn::ScatterArgs a;
+    int st = prepare_scatter(k_new, v_new, k_cache, v_cache, cache_lens, num_seqs, n_new, num_kv_heads,
+                             head_dim, max_len, &a);
+    if (st != ATTN_OK) return st;
+    if ((st = check_rope(rotary_ndims, head_dim, rope_theta)) != ATTN_OK) return st;
+    const attn::RopeParams rp = attn::make_rope(rotary_ndims, rope_theta);
+    return from_hip(attn::launch_kv_scatter(a, static_cast<hipStream_t>(stream), &rp));
 }
 
 }  // extern "C"

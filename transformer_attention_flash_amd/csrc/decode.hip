@@ -35,6 +35,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "rope.h"
 
 namespace attn {
 namespace {
@@ -82,9 +83,9 @@ __device__ __forceinline__ T load_stream(const T *p) {
 #endif
 }
 
-template <int D>
+template <int D, bool ROPE>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a, UnitMap map,
-                                                                int32_t n_hblk) {
+                                                                int32_t n_hblk, RopeParams rp) {
     constexpr int NT = D / 16;     // 16-column tiles of O^T
     constexpr int KV4 = D / 16;    // 16-byte K vectors per lane per 16-key tile
     constexpr int VW = D >= 64 ? 4 : 2;  // floats per V vector
@@ -123,14 +124,39 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     const int kfirst = k0 + kChunk * wave;
     constexpr int kStep = kChunk * kWavesPerBlock;
 
-    // q^T operand, pre-scaled so scores come out in log2 units.
+    // q^T operand, pre-scaled so scores come out in log2 units.  With a
+    // rotary embedding the query is first turned to the position of the
+    // newest cached token, L - 1 (lane's dims 16j + 4kq .. +3; the partner
+    // dims half a rotary width away are read from the same small q row).
     const float qs = a.scale * kLog2e;
     float qreg[KV4][4];
-    {
-        const float *qp = a.q + ((size_t)m * a.H + (head_ok ? h : 0)) * D + 4 * kq;
+    f32x4 qraw[KV4], qpart[KV4];
+    const float *qhead = a.q + ((size_t)m * a.H + (head_ok ? h : 0)) * D;
+    auto load_q = [&]() {
 #pragma unroll
         for (int j = 0; j < KV4; ++j) {
-            f32x4 v4 = head_ok ? *reinterpret_cast<const f32x4 *>(qp + 16 * j) : f32x4{0, 0, 0, 0};
+            const int l0 = 16 * j + 4 * kq;
+            qraw[j] = head_ok ? *reinterpret_cast<const f32x4 *>(qhead + l0) : f32x4{0, 0, 0, 0};
+            if constexpr (ROPE) {
+                const int pl = l0 < rp.half ? l0 + rp.half : l0 - rp.half;
+                qpart[j] = (head_ok && l0 < rp.rot) ? *reinterpret_cast<const f32x4 *>(qhead + pl)
+                                                    : f32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto finish_q = [&]() {
+#pragma unroll
+        for (int j = 0; j < KV4; ++j) {
+            f32x4 v4 = qraw[j];
+            if constexpr (ROPE) v4 = rope_rotate4(v4, qpart[j], 16 * j + 4 * kq, L > 0 ? L - 1 : 0, rp);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) qreg[j][c] = v4[c] * qs;
+        }
+    };
+    if constexpr (!ROPE) {
+#pragma unroll
+        for (int j = 0; j < KV4; ++j) {
+            const f32x4 v4 = head_ok ? *reinterpret_cast<const f32x4 *>(qhead + 16 * j + 4 * kq) : f32x4{0, 0, 0, 0};
 #pragma unroll
             for (int c = 0; c < 4; ++c) qreg[j][c] = v4[c] * qs;
         }
@@ -199,8 +225,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     // last chunk every lane's row clamps to k1 - 1, one row already in cache.
     load_k(kfirst);
     __builtin_amdgcn_sched_barrier(0);  // K before V, the order the loop keeps
+    if constexpr (ROPE) {
+        // The query's rotation (sin/cos per dim) overlaps the first chunk's
+        // loads: its q loads go out between K and V, so waiting for them
+        // leaves the V loads in flight.
+        load_q();
+        __builtin_amdgcn_sched_barrier(0);
+    }
     load_v(kfirst);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (ROPE) finish_q();
     for (int kb = kfirst; kb < k1; kb += kStep) {
 
         // Chunk kb's K rows into this wave's LDS tile (a wave's LDS accesses
@@ -397,7 +431,7 @@ int32_t query_capacity() {
     if (cap > 0) return cap;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0 ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D>, kThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, false>, kThreads, 0) != hipSuccess ||
         per_cu <= 0)
         return 512;
     cap = cus * per_cu;
@@ -425,7 +459,7 @@ size_t decode_workspace_bytes(int64_t M, int64_t H, int64_t D, int64_t max_len) 
     return (size_t)(slots * (D + 2) * (int64_t)sizeof(float));
 }
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopeParams *rope) {
     const int32_t g = a.H / a.Hkv;
     const int32_t n_hblk = (g + 15) / 16;
     const int64_t units_per_seq = (int64_t)a.Hkv * n_hblk;
@@ -467,11 +501,21 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     dim3 block(kThreads);
     if (acc > 0) {
         dim3 grid(acc);
-        switch (a.D) {
-            case 32: decode_split_kernel<32><<<grid, block, 0, stream>>>(a, map, n_hblk); break;
-            case 64: decode_split_kernel<64><<<grid, block, 0, stream>>>(a, map, n_hblk); break;
-            case 128: decode_split_kernel<128><<<grid, block, 0, stream>>>(a, map, n_hblk); break;
-            default: return hipErrorInvalidValue;
+        if (rope && rope->rot > 0) {
+            switch (a.D) {
+                case 32: decode_split_kernel<32, true><<<grid, block, 0, stream>>>(a, map, n_hblk, *rope); break;
+                case 64: decode_split_kernel<64, true><<<grid, block, 0, stream>>>(a, map, n_hblk, *rope); break;
+                case 128: decode_split_kernel<128, true><<<grid, block, 0, stream>>>(a, map, n_hblk, *rope); break;
+                default: return hipErrorInvalidValue;
+            }
+        } else {
+            const RopeParams none{};
+            switch (a.D) {
+                case 32: decode_split_kernel<32, false><<<grid, block, 0, stream>>>(a, map, n_hblk, none); break;
+                case 64: decode_split_kernel<64, false><<<grid, block, 0, stream>>>(a, map, n_hblk, none); break;
+                case 128: decode_split_kernel<128, false><<<grid, block, 0, stream>>>(a, map, n_hblk, none); break;
+                default: return hipErrorInvalidValue;
+            }
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -11,6 +11,8 @@
 
 namespace attn {
 
+struct RopeParams;  // rope.h
+
 // Per-sequence host values travel in the kernel arguments (at most 32).
 struct SeqInts {
     int32_t v[ATTN_MAX_SEQS];
@@ -24,7 +26,8 @@ struct ScatterArgs {
     SeqInts pos;  // write start position per sequence
     int32_t M, n_new, Hkv, D, max_len;
 };
-hipError_t launch_kv_scatter(const ScatterArgs &a, hipStream_t stream);
+// With rope (rotary_ndims > 0) the keys are rotated to their cache positions.
+hipError_t launch_kv_scatter(const ScatterArgs &a, hipStream_t stream, const RopeParams *rope = nullptr);
 
 // Full-sequence attention.  q and out are [B, S, H * D] (S queries per batch
 // element).  With cached == 0, k and v are [B, S, H * D] too (prefill from an
@@ -64,6 +67,8 @@ struct DecodeArgs {
 int32_t decode_max_splits(int32_t max_len);
 // Bytes of workspace for (M, H, D, max_len); 0 if it overflows.
 size_t decode_workspace_bytes(int64_t M, int64_t H, int64_t D, int64_t max_len);
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// With rope (rotary_ndims > 0) each sequence's query is rotated to position
+// lens[m] - 1 (the newest cached token's) before scoring.
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopeParams *rope = nullptr);
 
 }  // namespace attn
