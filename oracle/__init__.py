@@ -18,6 +18,8 @@ and follows the definitions cited there:
 * scatter -- trueno-gpu ``kv_cache_scatter_gpu``;
 * chunked prefill behind a cache -- trustformers-core ``attention_prefill_gpu_to_gpu``
   (the offset mask its nothing-cached mask leaves to other paths);
+* copy of a prefilled cache into a batch slot -- realizar
+  ``scatter_single_kv_to_batched``;
 * rotary position embedding -- trustformers-core ``rope_neox_gpu_to_gpu`` /
   ``rope_reference``; realizar ``apply_rope_to_buffer``.
 
@@ -64,6 +66,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_prefill_cached_rows.argtypes = [p, p, p, p, p, p, p, i64, p, i64, i64, i64, i64, i64, i64,
                                                ctypes.c_float]
     lib.oracle_prefill_cached_rows.restype = ctypes.c_int
+    lib.oracle_copy_to_slot.argtypes = [p, p, i64, i64, p, p, i64, i64, i64, i64, i64]
+    lib.oracle_copy_to_slot.restype = ctypes.c_int
     lib.oracle_rope.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_double]
     lib.oracle_rope.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
@@ -193,6 +197,18 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_prefill_cached_rows rejected its arguments")
         return out
+
+    def copy_to_slot(self, src_k, src_v, src_max_len, seq_len, dst_k, dst_v, slot, M, Hkv, d, max_len):
+        """In-place copy of a single cache [Hkv, src_max_len, d] into slot `slot` of [M, Hkv, max_len, d]."""
+        src_k, src_v = _f32(src_k), _f32(src_v)
+        if not (dst_k.flags.c_contiguous and dst_v.flags.c_contiguous):
+            raise ValueError("caches must be C-contiguous (updated in place)")
+        assert src_k.size == Hkv * src_max_len * d and dst_k.size == M * Hkv * max_len * d
+        rc = self.lib.oracle_copy_to_slot(_ptr(src_k), _ptr(src_v), src_max_len, seq_len, _ptr(_f32(dst_k)),
+                                          _ptr(_f32(dst_v)), slot, M, Hkv, d, max_len)
+        if rc != 0:
+            raise ValueError("oracle_copy_to_slot rejected its arguments")
+        return dst_k, dst_v
 
     def rope(self, x, pos, H, d, rotary_ndims, base):
         """NeoX half-split partial RoPE of rows [n, H*d] at positions pos[n]; returns f64 [n, H*d]."""

@@ -103,3 +103,14 @@ def rope(x, pos, H, d, rotary_ndims, base):
     x[:, :, :half] = z.real
     x[:, :, half:2 * half] = z.imag
     return x.reshape(len(pos), H * d)
+
+
+def copy_to_slot(src_k, src_v, src_max_len, seq_len, dst_k, dst_v, slot, M, Hkv, d, max_len):
+    """Slice assignment on uint32 views; returns new arrays."""
+    out = []
+    for src, dst in ((src_k, dst_k), (src_v, dst_v)):
+        b = np.array(dst, dtype=np.float32, copy=True).reshape(M, Hkv, max_len, d).view(np.uint32)
+        a = np.asarray(src, dtype=np.float32).reshape(Hkv, src_max_len, d).view(np.uint32)
+        b[slot, :, :seq_len, :] = a[:, :seq_len, :]
+        out.append(b.view(np.float32))
+    return tuple(out)

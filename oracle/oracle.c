@@ -226,6 +226,38 @@ int oracle_scatter(const float *k_new, const float *v_new, float *k_cache,
     return 0;
 }
 
+/* Copy of a prefilled single-sequence cache into slot `slot` of the batched
+ * cache (realizar 0.8.5 ..., `scatter_single_kv_to_batched`: once a prefill has
+ * filled the single cache, its rows go to the batched cache at the slot's
+ * offset slot * Hkv * max_len * d and the slot's length becomes seq_len; a
+ * seq_len of 0 changes nothing).  The single cache is [Hkv, src_max_len, d]
+ * (`init_kv_cache_gpu`), the batched one [M, Hkv, max_len, d]
+ * (`init_batched_kv_cache_gpu`).  For every KV head kh, rows 0 .. seq_len-1 of
+ * head kh are copied bit for bit to rows 0 .. seq_len-1 of head kh of the slot,
+ * so that decoding the slot sees exactly what decoding the single cache saw.
+ * Returns -1 (nothing written) on invalid sizes. */
+int oracle_copy_to_slot(const float *src_k, const float *src_v, int64_t src_max_len,
+                        int64_t seq_len, float *dst_k, float *dst_v, int64_t slot, int64_t M,
+                        int64_t Hkv, int64_t d, int64_t max_len)
+{
+    int64_t kh, r, l;
+    if (M <= 0 || Hkv <= 0 || d <= 0 || max_len <= 0 || src_max_len <= 0) return -1;
+    if (slot < 0 || slot >= M || seq_len < 0 || seq_len > src_max_len || seq_len > max_len) return -1;
+    for (kh = 0; kh < Hkv; ++kh)
+        for (r = 0; r < seq_len; ++r) {
+            int64_t s = (kh * src_max_len + r) * d;
+            int64_t t = ((slot * Hkv + kh) * max_len + r) * d;
+            for (l = 0; l < d; ++l) {
+                uint32_t bits;
+                memcpy(&bits, &src_k[s + l], 4);
+                memcpy(&dst_k[t + l], &bits, 4);
+                memcpy(&bits, &src_v[s + l], 4);
+                memcpy(&dst_v[t + l], &bits, 4);
+            }
+        }
+    return 0;
+}
+
 /* Chunked prefill behind an existing cache (the offset causal mask:
  * trustformers-core 0.2.0 ..., `attention_prefill_gpu_to_gpu` leaves a prefill
  * that follows cached tokens to the per-token decode path; this is that case in

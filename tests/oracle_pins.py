@@ -510,6 +510,99 @@ def pin_scatter_rejects_overflow(orc):
     assert not kc.any() and not vc.any()
 
 
+# --------------------------------------------------------------------------- slot copy
+#
+# realizar 0.8.5 ...cache_from_kv_cache.rs, ``scatter_single_kv_to_batched``:
+# a prefilled single cache goes to batch slot k at offset k * stride.
+
+
+def pin_slot_copy_golden_offsets(orc):
+    """A row copied into a slot lands at the slot / head / position offsets of tests/golden/kv_cache_layout.json."""
+    g = json.load(open(os.path.join(GOLDEN, "kv_cache_layout.json")))
+    for c in g["cases"]:
+        Hkv, max_len, d, slot, head, pos = (c[x] for x in ("num_kv_heads", "max_len", "head_dim", "slot", "head", "pos"))
+        M = slot + 1
+        src = np.zeros((Hkv, max_len, d), np.float32)
+        marker = np.arange(1, d + 1, dtype=np.float32)
+        src[head, pos] = marker
+        kc = np.zeros((M, Hkv, max_len, d), np.float32)
+        vc = kc.copy()
+        orc.copy_to_slot(src, src, max_len, pos + 1, kc, vc, slot, M, Hkv, d, max_len)
+        flat = kc.reshape(-1)
+        assert np.array_equal(flat[c["offset"]:c["offset"] + d], marker), f"case {c}"
+        assert np.count_nonzero(flat) == d
+
+
+def pin_slot_copy_then_decode_equals_single(orc):
+    """Decoding the slot after the copy gives exactly what decoding the single cache gave.
+
+    The single cache has its own max_len (20) and only 13 live rows of 3 KV
+    heads; a copy of Hkv * seq_len * d consecutive floats from the start of the
+    single cache (one block, as the page's D2D copy is written) would move head
+    0's rows 13..38 instead of heads 1 and 2: that reading fails here.
+    """
+    r = _rng("slotdecode")
+    Hkv, H, d, src_max, seq_len, M, max_len, slot = 3, 6, 4, 20, 13, 4, 16, 2
+    sk = r.standard_normal((Hkv, src_max, d)).astype(np.float32)
+    sv = r.standard_normal((Hkv, src_max, d)).astype(np.float32)
+    kc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    vc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    orc.copy_to_slot(sk, sv, src_max, seq_len, kc, vc, slot, M, Hkv, d, max_len)
+    q = r.standard_normal((M, H * d)).astype(np.float32)
+    lens = np.array([16, 5, seq_len, 0], np.int32)
+    got = orc.decode(q, kc, vc, lens, M, H, Hkv, d, max_len, _scale(d))[slot]
+    want = orc.decode(q[slot:slot + 1], sk, sv, np.array([seq_len], np.int32), 1, H, Hkv, d, src_max, _scale(d))[0]
+    assert np.array_equal(got, want), "slot decode differs from the single-cache decode"
+
+
+def pin_slot_copy_touches_only_the_slot_prefix(orc):
+    """Exactly Hkv * seq_len * d elements change: rows >= seq_len and other slots keep their bytes."""
+    r = _rng("slotuntouched")
+    for Hkv, d, src_max, seq_len, M, max_len, slot in [(2, 8, 10, 7, 3, 12, 1), (1, 4, 5, 5, 1, 5, 0),
+                                                        (4, 2, 30, 1, 5, 3, 4)]:
+        sk = r.standard_normal((Hkv, src_max, d)).astype(np.float32)
+        sent = np.full((M, Hkv, max_len, d), 0x7FC0DEAD, np.uint32).view(np.float32)
+        kc, vc = sent.copy(), sent.copy()
+        orc.copy_to_slot(sk, sk, src_max, seq_len, kc, vc, slot, M, Hkv, d, max_len)
+        changed = kc.view(np.uint32) != 0x7FC0DEAD
+        assert np.count_nonzero(changed) == Hkv * seq_len * d
+        assert changed[slot, :, :seq_len].all()
+        assert np.array_equal(kc.view(np.uint32), vc.view(np.uint32))
+
+
+def pin_slot_copy_brute(orc):
+    """Bit-exact agreement with numpy slice assignment (NaN payloads kept), and seq_len 0 is a no-op."""
+    r = _rng("slotbrute")
+    for Hkv, d, src_max, seq_len, M, max_len, slot in [(3, 4, 9, 6, 2, 7, 0), (2, 8, 4, 4, 6, 9, 5),
+                                                        (5, 2, 12, 0, 3, 12, 2), (1, 1, 1, 1, 1, 1, 0)]:
+        sk = r.standard_normal((Hkv, src_max, d)).astype(np.float32)
+        sv = r.standard_normal((Hkv, src_max, d)).astype(np.float32)
+        sk.view(np.uint32).reshape(-1)[0] = 0x7FA00001
+        kc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+        vc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+        bk, bv = brute.copy_to_slot(sk, sv, src_max, seq_len, kc, vc, slot, M, Hkv, d, max_len)
+        k0, v0 = kc.copy(), vc.copy()
+        orc.copy_to_slot(sk, sv, src_max, seq_len, kc, vc, slot, M, Hkv, d, max_len)
+        assert np.array_equal(kc.view(np.uint32), bk.reshape(kc.shape).view(np.uint32))
+        assert np.array_equal(vc.view(np.uint32), bv.reshape(vc.shape).view(np.uint32))
+        if seq_len == 0:
+            assert np.array_equal(kc.view(np.uint32), k0.view(np.uint32))
+
+
+def pin_slot_copy_rejects(orc):
+    """A slot outside the batch or more rows than either cache holds is refused, caches untouched."""
+    sk = np.ones((2, 4, 2), np.float32)
+    for seq_len, slot, M, max_len in ((5, 0, 1, 8), (4, 0, 1, 3), (1, 1, 1, 4), (1, -1, 2, 4), (-1, 0, 1, 4)):
+        kc = np.zeros((M, 2, max_len, 2), np.float32)
+        vc = kc.copy()
+        try:
+            orc.copy_to_slot(sk, sk, 4, seq_len, kc, vc, slot, M, 2, 2, max_len)
+        except ValueError:
+            assert not kc.any() and not vc.any()
+            continue
+        raise AssertionError(f"seq_len {seq_len} slot {slot} M {M} max_len {max_len} accepted")
+
+
 # --------------------------------------------------------------------------- rope
 #
 # GPT-NeoX half-split partial rotary embedding: trustformers-core 0.2.0

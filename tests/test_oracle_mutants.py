@@ -52,6 +52,13 @@ MUTANTS = [
     ("cached_rows_offset_dropped", "        n = P + r + 1; /* keys visible to this query */",
      "        n = r + 1; /* keys visible to this query */"),
     ("cached_modulo_head_map", "kh = h / (H / Hkv), r, j, l;", "kh = h % Hkv, r, j, l;"),
+    ("slot_copy_one_block", "            int64_t s = (kh * src_max_len + r) * d;\n            int64_t t = ((slot * Hkv + kh) * max_len + r) * d;",
+     "            int64_t s = (kh * seq_len + r) * d;\n            int64_t t = (slot * Hkv * max_len + kh * seq_len + r) * d;"),
+    ("slot_copy_stride_uses_src_len", "int64_t t = ((slot * Hkv + kh) * max_len + r) * d;",
+     "int64_t t = ((slot * Hkv + kh) * src_max_len + r) * d;"),
+    ("slot_copy_one_row_short", "        for (r = 0; r < seq_len; ++r) {\n            int64_t s",
+     "        for (r = 0; r + 1 < seq_len; ++r) {\n            int64_t s"),
+    ("slot_copy_v_from_k", "memcpy(&bits, &src_v[s + l], 4);", "memcpy(&bits, &src_k[s + l], 4);"),
     ("rope_sign_flip", "yr[i] = x1 * c - x2 * sn;", "yr[i] = x1 * c + x2 * sn;"),
     ("rope_sin_cos_swapped", "yr[i + half] = x1 * sn + x2 * c;", "yr[i + half] = x1 * c + x2 * sn;"),
     ("rope_exponent_uses_head_dim", "-2.0 * (double)i / (double)rotary_ndims", "-2.0 * (double)i / (double)d"),
