@@ -316,6 +316,21 @@ def main():
         log(f"rope: bulk append {r_bulk * 1e3:.1f} us ({r_blk_gbs:.0f} GB/s), append {r_app * 1e3:.1f} us, "
             f"decode {r_dec * 1e3:.1f} us ({r_dec_gbs:.0f} GB/s)")
 
+        # Slot copy: a single-sequence cache holding a 2048-token prefill (the
+        # bulk-append cache's slot 0) copied into slot 3 of the same batched shape.
+        sk, sv = bk[0], bv[0]
+        dk, dv = torch.empty_like(bk), torch.empty_like(bv)
+        s_ms = time_call(torch, lambda: taf.kv_cache_copy_to_slot(sk, sv, scfg.max_len, scfg.n_new, dk, dv, 3,
+                                                                  scfg.M, scfg.Hkv, scfg.d, scfg.max_len), fill)
+        s_bytes = 2 * 2 * scfg.Hkv * scfg.n_new * scfg.d * 4
+        s_gbs = s_bytes / (s_ms * 1e-3) / 1e9
+        result["next_rows"]["slot_copy"] = {
+            "workload": f"copy of {scfg.n_new} rows x {scfg.Hkv} KV heads x d {scfg.d} (K and V) into slot 3",
+            "us": round(s_ms * 1e3, 2), "gbs": round(s_gbs, 2), "frac_hbm": round(s_gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": s_bytes}
+        log(f"slot copy: {s_ms * 1e3:.1f} us ({s_gbs:.0f} GB/s)")
+        del dk, dv
+
     # Free the GPU copies before the host-side leg.
     del pq, pk, pv, pout, bk, bv, dq, dkn, dvn, dkc, dvc, dout, ws
     torch.cuda.empty_cache()

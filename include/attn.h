@@ -17,7 +17,9 @@
  *                            append, then attend with the causal mask offset
  *                            by each sequence's cached length.
  * The append and the decode also come with a rotary position embedding fused
- * in (kv_cache_scatter_rope, attn_decode_gqa_batched_rope).
+ * in (kv_cache_scatter_rope, attn_decode_gqa_batched_rope); a prefilled
+ * single-sequence cache can be copied into a batch slot
+ * (kv_cache_copy_to_slot), and the host length arrays reset or rolled back.
  *
  * Conventions shared by every entry point
  *   - Tensors are f32, row-major, contiguous, in DEVICE memory owned by the
@@ -51,6 +53,12 @@
 
 #ifdef __cplusplus
 extern "C" {
+#endif
+
+/* The library is built with hidden symbol visibility; exactly the functions
+ * declared here are exported. */
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility push(default)
 #endif
 
 typedef enum {
@@ -199,6 +207,52 @@ int kv_cache_scatter(const float *k_new, const float *v_new, float *k_cache, flo
                      int32_t num_kv_heads, int32_t head_dim, int32_t max_len, void *stream);
 
 /*
+ * Copy a prefilled single-sequence cache into one slot of the batched cache.
+ *
+ * Defines: realizar `scatter_single_kv_to_batched` (after a prefill fills the
+ * single cache of `init_kv_cache_gpu`, its rows go to the batched cache of
+ * `init_batched_kv_cache_gpu` at offset slot * num_kv_heads * max_len *
+ * head_dim, the slot's length becomes seq_len, and seq_len 0 does nothing).
+ * The copy is per KV head: rows 0 .. seq_len-1 of head kh of the single cache
+ * go to rows 0 .. seq_len-1 of head kh of the slot, bit for bit, so a decode of
+ * the slot sees what a decode of the single cache saw.  (The page writes one
+ * contiguous copy of num_kv_heads * seq_len * head_dim floats, which is the
+ * same thing only when num_kv_heads == 1 or seq_len == max_len.)  One layer
+ * per call; other rows and slots are untouched.
+ *
+ *   src_k, src_v      [num_kv_heads, src_max_len, head_dim]      read, rows < seq_len
+ *   k_cache, v_cache  [num_seqs, num_kv_heads, max_len, head_dim]  slot's rows < seq_len written
+ *   slot_lens         HOST [num_seqs] int32 or NULL; on success slot_lens[slot] = seq_len
+ *
+ * Errors: NULL cache or source pointer; num_seqs not in [1, 32], slot outside
+ * [0, num_seqs), num_kv_heads/max_len/src_max_len <= 0, seq_len < 0 or larger
+ * than src_max_len or max_len (INVALID_DIM); head_dim not in {32, 64, 128} or a
+ * misaligned pointer (UNSUPPORTED); an element count >= 2^40 (OVERFLOW); a cache
+ * overlapping a source or the other cache (ALIAS).  One launch (none for
+ * seq_len 0).
+ */
+int kv_cache_copy_to_slot(const float *src_k, const float *src_v, int32_t src_max_len,
+                          int32_t seq_len, float *k_cache, float *v_cache, int32_t slot,
+                          int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t max_len, int32_t *slot_lens, void *stream);
+
+/*
+ * Host bookkeeping of the per-sequence lengths (caller-owned HOST arrays of
+ * num_seqs int32, the lengths every other entry point takes).  No HIP call.
+ *   kv_lengths_reset     every length becomes 0 (realizar
+ *                        `reset_batched_kv_cache_gpu`, `reset_kv_cache_gpu`:
+ *                        a new generation; cache contents are left as they are
+ *                        and are never read past a length).
+ *   kv_lengths_rollback  every length above `position` becomes `position`
+ *                        (realizar `rollback_kv_cache_gpu`: drop speculative
+ *                        tokens, keep rows 0 .. position-1); shorter lengths stay.
+ * Errors: lens NULL (NULL); num_seqs not in [1, 32] or position < 0
+ * (INVALID_DIM), with lens untouched.
+ */
+int kv_lengths_reset(int32_t *lens, int32_t num_seqs);
+int kv_lengths_rollback(int32_t *lens, int32_t num_seqs, int32_t position);
+
+/*
  * Rotary position embedding (used by the *_rope entry points).
  *
  * Defines: trustformers-core `rope_neox_gpu_to_gpu` (GPT-NeoX half-split
@@ -249,6 +303,10 @@ int attn_decode_gqa_batched_rope(const float *q, const float *k_cache, const flo
 
 /* Static, NUL-terminated description of a status code. */
 const char *attn_status_string(int status);
+
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility pop
+#endif
 
 #ifdef __cplusplus
 }

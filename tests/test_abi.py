@@ -38,7 +38,8 @@ def lib():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "attn_prefill", "attn_prefill_cached", "attn_decode_workspace_bytes", "attn_decode_gqa_batched",
-        "kv_cache_scatter", "attn_status_string", "kv_cache_scatter_rope", "attn_decode_gqa_batched_rope"])
+        "kv_cache_scatter", "attn_status_string", "kv_cache_scatter_rope", "attn_decode_gqa_batched_rope",
+        "kv_cache_copy_to_slot", "kv_lengths_reset", "kv_lengths_rollback"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -48,6 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
+    assert exported == set(declared_functions()), f"undeclared exports: {sorted(exported - set(declared_functions()))}"
 
 
 def test_status_strings(lib):
@@ -208,6 +210,51 @@ def test_decode_rope_validation(lib):
     assert call(theta=float("nan")) == DIM
     assert call(rot=4) == UNSUP
     assert call(rot=100) == UNSUP
+
+
+def test_copy_to_slot_validation(lib):
+    def call(sk=A, sv=B_, src_max=64, seq_len=10, kc=C_, vc=O_, slot=1, M=2, Hkv=4, d=64, max_len=32, lens=None):
+        return lib.kv_cache_copy_to_slot(sk, sv, src_max, seq_len, kc, vc, slot, M, Hkv, d, max_len, lens, None)
+    assert call(sk=0) == NULL
+    assert call(vc=0) == NULL
+    assert call(M=0) == DIM
+    assert call(M=33, slot=0) == DIM
+    assert call(slot=2) == DIM
+    assert call(slot=-1) == DIM
+    assert call(seq_len=33) == DIM             # more rows than the batched cache holds
+    assert call(src_max=8) == DIM              # more rows than the single cache holds
+    assert call(seq_len=-1) == DIM
+    assert call(Hkv=0) == DIM
+    assert call(d=80) == UNSUP
+    assert call(kc=C_ + 8) == UNSUP
+    assert call(Hkv=2**12, max_len=2**20, d=128, M=32, seq_len=1, src_max=1) == OVF
+    assert call(vc=C_ + 64) == ALIAS           # caches overlap
+    assert call(kc=A) == ALIAS                 # cache over the source
+    lens = (ctypes.c_int32 * 2)(7, 7)
+    assert call(slot=5, lens=lens) == DIM and list(lens) == [7, 7]
+
+
+def test_lengths_reset_and_rollback(lib):
+    """realizar reset_batched_kv_cache_gpu (all lengths 0) and rollback_kv_cache_gpu (lengths above
+    `position` drop to it, shorter ones stay), on the host arrays the other entry points take."""
+    lens = (ctypes.c_int32 * 5)(10, 3, 0, 7, 4096)
+    assert lib.kv_lengths_rollback(lens, 5, 7) == OK
+    assert list(lens) == [7, 3, 0, 7, 7]
+    assert lib.kv_lengths_rollback(lens, 5, 0) == OK
+    assert list(lens) == [0, 0, 0, 0, 0]
+    lens = (ctypes.c_int32 * 3)(5, 6, 7)
+    assert lib.kv_lengths_rollback(lens, 3, -1) == DIM and list(lens) == [5, 6, 7]
+    assert lib.kv_lengths_rollback(lens, 0, 1) == DIM
+    assert lib.kv_lengths_rollback(None, 3, 1) == NULL
+    assert lib.kv_lengths_reset(lens, 3) == OK and list(lens) == [0, 0, 0]
+    assert lib.kv_lengths_reset(lens, 33) == DIM
+    assert lib.kv_lengths_reset(None, 1) == NULL
+    # The Python binding updates a list in place.
+    py = [9, 2, 11]
+    taf.kv_lengths_rollback(py, 3, 4)
+    assert py == [4, 2, 4]
+    taf.kv_lengths_reset(py, 3)
+    assert py == [0, 0, 0]
 
 
 def test_python_binding_rejects_cpu_tensors():

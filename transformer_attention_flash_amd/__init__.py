@@ -27,6 +27,9 @@ __all__ = [
     "kv_cache_scatter",
     "kv_cache_scatter_rope",
     "attn_decode_gqa_batched_rope",
+    "kv_cache_copy_to_slot",
+    "kv_lengths_reset",
+    "kv_lengths_rollback",
     "attn_status_string",
     "library",
     "library_path",
@@ -79,6 +82,12 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_gqa_batched_rope.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, i32, f32, p,
                                                      sz, p]
         lib.attn_decode_gqa_batched_rope.restype = ctypes.c_int
+        lib.kv_cache_copy_to_slot.argtypes = [p, p, i32, i32, p, p, i32, i32, i32, i32, i32, p, p]
+        lib.kv_cache_copy_to_slot.restype = ctypes.c_int
+        lib.kv_lengths_reset.argtypes = [p, i32]
+        lib.kv_lengths_reset.restype = ctypes.c_int
+        lib.kv_lengths_rollback.argtypes = [p, i32, i32]
+        lib.kv_lengths_rollback.restype = ctypes.c_int
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -234,3 +243,41 @@ def kv_cache_scatter_rope(k_new, v_new, k_cache, v_cache, cache_lens: Sequence[i
     _call("kv_cache_scatter_rope",
           library().kv_cache_scatter_rope(*ptrs, lens, num_seqs, n_new, num_kv_heads, head_dim, max_len,
                                           rotary_ndims, rope_theta, _stream_ptr(dev, stream)))
+
+
+def kv_cache_copy_to_slot(src_k, src_v, src_max_len: int, seq_len: int, k_cache, v_cache, slot: int,
+                          num_seqs: int, num_kv_heads: int, head_dim: int, max_len: int, slot_lens=None,
+                          stream=None) -> None:
+    """Rows 0..seq_len-1 of each KV head of a single cache go to batch slot `slot`.
+
+    ``slot_lens``, if given, is a mutable host sequence of num_seqs lengths whose
+    entry ``slot`` is set to seq_len on success.
+    """
+    dev = k_cache.device
+    sn = num_kv_heads * src_max_len * head_dim
+    cn = num_seqs * num_kv_heads * max_len * head_dim
+    ptrs = [_check_tensor("src_k", src_k, sn, dev), _check_tensor("src_v", src_v, sn, dev)]
+    cptrs = [_check_tensor("k_cache", k_cache, cn, dev), _check_tensor("v_cache", v_cache, cn, dev)]
+    lens = _host_ints("slot_lens", slot_lens, num_seqs) if slot_lens is not None else None
+    _call("kv_cache_copy_to_slot",
+          library().kv_cache_copy_to_slot(*ptrs, src_max_len, seq_len, *cptrs, slot, num_seqs, num_kv_heads,
+                                          head_dim, max_len, lens, _stream_ptr(dev, stream)))
+    if lens is not None:
+        slot_lens[slot] = lens[slot]
+
+
+def _lengths_call(name, lens, num_seqs, *extra):
+    arr = _host_ints("lens", lens, num_seqs)
+    _call(name, getattr(library(), name)(arr, num_seqs, *extra))
+    for m in range(num_seqs):
+        lens[m] = arr[m]
+
+
+def kv_lengths_reset(lens, num_seqs: int) -> None:
+    """Every length of the mutable host sequence ``lens`` becomes 0."""
+    _lengths_call("kv_lengths_reset", lens, num_seqs)
+
+
+def kv_lengths_rollback(lens, num_seqs: int, position: int) -> None:
+    """Every length of ``lens`` above ``position`` becomes ``position``."""
+    _lengths_call("kv_lengths_rollback", lens, num_seqs, position)

@@ -20,7 +20,7 @@ ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept out of the generated code on purpose; the
 # host pass warns that it does not know the feature, which is harmless.
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]

@@ -298,4 +298,44 @@ int kv_cache_scatter_rope(const float *k_new, const float *v_new, float *k_cache
     return from_hip(attn::launch_kv_scatter(a, static_cast<hipStream_t>(stream), &rp));
 }
 
+int kv_cache_copy_to_slot(const float *src_k, const float *src_v, int32_t src_max_len, int32_t seq_len,
+                          float *k_cache, float *v_cache, int32_t slot, int32_t num_seqs, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t max_len, int32_t *slot_lens, void *stream) {
+    if (!src_k || !src_v || !k_cache || !v_cache) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS || slot < 0 || slot >= num_seqs) return ATTN_ERR_INVALID_DIM;
+    if (num_kv_heads <= 0 || head_dim <= 0 || max_len <= 0 || src_max_len <= 0) return ATTN_ERR_INVALID_DIM;
+    if (seq_len < 0 || seq_len > src_max_len || seq_len > max_len) return ATTN_ERR_INVALID_DIM;
+    if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return ATTN_ERR_UNSUPPORTED;
+    int64_t src_elems, cache_elems, per_head;
+    if (!checked_mul({num_kv_heads, src_max_len, head_dim}, kMaxElems, &src_elems) ||
+        !checked_mul({num_seqs, num_kv_heads, max_len, head_dim}, kMaxElems, &cache_elems) ||
+        !checked_mul({seq_len, head_dim}, kMaxElems32, &per_head))
+        return ATTN_ERR_OVERFLOW;
+    const int64_t sb = src_elems * 4, cb = cache_elems * 4;
+    if (overlaps(k_cache, cb, v_cache, cb) || overlaps(k_cache, cb, src_k, sb) || overlaps(k_cache, cb, src_v, sb) ||
+        overlaps(v_cache, cb, src_k, sb) || overlaps(v_cache, cb, src_v, sb))
+        return ATTN_ERR_ALIAS;
+    attn::SlotCopyArgs a{src_k, src_v, k_cache, v_cache, src_max_len, seq_len, slot, num_kv_heads, head_dim, max_len};
+    const int st = from_hip(attn::launch_slot_copy(a, static_cast<hipStream_t>(stream)));
+    if (st == ATTN_OK && slot_lens) slot_lens[slot] = seq_len;
+    return st;
+}
+
+int kv_lengths_reset(int32_t *lens, int32_t num_seqs) {
+    if (!lens) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS) return ATTN_ERR_INVALID_DIM;
+    for (int32_t m = 0; m < num_seqs; ++m) lens[m] = 0;
+    return ATTN_OK;
+}
+
+int kv_lengths_rollback(int32_t *lens, int32_t num_seqs, int32_t position) {
+    if (!lens) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS || position < 0) return ATTN_ERR_INVALID_DIM;
+    for (int32_t m = 0; m < num_seqs; ++m)
+        if (lens[m] > position) lens[m] = position;
+    return ATTN_OK;
+}
+
 }  // extern "C"

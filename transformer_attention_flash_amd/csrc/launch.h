@@ -29,6 +29,17 @@ struct ScatterArgs {
 // With rope (rotary_ndims > 0) the keys are rotated to their cache positions.
 hipError_t launch_kv_scatter(const ScatterArgs &a, hipStream_t stream, const RopeParams *rope = nullptr);
 
+// Copy of rows 0 .. seq_len-1 of every KV head of a single cache
+// [Hkv, src_max_len, D] into slot `slot` of the batched cache [M, Hkv, max_len, D].
+struct SlotCopyArgs {
+    const float *src_k;
+    const float *src_v;
+    float *k_cache;
+    float *v_cache;
+    int32_t src_max_len, seq_len, slot, Hkv, D, max_len;
+};
+hipError_t launch_slot_copy(const SlotCopyArgs &a, hipStream_t stream);
+
 // Full-sequence attention.  q and out are [B, S, H * D] (S queries per batch
 // element).  With cached == 0, k and v are [B, S, H * D] too (prefill from an
 // empty cache).  With cached == 1, k and v are the caches [B, Hkv, max_len, D]:

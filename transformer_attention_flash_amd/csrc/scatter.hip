@@ -1,4 +1,4 @@
-// scatter.hip -- KV-cache append: copy rows of new keys and values from the
+// scatter.hip -- KV-cache writes.  The append copies rows of new keys and values from the
 // interleaved [M, n_new, Hkv * D] layout the projections produce into the
 // head-first batched cache [M, Hkv, max_len, D] at each sequence's position.
 //
@@ -7,6 +7,8 @@
 // cache[head, pos, :]), generalised to n_new rows and to the batched cache of
 // realizar 0.8.5 src/cuda/executor/cache_from_cache_from_kv_cache.rs,
 // `init_batched_kv_cache_gpu` (per-sequence stride Hkv * max_len * D).
+// The slot copy moves a prefilled single-sequence cache into one slot of the
+// batched cache (realizar, `scatter_single_kv_to_batched`), head by head.
 //
 // The copy is HBM-bound: each 16-byte vector is read once and written once.
 // Consecutive lanes take consecutive vectors of the source, so reads are fully
@@ -144,7 +146,57 @@ hipError_t launch_typed(const ScatterArgs &a, const RopeParams &rp, hipStream_t 
     return hipGetLastError();
 }
 
+// Slot copy: grid (vector blocks of one head, Hkv, 2 = K/V).  A head's live
+// rows are seq_len * D contiguous floats in both caches, so this is a straight
+// streaming copy per head at two different base offsets.
+#ifndef ATTN_SLOT_VEC
+#define ATTN_SLOT_VEC 4
+#endif
+#ifndef ATTN_SLOT_NT
+#define ATTN_SLOT_NT 1
+#endif
+constexpr int kSlotVec = ATTN_SLOT_VEC;
+
+__global__ __launch_bounds__(kThreads) void slot_copy_kernel(SlotCopyArgs a, uint32_t per_head_vec) {
+    const int kh = blockIdx.y;
+    const bool is_v = blockIdx.z;
+    const size_t q = (size_t)a.D / 4;
+    const f32x4 *__restrict__ src =
+        reinterpret_cast<const f32x4 *>(is_v ? a.src_v : a.src_k) + (size_t)kh * a.src_max_len * q;
+    f32x4 *__restrict__ dst = reinterpret_cast<f32x4 *>(is_v ? a.v_cache : a.k_cache) +
+                              ((size_t)a.slot * a.Hkv + kh) * a.max_len * q;
+    const uint32_t first = blockIdx.x * (kThreads * kSlotVec) + threadIdx.x;
+    f32x4 buf[kSlotVec];
+#pragma unroll
+    for (int u = 0; u < kSlotVec; ++u) {
+        const uint32_t i = first + u * kThreads;
+#if ATTN_SLOT_NT
+        if (i < per_head_vec) buf[u] = __builtin_nontemporal_load(src + i);
+#else
+        if (i < per_head_vec) buf[u] = src[i];
+#endif
+    }
+#pragma unroll
+    for (int u = 0; u < kSlotVec; ++u) {
+        const uint32_t i = first + u * kThreads;
+#if ATTN_SLOT_NT
+        if (i < per_head_vec) __builtin_nontemporal_store(buf[u], dst + i);
+#else
+        if (i < per_head_vec) dst[i] = buf[u];
+#endif
+    }
+}
+
 }  // namespace
+
+hipError_t launch_slot_copy(const SlotCopyArgs &a, hipStream_t stream) {
+    if (a.seq_len == 0) return hipSuccess;
+    const uint32_t per_head_vec = (uint32_t)((int64_t)a.seq_len * a.D / 4);
+    const uint32_t per_block = kThreads * kSlotVec;
+    dim3 grid((per_head_vec + per_block - 1) / per_block, a.Hkv, 2);
+    slot_copy_kernel<<<grid, dim3(kThreads), 0, stream>>>(a, per_head_vec);
+    return hipGetLastError();
+}
 
 hipError_t launch_kv_scatter(const ScatterArgs &a, hipStream_t stream, const RopeParams *rope) {
     if (rope && rope->rot > 0) return launch_typed<true>(a, *rope, stream);
