@@ -18,6 +18,8 @@ and follows the definitions cited there:
 * scatter -- trueno-gpu ``kv_cache_scatter_gpu``;
 * chunked prefill behind a cache -- trustformers-core ``attention_prefill_gpu_to_gpu``
   (the offset mask its nothing-cached mask leaves to other paths);
+* reduced-precision prefill -- trueno-gpu ``batched_gemm`` (fp16 tensor-core
+  operands): attention of the inputs rounded to binary16 / bfloat16;
 * copy of a prefilled cache into a batch slot -- realizar
   ``scatter_single_kv_to_batched``;
 * rotary position embedding -- trustformers-core ``rope_neox_gpu_to_gpu`` /
@@ -68,6 +70,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_prefill_cached_rows.restype = ctypes.c_int
     lib.oracle_copy_to_slot.argtypes = [p, p, i64, i64, p, p, i64, i64, i64, i64, i64]
     lib.oracle_copy_to_slot.restype = ctypes.c_int
+    lib.oracle_round16.argtypes = [p, p, i64, ctypes.c_int]
+    lib.oracle_round16.restype = ctypes.c_int
+    lib.oracle_prefill_lowp.argtypes = [p, p, p, p, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_int]
+    lib.oracle_prefill_lowp.restype = ctypes.c_int
     lib.oracle_rope.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_double]
     lib.oracle_rope.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
@@ -209,6 +215,26 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_copy_to_slot rejected its arguments")
         return dst_k, dst_v
+
+    FP16, BF16 = 1, 2
+
+    def round16(self, x, fmt):
+        """f32 values rounded (nearest, ties to even) to binary16 (fmt 1) or bfloat16 (fmt 2), as f32."""
+        x = _f32(x)
+        y = np.empty_like(x)
+        if self.lib.oracle_round16(_ptr(x), _ptr(y), x.size, int(fmt)) != 0:
+            raise ValueError("oracle_round16 rejected its arguments")
+        return y
+
+    def prefill_lowp(self, q, k, v, B, S, H, d, scale, causal, fmt):
+        """Attention (fp64) of q, k, v rounded to the 16-bit format fmt; [B, S, H*d]."""
+        q, k, v = _f32(q), _f32(k), _f32(v)
+        out = np.empty(B * S * H * d, dtype=np.float64)
+        rc = self.lib.oracle_prefill_lowp(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, S, H, d,
+                                          float(np.float32(scale)), 1 if causal else 0, int(fmt))
+        if rc != 0:
+            raise ValueError("oracle_prefill_lowp rejected its arguments")
+        return out.reshape(B, S, H * d)
 
     def rope(self, x, pos, H, d, rotary_ndims, base):
         """NeoX half-split partial RoPE of rows [n, H*d] at positions pos[n]; returns f64 [n, H*d]."""

@@ -399,6 +399,70 @@ int oracle_rope(const float *x, const int32_t *pos, double *out, int64_t n_rows,
     return 0;
 }
 
+/* Rounding of an f32 value to a 16-bit floating-point format, round to
+ * nearest, ties to even (IEEE 754 binary16, or bfloat16: the f32 exponent
+ * range with 8 significant bits).  The reduced-precision prefill (trueno-gpu
+ * 0.4.11 ..., `batched_gemm`: the GEMM operands go through fp16 tensor cores
+ * when k >= 64) computes attention of the inputs rounded this way.
+ * fmt 1 = binary16 (11 significant bits, normal exponents >= -14, largest
+ * finite 65504), fmt 2 = bfloat16 (8 bits, >= -126, largest (2 - 2^-7) 2^127).
+ * Written from the definition: find the spacing of representable numbers at
+ * x (the subnormal spacing below the smallest normal), round x / spacing to
+ * the nearest integer (ties to even: nearbyint in the default rounding mode),
+ * and overflow to infinity past the largest finite value. */
+static double round_sig(double x, int p, int emin, double maxv)
+{
+    int e;
+    double q, r;
+    if (x == 0.0 || !isfinite(x)) return x;
+    frexp(x, &e); /* |x| = m 2^e, 1/2 <= m < 1: leading bit at 2^(e-1) */
+    e -= 1;
+    if (e < emin) e = emin;
+    q = ldexp(1.0, e - (p - 1));
+    r = nearbyint(x / q) * q;
+    if (fabs(r) > maxv) return copysign(INFINITY, x);
+    return r;
+}
+
+int oracle_round16(const float *x, float *y, int64_t n, int fmt)
+{
+    int64_t i;
+    int p, emin;
+    double maxv;
+    if (fmt == 1) {
+        p = 11; emin = -14; maxv = 65504.0;
+    } else if (fmt == 2) {
+        p = 8; emin = -126; maxv = ldexp(2.0 - ldexp(1.0, -7), 127);
+    } else {
+        return -1;
+    }
+    for (i = 0; i < n; ++i) y[i] = (float)round_sig((double)x[i], p, emin, maxv);
+    return 0;
+}
+
+/* Reduced-precision prefill: oracle_prefill of q, k and v each rounded to the
+ * 16-bit format `fmt` (the products of 16-bit operands are exact in the
+ * wider accumulation; what the device's own rounding of the probabilities adds
+ * is bounded in the tests, not modelled here). */
+int oracle_prefill_lowp(const float *q, const float *k, const float *v, double *out, int64_t B,
+                        int64_t S, int64_t H, int64_t d, float scale, int causal, int fmt)
+{
+    int64_t n = B * S * H * d;
+    float *rq, *rk, *rv;
+    int rc = -1;
+    if (n <= 0) return -1;
+    rq = (float *)malloc((size_t)n * sizeof(float));
+    rk = (float *)malloc((size_t)n * sizeof(float));
+    rv = (float *)malloc((size_t)n * sizeof(float));
+    if (rq && rk && rv && oracle_round16(q, rq, n, fmt) == 0 && oracle_round16(k, rk, n, fmt) == 0 &&
+        oracle_round16(v, rv, n, fmt) == 0)
+        rc = oracle_prefill(rq, rk, rv, out, B, S, H, d, scale, causal);
+    free(rq);
+    free(rk);
+    free(rv);
+    return rc;
+}
+
 /* Number of OpenMP threads a parallel region would use (for reporting). */
 int oracle_num_threads(void)
 {

@@ -510,6 +510,97 @@ def pin_scatter_rejects_overflow(orc):
     assert not kc.any() and not vc.any()
 
 
+# --------------------------------------------------------------------------- reduced precision
+#
+# trueno-gpu 0.4.11 ..., ``batched_gemm``: for k >= 64 the attention GEMMs run on
+# fp16 tensor-core operands.  Reading: the reduced-precision prefill is the
+# attention of the inputs rounded (nearest, ties to even) to the 16-bit format.
+
+
+def _bf16_by_bits(x):
+    """bfloat16 rounding by integer arithmetic on the f32 bit pattern (finite inputs)."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return r.astype(np.uint32).view(np.float32)
+
+
+def _rounding_samples():
+    r = _rng("round16")
+    parts = [r.standard_normal(20000) * s for s in (1e-6, 1e-3, 1.0, 30.0, 3e4)]
+    parts.append(r.uniform(-7e4, 7e4, 5000))
+    # Ties and near-ties at several binades, both formats' subnormals, overflow edges.
+    ties = []
+    for e in range(-30, 20):
+        base = 2.0 ** e
+        for m in range(1, 9):
+            ties += [base * (1 + m * 2.0 ** -11), base * (1 + (2 * m + 1) * 2.0 ** -12),
+                     base * (1 + (2 * m + 1) * 2.0 ** -9), base * (1 + m * 2.0 ** -8)]
+    parts.append(np.array(ties))
+    parts.append(np.array([0.0, -0.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14, 65504, 65519.99, 65520,
+                           -65520, 3.0e38, 3.4e38, 2.0 ** -126, 2.0 ** -133, 2.0 ** -134, 1e-40]))
+    x = np.concatenate(parts).astype(np.float32)
+    return np.concatenate([x, -x])
+
+
+def pin_round16_binary16_matches_numpy(orc):
+    """binary16 rounding equals numpy's float16 conversion (its own implementation), value by value."""
+    x = _rounding_samples()
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).astype(np.float32)
+    got = orc.round16(x, orc.FP16)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), \
+        f"{np.count_nonzero(got.view(np.uint32) != want.view(np.uint32))} values differ"
+
+
+def pin_round16_bfloat16_matches_bit_rounding(orc):
+    """bfloat16 rounding equals round-to-nearest-even on the f32 bit pattern (a second formulation)."""
+    x = _rounding_samples()
+    got = orc.round16(x, orc.BF16)
+    want = _bf16_by_bits(x)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), \
+        f"{np.count_nonzero(got.view(np.uint32) != want.view(np.uint32))} values differ"
+
+
+def pin_round16_hand_cases(orc):
+    """Ties go to even, subnormals keep their spacing, overflow goes to infinity, NaN stays NaN."""
+    cases = [
+        (orc.BF16, 1 + 2.0 ** -8, 1.0), (orc.BF16, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -6),
+        (orc.BF16, 1 + 2.0 ** -7, 1 + 2.0 ** -7), (orc.BF16, 2.0 ** -133, 2.0 ** -133),
+        (orc.BF16, 3.4e38, np.inf), (orc.BF16, -(2 - 2.0 ** -7) * 2.0 ** 127, -(2 - 2.0 ** -7) * 2.0 ** 127),
+        (orc.FP16, 1 + 2.0 ** -11, 1.0), (orc.FP16, 1 + 3 * 2.0 ** -11, 1 + 2.0 ** -9),
+        (orc.FP16, 65519.0, 65504.0), (orc.FP16, 65520.0, np.inf), (orc.FP16, -65520.0, -np.inf),
+        (orc.FP16, 2.0 ** -25, 0.0), (orc.FP16, 3 * 2.0 ** -26, 2.0 ** -24), (orc.FP16, 2.0 ** -24, 2.0 ** -24),
+        (orc.FP16, 0.1, 0.0999755859375), (orc.BF16, 0.1, 0.10009765625),
+    ]
+    for fmt, x, want in cases:
+        got = float(orc.round16(np.array([x], np.float32), fmt)[0])
+        assert got == np.float32(want), f"fmt {fmt}: {x!r} -> {got!r}, want {want!r}"
+    for fmt in (orc.FP16, orc.BF16):
+        assert np.isnan(orc.round16(np.array([np.nan], np.float32), fmt)[0])
+        x = _rounding_samples()
+        once = orc.round16(x, fmt)
+        with np.errstate(invalid="ignore"):
+            assert np.array_equal(orc.round16(once, fmt).view(np.uint32), once.view(np.uint32)), "not idempotent"
+
+
+def pin_prefill_lowp_is_prefill_of_rounded_inputs(orc):
+    """Exactly the plain attention of the rounded inputs (brute force on numpy-rounded fp16 inputs too),
+    and equal to plain attention when the inputs are already representable."""
+    r = _rng("lowp")
+    for B, S, H, d, causal in [(1, 7, 2, 8, True), (2, 5, 3, 4, False), (1, 9, 1, 16, True)]:
+        q, k, v = (r.standard_normal((B, S, H * d)).astype(np.float32) for _ in range(3))
+        for fmt in (orc.FP16, orc.BF16):
+            got = orc.prefill_lowp(q, k, v, B, S, H, d, _scale(d), causal, fmt)
+            rq, rk, rv = (orc.round16(x, fmt) for x in (q, k, v))
+            _close(got, orc.prefill(rq, rk, rv, B, S, H, d, _scale(d), causal), 0.0, f"lowp fmt {fmt}")
+        hq, hk, hv = (x.astype(np.float16).astype(np.float32) for x in (q, k, v))
+        _close(orc.prefill_lowp(q, k, v, B, S, H, d, _scale(d), causal, orc.FP16),
+               brute.prefill(hq, hk, hv, B, S, H, d, _scale(d), causal), 1e-12, "lowp fp16 brute")
+        g = (np.round(r.standard_normal((B, S, H * d)) * 8) / 8).astype(np.float32)  # exact in both formats
+        _close(orc.prefill_lowp(g, g, g, B, S, H, d, _scale(d), causal, orc.BF16),
+               orc.prefill(g, g, g, B, S, H, d, _scale(d), causal), 0.0, "representable inputs")
+
+
 # --------------------------------------------------------------------------- slot copy
 #
 # realizar 0.8.5 ...cache_from_kv_cache.rs, ``scatter_single_kv_to_batched``:

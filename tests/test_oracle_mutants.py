@@ -59,6 +59,13 @@ MUTANTS = [
     ("slot_copy_one_row_short", "        for (r = 0; r < seq_len; ++r) {\n            int64_t s",
      "        for (r = 0; r + 1 < seq_len; ++r) {\n            int64_t s"),
     ("slot_copy_v_from_k", "memcpy(&bits, &src_v[s + l], 4);", "memcpy(&bits, &src_k[s + l], 4);"),
+    ("round16_truncates", "r = nearbyint(x / q) * q;", "r = trunc(x / q) * q;"),
+    ("round16_ties_away", "r = nearbyint(x / q) * q;", "r = round(x / q) * q;"),
+    ("round16_bf16_seven_bits", "p = 8; emin = -126;", "p = 7; emin = -126;"),
+    ("round16_no_subnormal_floor", "    if (e < emin) e = emin;\n", ""),
+    ("round16_no_overflow", "if (fabs(r) > maxv) return copysign(INFINITY, x);", "(void)maxv;"),
+    ("lowp_v_not_rounded", "oracle_round16(v, rv, n, fmt) == 0)\n        rc = oracle_prefill(rq, rk, rv,",
+     "oracle_round16(v, rv, n, fmt) == 0)\n        rc = oracle_prefill(rq, rk, v,"),
     ("rope_sign_flip", "yr[i] = x1 * c - x2 * sn;", "yr[i] = x1 * c + x2 * sn;"),
     ("rope_sin_cos_swapped", "yr[i + half] = x1 * sn + x2 * c;", "yr[i + half] = x1 * c + x2 * sn;"),
     ("rope_exponent_uses_head_dim", "-2.0 * (double)i / (double)rotary_ndims", "-2.0 * (double)i / (double)d"),
