@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+LOWP_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
 FP32_MFMA_PEAK_TFLOPS = 157.3
 
 METRIC = "decode attn HBM GB/s (% peak) + prefill TFLOP/s (% fp32 MFMA peak), 1 GPU"
@@ -315,6 +316,19 @@ def main():
                     "not part of ms_per_step"}
         log(f"rope: bulk append {r_bulk * 1e3:.1f} us ({r_blk_gbs:.0f} GB/s), append {r_app * 1e3:.1f} us, "
             f"decode {r_dec * 1e3:.1f} us ({r_dec_gbs:.0f} GB/s)")
+
+        # Reduced-precision prefill: the step's causal prefill on 16-bit MFMA operands.
+        lowp = {}
+        for pname, prec in (("fp16", taf.ATTN_PREC_FP16), ("bf16", taf.ATTN_PREC_BF16)):
+            lp_ms = time_call(torch, lambda: taf.attn_prefill_lowp(pq, pk, pv, pout, pcfg.B, pcfg.S, pcfg.H, pcfg.d,
+                                                                   pcfg.scale, True, prec), fill)
+            lp_tf = pre_flops / (lp_ms * 1e-3) / 1e12
+            lowp[pname] = {"us": round(lp_ms * 1e3, 2), "tflops": round(lp_tf, 3),
+                           "frac_mfma": round(lp_tf / LOWP_MFMA_PEAK_TFLOPS, 4)}
+            log(f"prefill {pname}: {lp_ms * 1e3:.1f} us, {lp_tf:.1f} TFLOP/s")
+        result["next_rows"]["prefill_lowp"] = {
+            "workload": pcfg.name, "algorithmic_flops": pre_flops, "peak_tflops": LOWP_MFMA_PEAK_TFLOPS, **lowp,
+            "note": "f32 in and out, q/k/v and probabilities rounded to the 16-bit type for the MFMA operands"}
 
         # Slot copy: a single-sequence cache holding a 2048-token prefill (the
         # bulk-append cache's slot 0) copied into slot 3 of the same batched shape.

@@ -7,7 +7,8 @@
  * Four operations, each enqueued on a caller-supplied HIP stream:
  *   attn_prefill             full-sequence attention over interleaved
  *                            [batch, seq, n_heads * head_dim] activations,
- *                            optionally causal;
+ *                            optionally causal (attn_prefill_lowp: the same
+ *                            on 16-bit fp16 / bf16 matrix-core operands);
  *   attn_decode_gqa_batched  one query token per sequence for up to 32
  *                            sequences against a preallocated GQA KV cache,
  *                            each sequence with its own length;
@@ -37,7 +38,7 @@
  *   - Outputs must not overlap inputs (ATTN_ERR_ALIAS).
  *
  * Sources (page title, then section): trueno-gpu 0.4.11
- * src/memory/resident/attention.rs (`batched_multihead_attention`,
+ * src/memory/resident/attention.rs (`batched_multihead_attention`, `batched_gemm`,
  * `incremental_attention_gpu_with_stream`, `kv_cache_scatter_gpu`);
  * trustformers-core 0.2.0 src/gpu_ops/cuda/oxicuda/attention.rs
  * (`attention_prefill_gpu_to_gpu`, `attention_decode_gpu_to_gpu`,
@@ -72,6 +73,12 @@ typedef enum {
     ATTN_ERR_ALIAS = 7        /* an output buffer overlaps an input buffer */
 } attn_status;
 
+/* Operand formats of attn_prefill_lowp. */
+typedef enum {
+    ATTN_PREC_FP16 = 1, /* IEEE binary16: 11 significant bits, largest finite 65504 */
+    ATTN_PREC_BF16 = 2  /* bfloat16: 8 significant bits, the f32 exponent range */
+} attn_precision;
+
 /* Largest number of sequences a decode or scatter call takes (the batched
  * cache holds 1..32 sequences: realizar `init_batched_kv_cache_gpu`). */
 #define ATTN_MAX_SEQS 32
@@ -102,6 +109,28 @@ typedef enum {
 int attn_prefill(const float *q, const float *k, const float *v, float *out,
                  int32_t batch, int32_t seq_len, int32_t n_heads, int32_t head_dim,
                  float scale, int32_t causal, void *stream);
+
+/*
+ * Reduced-precision full-sequence attention: attn_prefill with both products
+ * on 16-bit matrix-core operands.
+ *
+ * Defines: trueno-gpu `batched_gemm`, which runs the attention GEMMs on fp16
+ * tensor-core operands once k >= 64 (WMMA, wider accumulation).  Here q, k and
+ * v are rounded to `precision` (nearest, ties to even) as they are read; the
+ * scores accumulate in f32 (the product of two 16-bit values is exact in f32);
+ * the softmax runs in f32; the probabilities are rounded to `precision` as the
+ * operand of the P.V product, which accumulates in f32; the running sums and
+ * the final normalisation use the f32 probabilities.  Inputs and output stay
+ * f32 in memory, with the layout, arguments and errors of attn_prefill.
+ *   precision  ATTN_PREC_FP16 or ATTN_PREC_BF16 (anything else: UNSUPPORTED)
+ * Accuracy: against the exact attention of the rounded inputs, an output
+ * element is off by at most about u * max|v| (u = 2^-11 for fp16, 2^-8 for
+ * bf16: the rounding of the probabilities) plus f32 rounding; inputs must fit
+ * the format (|x| <= 65504 for fp16, else they round to infinity).
+ */
+int attn_prefill_lowp(const float *q, const float *k, const float *v, float *out,
+                      int32_t batch, int32_t seq_len, int32_t n_heads, int32_t head_dim,
+                      float scale, int32_t causal, int32_t precision, void *stream);
 
 /*
  * Chunked prefill behind an existing KV cache: append the keys and values of a

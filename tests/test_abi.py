@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "attn_prefill", "attn_prefill_cached", "attn_decode_workspace_bytes", "attn_decode_gqa_batched",
         "kv_cache_scatter", "attn_status_string", "kv_cache_scatter_rope", "attn_decode_gqa_batched_rope",
-        "kv_cache_copy_to_slot", "kv_lengths_reset", "kv_lengths_rollback"])
+        "kv_cache_copy_to_slot", "kv_lengths_reset", "kv_lengths_rollback", "attn_prefill_lowp"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -77,6 +77,21 @@ def test_prefill_validation(lib):
     assert prefill(lib, b=64, s=65536, h=64, d=128) == OVF
     assert prefill(lib, out=A + 64) == ALIAS      # out starts inside q
     assert prefill(lib, out=C_ - 16) == ALIAS     # out runs into v
+
+
+def test_prefill_lowp_validation(lib):
+    def call(q=A, out=O_, b=1, s=64, h=4, d=32, scale=0.125, causal=0, prec=2):
+        return lib.attn_prefill_lowp(q, B_, C_, out, b, s, h, d, scale, causal, prec, None)
+    assert call(q=0) == NULL
+    assert call(b=0) == DIM
+    assert call(causal=3) == DIM
+    assert call(scale=float("nan")) == DIM
+    assert call(d=96) == UNSUP
+    assert call(prec=0) == UNSUP
+    assert call(prec=3) == UNSUP
+    assert call(q=A + 8) == UNSUP
+    assert call(b=64, s=65536, h=64, d=128) == OVF
+    assert call(out=A + 64) == ALIAS
 
 
 def decode(lib, q=A, k=B_, v=C_, lens=None, out=O_, M=2, H=8, Hkv=2, d=64, max_len=100, scale=0.125,

@@ -1,0 +1,122 @@
+"""Reduced-precision prefill (16-bit MFMA operands) on the GPU against the oracle.
+
+The oracle computes the exact (fp64) attention of q, k and v rounded to the
+16-bit format.  The kernel additionally rounds the probabilities to that
+format for the P.V product while normalising with the f32 sum, so an output
+element may move by up to u * max|v| (u = 2^-11 for binary16, 2^-8 for
+bfloat16) on top of f32 rounding; the contract asserted here is
+
+    max |gpu - oracle_lowp| <= 2 u max|v_rounded| + 1e-5.
+
+Cases: ragged S across 32-key and 128-query tiles, every head_dim, batch > 1,
+causal and not, a non-default scale with large scores, both formats, and the
+three prefill workloads at full size (sampled rows for the causal one).  The
+error against the exact f32-input attention is printed for reference (it is
+dominated by the rounding of q and k, not part of the contract).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import transformer_attention_flash_amd as taf
+from transformer_attention_flash_amd import workloads as wl
+from gpu_common import nan_like, note, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = {"fp16": (taf.ATTN_PREC_FP16, 2.0 ** -11), "bf16": (taf.ATTN_PREC_BF16, 2.0 ** -8)}
+
+SMALL = [
+    # B, S, H, d
+    (1, 1, 1, 32),
+    (1, 31, 2, 32),
+    (2, 33, 3, 64),
+    (1, 127, 1, 128),
+    (1, 129, 2, 128),
+    (3, 200, 2, 64),
+    (2, 300, 4, 128),
+    (1, 500, 8, 128),
+    (1, 257, 16, 32),
+]
+
+
+def run_lowp(q, k, v, B, S, H, d, scale, causal, prec):
+    out = nan_like((B, S, H * d))
+    taf.attn_prefill_lowp(to_dev(q), to_dev(k), to_dev(v), out, B, S, H, d, scale, causal, prec)
+    return to_host(out)
+
+
+def check(got, want, v_rounded, u, what):
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    tol = 2.0 * u * float(np.max(np.abs(v_rounded))) + 1e-5
+    err = float(np.max(np.abs(got - want)))
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.3e}"
+    return err
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}_S{c[1]}_H{c[2]}_d{c[3]}" for c in SMALL])
+def test_prefill_lowp_small(case, causal, fmt):
+    B, S, H, d = case
+    prec, u = FORMATS[fmt]
+    rng = np.random.default_rng(11 + S * 13 + H + d)
+    q, k, v = (rng.standard_normal((B, S, H * d), dtype=np.float32) for _ in range(3))
+    scale = wl.scale_for(d)
+    note(f"prefill_lowp {fmt} B={B} S={S} H={H} d={d} causal={causal}")
+    got = run_lowp(q, k, v, B, S, H, d, scale, causal, prec)
+    orc = oracle.default()
+    want = orc.prefill_lowp(q, k, v, B, S, H, d, scale, causal, prec)
+    check(got, want, orc.round16(v, prec), u, f"{fmt} {case} causal={causal}")
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_prefill_lowp_large_scores_and_custom_scale(fmt):
+    B, S, H, d = 1, 333, 2, 128
+    prec, u = FORMATS[fmt]
+    rng = np.random.default_rng(4)
+    q = (rng.standard_normal((B, S, H * d), dtype=np.float32) * 6).astype(np.float32)
+    k, v = (rng.standard_normal((B, S, H * d), dtype=np.float32) for _ in range(2))
+    note(f"prefill_lowp {fmt} large scores")
+    orc = oracle.default()
+    for causal in (False, True):
+        got = run_lowp(q, k, v, B, S, H, d, 0.3, causal, prec)
+        want = orc.prefill_lowp(q, k, v, B, S, H, d, 0.3, causal, prec)
+        check(got, want, orc.round16(v, prec), u, f"{fmt} large scores causal={causal}")
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("cid", [1, 2])
+def test_prefill_lowp_full_size_noncausal(cid, fmt):
+    cfg = wl.PREFILL[cid]
+    prec, u = FORMATS[fmt]
+    q, k, v = wl.prefill_inputs(cfg)
+    note(f"prefill_lowp {fmt} full size {cfg.name}")
+    got = run_lowp(q, k, v, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, cfg.causal, prec)
+    orc = oracle.default()
+    want = orc.prefill_lowp(q, k, v, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, cfg.causal, prec)
+    err = check(got, want, orc.round16(v, prec), u, f"{fmt} {cfg.name}")
+    exact = orc.prefill(q, k, v, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, cfg.causal)
+    note(f"  {fmt} {cfg.name}: err vs rounded-input oracle {err:.2e}, "
+         f"vs f32-input attention {float(np.max(np.abs(got - exact))):.2e}")
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+def test_prefill_lowp_full_size_causal_sampled(fmt):
+    cfg = wl.PREFILL[3]
+    prec, u = FORMATS[fmt]
+    q, k, v = wl.prefill_inputs(cfg)
+    note(f"prefill_lowp {fmt} full size {cfg.name}")
+    got = run_lowp(q, k, v, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, cfg.causal, prec)
+    assert np.all(np.isfinite(got)), "every output element is written"
+    orc = oracle.default()
+    rq, rk, rv = (orc.round16(x, prec) for x in (q, k, v))
+    rng = np.random.default_rng(34)
+    rows = [0, 1, 31, 32, 127, 128, 129, 1023, 1024, 2046, 2047] + rng.integers(0, cfg.S, 21).tolist()
+    sel = np.array([(b, i, h) for b in range(cfg.B) for i in rows for h in ((i + b) % cfg.H, (5 * i) % cfg.H)],
+                   np.int64)
+    # The reduced-precision attention is the attention of the rounded inputs (pinned on the CPU).
+    want = orc.prefill_rows(rq, rk, rv, sel, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, True)
+    got_sel = np.stack([got[b, i, h * cfg.d:(h + 1) * cfg.d] for b, i, h in sel])
+    check(got_sel, want, rv, u, f"{fmt} causal full-size sampled rows")

@@ -22,6 +22,9 @@ __all__ = [
     "ATTN_MAX_SEQS",
     "attn_prefill",
     "attn_prefill_cached",
+    "attn_prefill_lowp",
+    "ATTN_PREC_FP16",
+    "ATTN_PREC_BF16",
     "attn_decode_workspace_bytes",
     "attn_decode_gqa_batched",
     "kv_cache_scatter",
@@ -36,6 +39,8 @@ __all__ = [
 ]
 
 ATTN_MAX_SEQS = 32
+ATTN_PREC_FP16 = 1
+ATTN_PREC_BF16 = 2
 _STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_INVALID_DIM", 3: "ATTN_ERR_UNSUPPORTED",
     4: "ATTN_ERR_OVERFLOW", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_ALIAS",
@@ -69,6 +74,8 @@ def library() -> ctypes.CDLL:
         p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
         lib.attn_prefill.argtypes = [p, p, p, p, i32, i32, i32, i32, f32, i32, p]
         lib.attn_prefill.restype = ctypes.c_int
+        lib.attn_prefill_lowp.argtypes = [p, p, p, p, i32, i32, i32, i32, f32, i32, i32, p]
+        lib.attn_prefill_lowp.restype = ctypes.c_int
         lib.attn_prefill_cached.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p]
         lib.attn_prefill_cached.restype = ctypes.c_int
         lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -153,6 +160,17 @@ def attn_prefill(q, k, v, out, batch: int, seq_len: int, n_heads: int, head_dim:
     ptrs = [_check_tensor(nm, t, n, dev) for nm, t in (("q", q), ("k", k), ("v", v), ("out", out))]
     _call("attn_prefill", library().attn_prefill(*ptrs, batch, seq_len, n_heads, head_dim, scale,
                                                  1 if causal else 0, _stream_ptr(dev, stream)))
+
+
+def attn_prefill_lowp(q, k, v, out, batch: int, seq_len: int, n_heads: int, head_dim: int,
+                      scale: float, causal: bool, precision: int, stream=None) -> None:
+    """attn_prefill on 16-bit MFMA operands; precision ATTN_PREC_FP16 or ATTN_PREC_BF16 (f32 in and out)."""
+    n = batch * seq_len * n_heads * head_dim
+    dev = q.device
+    ptrs = [_check_tensor(nm, t, n, dev) for nm, t in (("q", q), ("k", k), ("v", v), ("out", out))]
+    _call("attn_prefill_lowp", library().attn_prefill_lowp(*ptrs, batch, seq_len, n_heads, head_dim, scale,
+                                                           1 if causal else 0, int(precision),
+                                                           _stream_ptr(dev, stream)))
 
 
 def attn_prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens: Sequence[int], out, num_seqs: int,

@@ -180,6 +180,39 @@ int attn_prefill(const float *q, const float *k, const float *v, float *out, int
     return from_hip(attn::launch_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+int attn_prefill_lowp(const float *q, const float *k, const float *v, float *out, int32_t batch,
+                      int32_t seq_len, int32_t n_heads, int32_t head_dim, float scale, int32_t causal,
+                      int32_t precision, void *stream) {
+    if (!q || !k || !v || !out) return ATTN_ERR_NULL;
+    if (batch <= 0 || seq_len <= 0 || n_heads <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_DIM;
+    if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID_DIM;
+    if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (precision != ATTN_PREC_FP16 && precision != ATTN_PREC_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_UNSUPPORTED;
+    int64_t elems;
+    if (!checked_mul({batch, seq_len, n_heads, head_dim}, kMaxElems32, &elems)) return ATTN_ERR_OVERFLOW;
+    const int64_t bytes = elems * 4;
+    if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) || overlaps(out, bytes, v, bytes))
+        return ATTN_ERR_ALIAS;
+
+    attn::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.B = batch;
+    a.S = seq_len;
+    a.H = n_heads;
+    a.D = head_dim;
+    a.scale = scale;
+    a.causal = causal;
+    a.cached = 0;
+    a.Hkv = n_heads;
+    a.max_len = seq_len;
+    return from_hip(attn::launch_prefill_lowp(a, precision, static_cast<hipStream_t>(stream)));
+}
+
 int attn_prefill_cached(const float *q, const float *k_new, const float *v_new, float *k_cache,
                         float *v_cache, const int32_t *cache_lens, float *out, int32_t num_seqs,
                         int32_t n_new, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -58,6 +58,9 @@ struct PrefillArgs {
     SeqInts pos;
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+// The same attention (cached must be 0) on 16-bit MFMA operands:
+// precision ATTN_PREC_FP16 or ATTN_PREC_BF16.
+hipError_t launch_prefill_lowp(const PrefillArgs &a, int32_t precision, hipStream_t stream);
 
 // Split-KV decode.  Workspace layout (floats):
 //   acc[M][H][max_splits][D]  unnormalised per-split outputs

@@ -1,0 +1,319 @@
+// prefill_lowp.hip -- reduced-precision fused prefill: the attention of
+// [B, S, H * D] f32 activations with both products on 16-bit MFMA operands
+// (binary16 or bfloat16) and everything else in f32.
+//
+// Semantics: the same attention as prefill.hip (trueno-gpu 0.4.11
+// src/memory/resident/attention.rs, `batched_multihead_attention`;
+// trustformers-core 0.2.0 src/gpu_ops/cuda/oxicuda/attention.rs,
+// `attention_prefill_gpu_to_gpu`), computed the way trueno-gpu's
+// `batched_gemm` does once k >= 64: GEMM operands rounded to fp16 for the
+// tensor cores, products accumulated wider.  Here q, k and v are rounded to
+// the 16-bit type (nearest, ties to even) as they are loaded; the scores
+// S^T = K Q^T accumulate in f32 (a product of two 16-bit values is exact in
+// f32); the online softmax runs in f32; the probabilities are rounded to the
+// 16-bit type as the operand of O^T = V^T P^T, which accumulates in f32; the
+// running sum and the final normalisation use the f32 probabilities.
+//
+// Layout of v_mfma_f32_32x32x16_{bf16,f16} (lane l, i = l % 32, h = l / 32):
+// operand A supplies A[i][8h .. 8h+7], operand B supplies B[8h .. 8h+7][i],
+// output register v holds D[8 (v / 4) + 4 h + (v % 4)][i].  The k order inside
+// one instruction is free as long as both operands agree, which the P.V
+// product uses: the score registers of a lane hold keys 4h .. 4h+3 and
+// 8+4h .. 8+4h+3 of each 16-key half of a 32-key sub-tile, so those eight keys
+// are that lane's k slots, the probabilities go from score registers to
+// operand registers with a conversion only, and V^T is read at the same keys.
+//
+// Work decomposition as in prefill.hip: a workgroup owns BM = 128 queries of
+// one (b, h), each wave 32 of them with its Q slice (16-bit) and its 32 x D
+// f32 output in registers.  K/V tiles of BN keys are loaded as f32 into
+// registers one tile ahead, rounded, and written to a double-buffered LDS
+// tile: K row-major (rows padded by 16 bytes: the 16-byte operand reads of 8
+// consecutive rows hit distinct banks), V transposed to [D][BN] with its
+// 8-byte key groups XOR-swizzled by dimension (conflict-free operand reads).
+// One workgroup barrier per tile.
+#include "device_common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int BM = 32 * kWaves;  // queries per workgroup
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <typename T> struct Lp;
+template <> struct Lp<__bf16> {
+    typedef bf16x4 v4;
+    typedef bf16x8 v8;
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, const f32x16 &c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Lp<_Float16> {
+    typedef f16x4 v4;
+    typedef f16x8 v8;
+    static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, const f32x16 &c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Key row (within a 32-key sub-tile) / output row of register v in lane-half h.
+__device__ __forceinline__ int mrow(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
+
+template <typename T, typename V4>
+__device__ __forceinline__ V4 round4(f32x4 x) {
+    return V4{(T)x[0], (T)x[1], (T)x[2], (T)x[3]};
+}
+
+template <int D, int BN, bool CAUSAL, typename T>
+__global__ __launch_bounds__(kThreads, 2) void prefill_lowp_kernel(PrefillArgs a, int32_t n_qtiles,
+                                                                   int32_t xcd_remap) {
+    typedef typename Lp<T>::v4 v4;
+    typedef typename Lp<T>::v8 v8;
+    constexpr int NT = D / 32;   // 32-row tiles of O^T
+    constexpr int KK = D / 16;   // k steps of the score product
+    constexpr int NSUB = BN / 32;  // 32-key sub-tiles per tile
+    constexpr int KP = D + 8;    // LDS pitch of a K row (elements)
+    constexpr int U = BN / 4;    // 8-byte key groups per V^T row
+    // Staging: a thread moves blocks of 4 keys x 4 dims of K and of V.
+    constexpr int NBLK = (BN / 4) * (D / 4);
+    constexpr int BPT = (NBLK + kThreads - 1) / kThreads;  // blocks per thread
+    static_assert(BN == 32 || BN == 64, "tile of 32 or 64 keys");
+
+    __shared__ __attribute__((aligned(16))) T Ks0[BN * KP];
+    __shared__ __attribute__((aligned(16))) T Vt0[D * BN];
+    __shared__ __attribute__((aligned(16))) T Ks1[BN * KP];
+    __shared__ __attribute__((aligned(16))) T Vt1[D * BN];
+
+    // ---- block -> (b, h, query tile): heavy causal tiles first; with
+    // xcd_remap the query tiles of one (b, h) share an XCD (and its L2).
+    const int BH = a.B * a.H;
+    int bh, qt;
+    {
+        const int bid = blockIdx.x;
+        int rank;
+        if (xcd_remap) {
+            const int per_xcd_bh = BH / 8;
+            const int x = bid % 8, t = bid / 8;
+            bh = 8 * (t % per_xcd_bh) + x;
+            rank = t / per_xcd_bh;
+        } else {
+            bh = bid % BH;
+            rank = bid / BH;
+        }
+        qt = CAUSAL ? n_qtiles - 1 - rank : rank;
+    }
+    const int b = bh / a.H;
+    const int hd = bh % a.H;
+    const int S = a.S;
+    const size_t row_stride = (size_t)a.H * D;
+    const size_t head_base = (size_t)b * S * row_stride + (size_t)hd * D;
+    const float *__restrict__ qg = a.q + head_base;
+    const float *__restrict__ kg = a.k + head_base;
+    const float *__restrict__ vg = a.v + head_base;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int li = lane & 31;
+    const int lh = lane >> 5;
+    const int q0 = qt * BM;
+    const int qw0 = q0 + 32 * wave;
+    const int my_q = qw0 + li;
+
+    // ---- Q^T operand: query my_q, dims 16 kk + 8 lh .. +7, rounded.
+    v8 qop[KK];
+    {
+        const bool ok = my_q < S;
+        const float *qp = qg + (size_t)(ok ? my_q : 0) * row_stride + 8 * lh;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const f32x4 x0 = ok ? *reinterpret_cast<const f32x4 *>(qp + 16 * kk) : f32x4{0, 0, 0, 0};
+            const f32x4 x1 = ok ? *reinterpret_cast<const f32x4 *>(qp + 16 * kk + 4) : f32x4{0, 0, 0, 0};
+            const v4 r0 = round4<T, v4>(x0), r1 = round4<T, v4>(x1);
+            qop[kk] = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    }
+    const float qs = a.scale * kLog2e;  // scores to log2 units
+
+    f32x16 o[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[n] = f32x16{};
+    float m_run = kNegBig;
+    float l_run = 0.f;
+
+    const int n_ktiles_all = (S + BN - 1) / BN;
+    const int n_ktiles = CAUSAL ? min(n_ktiles_all, (min(q0 + BM, S) - 1) / BN + 1) : n_ktiles_all;
+
+    // ---- staging: block blk = (key quad kq, dim chunk c); rows past S read
+    // row S - 1 (in bounds; their scores are masked, probabilities exactly 0).
+    f32x4 kst[BPT][4], vst[BPT][4];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int blk = tid + kThreads * u;
+            if (NBLK % kThreads == 0 || blk < NBLK) {
+                const int c = blk % (D / 4), kq = blk / (D / 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const size_t key = (size_t)min(kt * BN + 4 * kq + j, S - 1);
+                    kst[u][j] = *reinterpret_cast<const f32x4 *>(kg + key * row_stride + 4 * c);
+                    vst[u][j] = *reinterpret_cast<const f32x4 *>(vg + key * row_stride + 4 * c);
+                }
+            }
+        }
+    };
+    auto write_tile = [&](T *Ks, T *Vt) {
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int blk = tid + kThreads * u;
+            if (NBLK % kThreads == 0 || blk < NBLK) {
+                const int c = blk % (D / 4), kq = blk / (D / 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *reinterpret_cast<v4 *>(Ks + (4 * kq + j) * KP + 4 * c) = round4<T, v4>(kst[u][j]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int dim = 4 * c + e;
+                    const int swz = (U == 16) ? (dim & 15) : ((dim >> 1) & 7);
+                    const f32x4 col = {vst[u][0][e], vst[u][1][e], vst[u][2][e], vst[u][3][e]};
+                    *reinterpret_cast<v4 *>(Vt + dim * BN + 4 * (kq ^ swz)) = round4<T, v4>(col);
+                }
+            }
+        }
+    };
+
+    auto compute = [&](int kt, const T *Ks, const T *Vt) {
+        const int kt0 = kt * BN;
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub) {
+            const int ks0 = kt0 + 32 * sub;  // first key of the sub-tile
+            if (CAUSAL && ks0 > qw0 + 31) break;  // wave-uniform: above this wave's diagonal
+            // S^T = K Q^T: lane supplies K[key ks0 + li][16 kk + 8 lh .. +7].
+            f32x16 s = f32x16{};
+            const T *krow = Ks + (32 * sub + li) * KP + 8 * lh;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                s = Lp<T>::mfma(*reinterpret_cast<const v8 *>(krow + 16 * kk), qop[kk], s);
+
+            const bool need_mask = (ks0 + 32 > S) || (CAUSAL && ks0 + 31 > qw0);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                float x = s[v] * qs;
+                if (need_mask) {
+                    const int key = ks0 + mrow(v, lh);
+                    if (key >= S || (CAUSAL && key > my_q)) x = -INFINITY;
+                }
+                s[v] = x;
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            float psum = 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                s[v] = fast_exp2(s[v] - m_new);
+                psum += s[v];
+            }
+            l_run = l_run * alpha + psum;
+            if (__any(alpha != 1.0f)) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n) o[n] *= alpha;
+            }
+
+            // O^T += V^T P^T over two 16-key halves t: this lane's k slots are
+            // keys 16t + 4lh + (0..3) and 16t + 8 + 4lh + (0..3) of the sub-tile.
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const v4 p0 = round4<T, v4>(f32x4{s[8 * t + 0], s[8 * t + 1], s[8 * t + 2], s[8 * t + 3]});
+                const v4 p1 = round4<T, v4>(f32x4{s[8 * t + 4], s[8 * t + 5], s[8 * t + 6], s[8 * t + 7]});
+                const v8 pop = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+                const int g0 = 8 * sub + 4 * t + lh;  // 8-byte key groups of the tile
+                const int g1 = g0 + 2;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    const int dim = 32 * n + li;
+                    const int swz = (U == 16) ? (dim & 15) : ((dim >> 1) & 7);
+                    const v4 a0 = *reinterpret_cast<const v4 *>(Vt + dim * BN + 4 * (g0 ^ swz));
+                    const v4 a1 = *reinterpret_cast<const v4 *>(Vt + dim * BN + 4 * (g1 ^ swz));
+                    o[n] = Lp<T>::mfma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), pop, o[n]);
+                }
+            }
+        }
+    };
+
+    // ---- pipeline: tile kt+1 is in registers while tile kt is consumed from
+    // LDS; after the barrier that ends tile kt, tile kt+2's loads go out.
+    load_tile(0);
+    write_tile(Ks0, Vt0);
+    __syncthreads();
+    if (n_ktiles > 1) load_tile(1);
+    for (int kt = 0; kt < n_ktiles; kt += 2) {
+        compute(kt, Ks0, Vt0);
+        if (kt + 1 < n_ktiles) write_tile(Ks1, Vt1);
+        __syncthreads();
+        if (kt + 2 < n_ktiles) load_tile(kt + 2);
+        if (kt + 1 < n_ktiles) {
+            compute(kt + 1, Ks1, Vt1);
+            if (kt + 2 < n_ktiles) write_tile(Ks0, Vt0);
+            __syncthreads();
+            if (kt + 3 < n_ktiles) load_tile(kt + 3);
+        }
+    }
+
+    // ---- normalise and store: lane holds query my_q, dims 32 n + 8 g + 4 lh + (0..3).
+    l_run += __shfl_xor(l_run, 32);
+    if (my_q < S) {
+        const float inv = 1.0f / l_run;
+        float *op = a.out + head_base + (size_t)my_q * row_stride + 4 * lh;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<f32x4 *>(op + 32 * n + 8 * g) =
+                    f32x4{o[n][4 * g] * inv, o[n][4 * g + 1] * inv, o[n][4 * g + 2] * inv, o[n][4 * g + 3] * inv};
+    }
+}
+
+#ifndef ATTN_LOWP_BN
+#define ATTN_LOWP_BN 64
+#endif
+
+template <int D, bool CAUSAL, typename T>
+hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
+    const int32_t n_qtiles = (a.S + BM - 1) / BM;
+    const int32_t BH = a.B * a.H;
+    const int32_t xcd_remap = (BH % 8 == 0) ? 1 : 0;
+    dim3 grid((unsigned)(BH * n_qtiles));
+    prefill_lowp_kernel<D, ATTN_LOWP_BN, CAUSAL, T><<<grid, dim3(kThreads), 0, stream>>>(a, n_qtiles, xcd_remap);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const PrefillArgs &a, hipStream_t stream) {
+    switch (a.D) {
+        case 32: return a.causal ? launch_typed<32, true, T>(a, stream) : launch_typed<32, false, T>(a, stream);
+        case 64: return a.causal ? launch_typed<64, true, T>(a, stream) : launch_typed<64, false, T>(a, stream);
+        case 128: return a.causal ? launch_typed<128, true, T>(a, stream) : launch_typed<128, false, T>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_lowp(const PrefillArgs &a, int32_t precision, hipStream_t stream) {
+    if (precision == ATTN_PREC_BF16) return launch_t<__bf16>(a, stream);
+    if (precision == ATTN_PREC_FP16) return launch_t<_Float16>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace attn
