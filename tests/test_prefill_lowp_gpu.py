@@ -8,9 +8,11 @@ bfloat16) on top of f32 rounding; the contract asserted here is
 
     max |gpu - oracle_lowp| <= 2 u max|v_rounded| + 1e-5.
 
-Cases: ragged S across 32-key and 128-query tiles, every head_dim, batch > 1,
-causal and not, a non-default scale with large scores, both formats, and the
-three prefill workloads at full size (sampled rows for the causal one).  The
+Cases: ragged S across 32/64-key and 128/256-query tiles, every head_dim,
+batch > 1, causal and not, both work decompositions (4 and 8 waves per
+workgroup, chosen by problem size), a non-default and a negative scale with
+large scores, both formats, and the three prefill workloads at full size
+(sampled rows for the causal one).  The
 error against the exact f32-input attention is printed for reference (it is
 dominated by the rounding of q and k, not part of the contract).
 """
@@ -71,6 +73,35 @@ def test_prefill_lowp_small(case, causal, fmt):
     check(got, want, orc.round16(v, prec), u, f"{fmt} {case} causal={causal}")
 
 
+EIGHT_WAVE = [
+    # B, S, H, d: B*H*ceil(S/256) >= 512 runs the 256-query, 64-key-tile path; ragged S
+    (2, 1000, 64, 128),
+    (4, 777, 32, 64),
+    (16, 300, 32, 32),
+]
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("case", EIGHT_WAVE, ids=[f"B{c[0]}_S{c[1]}_H{c[2]}_d{c[3]}" for c in EIGHT_WAVE])
+def test_prefill_lowp_eight_wave_path(case, causal, fmt):
+    B, S, H, d = case
+    prec, u = FORMATS[fmt]
+    rng = np.random.default_rng(17 + S + H + d)
+    q, k, v = (rng.standard_normal((B, S, H * d), dtype=np.float32) for _ in range(3))
+    scale = wl.scale_for(d)
+    note(f"prefill_lowp {fmt} eight-wave B={B} S={S} H={H} d={d} causal={causal}")
+    got = run_lowp(q, k, v, B, S, H, d, scale, causal, prec)
+    assert np.all(np.isfinite(got)), "every output element is written"
+    orc = oracle.default()
+    rq, rk, rv = (orc.round16(x, prec) for x in (q, k, v))
+    rows = sorted({0, 1, 31, 32, 63, 64, 127, 128, 255, 256, S // 2, S - 65, S - 64, S - 1})
+    sel = np.array([(b, i, h) for b in range(B) for i in rows for h in range(0, H, max(1, H // 8))], np.int64)
+    want = orc.prefill_rows(rq, rk, rv, sel, B, S, H, d, scale, causal)
+    got_sel = np.stack([got[b, i, h * d:(h + 1) * d] for b, i, h in sel])
+    check(got_sel, want, rv, u, f"{fmt} eight-wave {case} causal={causal}")
+
+
 @pytest.mark.parametrize("fmt", list(FORMATS))
 def test_prefill_lowp_large_scores_and_custom_scale(fmt):
     B, S, H, d = 1, 333, 2, 128
@@ -81,9 +112,10 @@ def test_prefill_lowp_large_scores_and_custom_scale(fmt):
     note(f"prefill_lowp {fmt} large scores")
     orc = oracle.default()
     for causal in (False, True):
-        got = run_lowp(q, k, v, B, S, H, d, 0.3, causal, prec)
-        want = orc.prefill_lowp(q, k, v, B, S, H, d, 0.3, causal, prec)
-        check(got, want, orc.round16(v, prec), u, f"{fmt} large scores causal={causal}")
+        for scale in (0.3, -0.2):
+            got = run_lowp(q, k, v, B, S, H, d, scale, causal, prec)
+            want = orc.prefill_lowp(q, k, v, B, S, H, d, scale, causal, prec)
+            check(got, want, orc.round16(v, prec), u, f"{fmt} large scores scale={scale} causal={causal}")
 
 
 @pytest.mark.parametrize("fmt", list(FORMATS))

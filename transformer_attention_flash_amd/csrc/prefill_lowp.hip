@@ -23,23 +23,22 @@
 // are that lane's k slots, the probabilities go from score registers to
 // operand registers with a conversion only, and V^T is read at the same keys.
 //
-// Work decomposition as in prefill.hip: a workgroup owns BM = 128 queries of
-// one (b, h), each wave 32 of them with its Q slice (16-bit) and its 32 x D
-// f32 output in registers.  K/V tiles of BN keys are loaded as f32 into
-// registers one tile ahead, rounded, and written to a double-buffered LDS
-// tile: K row-major (rows padded by 16 bytes: the 16-byte operand reads of 8
-// consecutive rows hit distinct banks), V transposed to [D][BN] with its
-// 8-byte key groups XOR-swizzled by dimension (conflict-free operand reads).
-// One workgroup barrier per tile.
+// Work decomposition as in prefill.hip: a workgroup owns BM = 32 NW queries
+// of one (b, h) (NW = 8 waves, or 4 for small problems), each wave 32 of them
+// with its Q slice (16-bit) and its 32 x D f32 output in registers.  K/V tiles
+// of BN keys are loaded as f32 into registers one tile ahead, rounded, and
+// written to a double-buffered LDS tile: K row-major (rows padded by 16 bytes:
+// the 16-byte operand reads of 8 consecutive rows hit distinct banks), V
+// transposed to [D][BN] with its 8-byte key groups XOR-swizzled by dimension
+// (conflict-free operand reads).  One workgroup barrier per tile.  The
+// softmax rescales lazily (see kLazy).
 #include "device_common.h"
 #include "launch.h"
 
 namespace attn {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int BM = 32 * kWaves;  // queries per workgroup
+constexpr float kLazy = 8.0f;    // log2 headroom of the lazily rescaled softmax
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -70,9 +69,13 @@ __device__ __forceinline__ V4 round4(f32x4 x) {
     return V4{(T)x[0], (T)x[1], (T)x[2], (T)x[3]};
 }
 
-template <int D, int BN, bool CAUSAL, typename T>
-__global__ __launch_bounds__(kThreads, 2) void prefill_lowp_kernel(PrefillArgs a, int32_t n_qtiles,
-                                                                   int32_t xcd_remap) {
+// NW waves of 32 queries each (BM = 32 NW queries per workgroup), key tiles of
+// BN keys; two waves per SIMD either way.
+template <int D, int NW, int BN, bool CAUSAL, typename T>
+__global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(PrefillArgs a, int32_t n_qtiles,
+                                                                          int32_t xcd_remap) {
+    constexpr int kThreads = kWave * NW;
+    constexpr int BM = 32 * NW;
     typedef typename Lp<T>::v4 v4;
     typedef typename Lp<T>::v8 v8;
     constexpr int NT = D / 32;   // 32-row tiles of O^T
@@ -126,20 +129,25 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_lowp_kernel(PrefillArgs a
     const int qw0 = q0 + 32 * wave;
     const int my_q = qw0 + li;
 
-    // ---- Q^T operand: query my_q, dims 16 kk + 8 lh .. +7, rounded.
-    v8 qop[KK];
-    {
+    // ---- Q^T operand: query my_q, dims 16 kk + 8 lh .. +7, rounded.  For a
+    // negative scale the query is negated first (rounding is symmetric, so
+    // the scores are exactly negated) and |scale| is used: the softmax then
+    // always multiplies by a non-negative factor and can take its maximum on
+    // the raw scores.
+    const float qsign = a.scale < 0.f ? -1.f : 1.f;
+    const float qsa = fabsf(a.scale) * kLog2e;  // raw scores to log2 units
+    v8 qop[KK];  // filled below, once the first K/V tile's loads are in flight
+    auto load_q = [&]() {
         const bool ok = my_q < S;
         const float *qp = qg + (size_t)(ok ? my_q : 0) * row_stride + 8 * lh;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             const f32x4 x0 = ok ? *reinterpret_cast<const f32x4 *>(qp + 16 * kk) : f32x4{0, 0, 0, 0};
             const f32x4 x1 = ok ? *reinterpret_cast<const f32x4 *>(qp + 16 * kk + 4) : f32x4{0, 0, 0, 0};
-            const v4 r0 = round4<T, v4>(x0), r1 = round4<T, v4>(x1);
+            const v4 r0 = round4<T, v4>(x0 * qsign), r1 = round4<T, v4>(x1 * qsign);
             qop[kk] = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-    }
-    const float qs = a.scale * kLog2e;  // scores to log2 units
+    };
 
     f32x16 o[NT];
 #pragma unroll
@@ -150,20 +158,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_lowp_kernel(PrefillArgs a
     const int n_ktiles_all = (S + BN - 1) / BN;
     const int n_ktiles = CAUSAL ? min(n_ktiles_all, (min(q0 + BM, S) - 1) / BN + 1) : n_ktiles_all;
 
-    // ---- staging: block blk = (key quad kq, dim chunk c); rows past S read
-    // row S - 1 (in bounds; their scores are masked, probabilities exactly 0).
+    // ---- staging: block blk = (key quad kq, dim chunk c).  Element offsets
+    // within a tile are fixed per thread; a tile adds a uniform base, so a
+    // load is a 32-bit offset from a scalar base.  In the last, partial tile
+    // rows past S read row S - 1 (in bounds; their scores are masked and their
+    // probabilities are exactly 0).
     f32x4 kst[BPT][4], vst[BPT][4];
+    uint32_t goff[BPT][4];  // element offset of row 4 kq + j, chunk c, within a tile
+    int rowq[BPT];          // 4 kq
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+        const int blk = tid + kThreads * u;
+        const int c = blk % (D / 4), kq = blk / (D / 4);
+        rowq[u] = 4 * kq;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) goff[u][j] = (uint32_t)((size_t)(4 * kq + j) * row_stride + 4 * c);
+    }
     auto load_tile = [&](int kt) {
+        const size_t tbase = (size_t)kt * BN * row_stride;
+        const float *kt_g = kg + tbase;
+        const float *vt_g = vg + tbase;
+        const bool partial = kt * BN + BN > S;  // uniform
 #pragma unroll
         for (int u = 0; u < BPT; ++u) {
             const int blk = tid + kThreads * u;
             if (NBLK % kThreads == 0 || blk < NBLK) {
-                const int c = blk % (D / 4), kq = blk / (D / 4);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const size_t key = (size_t)min(kt * BN + 4 * kq + j, S - 1);
-                    kst[u][j] = *reinterpret_cast<const f32x4 *>(kg + key * row_stride + 4 * c);
-                    vst[u][j] = *reinterpret_cast<const f32x4 *>(vg + key * row_stride + 4 * c);
+                    uint32_t off = goff[u][j];
+                    if (partial) {
+                        const int over = kt * BN + rowq[u] + j - (S - 1);
+                        if (over > 0) off -= (uint32_t)((size_t)over * row_stride);
+                    }
+                    kst[u][j] = *reinterpret_cast<const f32x4 *>(kt_g + off);
+                    vst[u][j] = *reinterpret_cast<const f32x4 *>(vt_g + off);
                 }
             }
         }
@@ -189,54 +217,97 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_lowp_kernel(PrefillArgs a
     };
 
     auto compute = [&](int kt, const T *Ks, const T *Vt) {
-        const int kt0 = kt * BN;
-#pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub) {
-            const int ks0 = kt0 + 32 * sub;  // first key of the sub-tile
-            if (CAUSAL && ks0 > qw0 + 31) break;  // wave-uniform: above this wave's diagonal
-            // S^T = K Q^T: lane supplies K[key ks0 + li][16 kk + 8 lh .. +7].
-            f32x16 s = f32x16{};
-            const T *krow = Ks + (32 * sub + li) * KP + 8 * lh;
+        const int kt0 = kt * BN;  // first key of the tile
+        if (CAUSAL && kt0 > qw0 + 31) return;  // wave-uniform: whole tile above this wave's diagonal
+        // S^T = K Q^T for the NSUB 32-key sub-tiles at once: their MFMA chains
+        // are independent, so interleaving them keeps the matrix pipe busy.
+        // Lane supplies K[key 32 sub + li][16 kk + 8 lh .. +7].
+        // Lane supplies K[key 32 sub + li][16 kk + 8 lh .. +7].  One sub-tile:
+        // all its K operands are read from LDS before the MFMA chain starts, so
+        // the chain does not wait on an LDS round trip per step.  Two
+        // sub-tiles: their chains are independent and interleaved instead.
+        f32x16 s[NSUB];
+        if constexpr (NSUB == 1) {
+            v8 kop[KK];
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-                s = Lp<T>::mfma(*reinterpret_cast<const v8 *>(krow + 16 * kk), qop[kk], s);
-
-            const bool need_mask = (ks0 + 32 > S) || (CAUSAL && ks0 + 31 > qw0);
+                kop[kk] = *reinterpret_cast<const v8 *>(Ks + li * KP + 8 * lh + 16 * kk);
+            // Keep the reads ahead of the chain (the scheduler would otherwise
+            // sink each read next to its MFMA to save registers).
+            __builtin_amdgcn_sched_barrier(0);
+            // Two independent accumulation chains (even and odd k steps).
+            f32x16 s1 = f32x16{};
+            s[0] = f32x16{};
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float x = s[v] * qs;
-                if (need_mask) {
-                    const int key = ks0 + mrow(v, lh);
-                    if (key >= S || (CAUSAL && key > my_q)) x = -INFINITY;
+            for (int kk = 0; kk < KK; kk += 2) {
+                s[0] = Lp<T>::mfma(kop[kk], qop[kk], s[0]);
+                if (kk + 1 < KK) s1 = Lp<T>::mfma(kop[kk + 1], qop[kk + 1], s1);
+            }
+            s[0] += s1;
+        } else {
+#pragma unroll
+            for (int sub = 0; sub < NSUB; ++sub) s[sub] = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                for (int sub = 0; sub < NSUB; ++sub)
+                    s[sub] = Lp<T>::mfma(
+                        *reinterpret_cast<const v8 *>(Ks + (32 * sub + li) * KP + 8 * lh + 16 * kk), qop[kk], s[sub]);
+        }
+
+        // Online softmax over the tile's BN keys in raw score units: the
+        // scale (>= 0, see qsa) is folded into the exponent's FMA.
+        const bool need_mask = (kt0 + BN > S) || (CAUSAL && kt0 + BN - 1 > qw0);
+        if (need_mask) {
+#pragma unroll
+            for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = kt0 + 32 * sub + mrow(v, lh);
+                    if (key >= S || (CAUSAL && key > my_q)) s[sub][v] = -INFINITY;
                 }
-                s[v] = x;
-            }
-            float mx = s[0];
+        }
+        float mx = s[0][0];
 #pragma unroll
-            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sub][v]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // Lazy rescaling: the reference maximum m_run moves (and O and l are
+        // rescaled) only when a lane's scores would exceed it by more than
+        // 2^kLazy; otherwise the probabilities are taken against the stale
+        // reference and stay below 2^kLazy, well inside f32 and both 16-bit
+        // formats.  The decision is wave-uniform, so most tiles skip the
+        // 16 * NT multiplies of the rescale.
+        if (__any((mx - m_run) * qsa > kLazy)) {
             const float m_new = fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - m_new);
+            const float alpha = fast_exp2((m_run - m_new) * qsa);
             m_run = m_new;
-            float psum = 0.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) o[n] *= alpha;
+        }
+        const float mb = m_run * qsa;
+        float psum = 0.f;
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                s[v] = fast_exp2(s[v] - m_new);
-                psum += s[v];
+                float pv = fast_exp2(fmaf(s[sub][v], qsa, -mb));
+                if (need_mask) pv = (s[sub][v] == -INFINITY) ? 0.f : pv;  // exact zeros, also for scale 0
+                s[sub][v] = pv;
+                psum += pv;
             }
-            l_run = l_run * alpha + psum;
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int n = 0; n < NT; ++n) o[n] *= alpha;
-            }
+        l_run += psum;
 
-            // O^T += V^T P^T over two 16-key halves t: this lane's k slots are
-            // keys 16t + 4lh + (0..3) and 16t + 8 + 4lh + (0..3) of the sub-tile.
+        // O^T += V^T P^T over the 16-key halves t of each sub-tile: this lane's
+        // k slots are keys 16t + 4lh + (0..3) and 16t + 8 + 4lh + (0..3).  All
+        // V operands of a sub-tile are read before its MFMAs, as for K.
+#pragma unroll
+        for (int sub = 0; sub < NSUB; ++sub) {
+            v8 vop[2][NT];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const v4 p0 = round4<T, v4>(f32x4{s[8 * t + 0], s[8 * t + 1], s[8 * t + 2], s[8 * t + 3]});
-                const v4 p1 = round4<T, v4>(f32x4{s[8 * t + 4], s[8 * t + 5], s[8 * t + 6], s[8 * t + 7]});
-                const v8 pop = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
                 const int g0 = 8 * sub + 4 * t + lh;  // 8-byte key groups of the tile
                 const int g1 = g0 + 2;
 #pragma unroll
@@ -245,15 +316,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_lowp_kernel(PrefillArgs a
                     const int swz = (U == 16) ? (dim & 15) : ((dim >> 1) & 7);
                     const v4 a0 = *reinterpret_cast<const v4 *>(Vt + dim * BN + 4 * (g0 ^ swz));
                     const v4 a1 = *reinterpret_cast<const v4 *>(Vt + dim * BN + 4 * (g1 ^ swz));
-                    o[n] = Lp<T>::mfma(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7), pop, o[n]);
+                    vop[t][n] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
             }
+            v8 pop[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const v4 p0 = round4<T, v4>(f32x4{s[sub][8 * t + 0], s[sub][8 * t + 1], s[sub][8 * t + 2],
+                                                  s[sub][8 * t + 3]});
+                const v4 p1 = round4<T, v4>(f32x4{s[sub][8 * t + 4], s[sub][8 * t + 5], s[sub][8 * t + 6],
+                                                  s[sub][8 * t + 7]});
+                pop[t] = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) o[n] = Lp<T>::mfma(vop[t][n], pop[t], o[n]);
         }
     };
 
     // ---- pipeline: tile kt+1 is in registers while tile kt is consumed from
     // LDS; after the barrier that ends tile kt, tile kt+2's loads go out.
     load_tile(0);
+    load_q();  // the Q and first-tile loads overlap: one memory round trip, not two
     write_tile(Ks0, Vt0);
     __syncthreads();
     if (n_ktiles > 1) load_tile(1);
@@ -284,17 +370,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_lowp_kernel(PrefillArgs a
     }
 }
 
-#ifndef ATTN_LOWP_BN
-#define ATTN_LOWP_BN 64
-#endif
-
+// Eight waves (256 queries) per workgroup halve the K/V reads and conversions
+// per query; four waves keep small problems spread over the 256 CUs.  One
+// eight-wave workgroup fills a CU, so eight waves are used when that still
+// gives at least two workgroups per CU.
 template <int D, bool CAUSAL, typename T>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
-    const int32_t n_qtiles = (a.S + BM - 1) / BM;
     const int32_t BH = a.B * a.H;
     const int32_t xcd_remap = (BH % 8 == 0) ? 1 : 0;
-    dim3 grid((unsigned)(BH * n_qtiles));
-    prefill_lowp_kernel<D, ATTN_LOWP_BN, CAUSAL, T><<<grid, dim3(kThreads), 0, stream>>>(a, n_qtiles, xcd_remap);
+    const int32_t tiles8 = (a.S + 255) / 256;
+    if ((int64_t)BH * tiles8 >= 512) {
+        dim3 grid((unsigned)(BH * tiles8));
+        prefill_lowp_kernel<D, 8, 64, CAUSAL, T><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
+    } else {
+        const int32_t tiles4 = (a.S + 127) / 128;
+        dim3 grid((unsigned)(BH * tiles4));
+        prefill_lowp_kernel<D, 4, 32, CAUSAL, T><<<grid, dim3(kWave * 4), 0, stream>>>(a, tiles4, xcd_remap);
+    }
     return hipGetLastError();
 }
 
