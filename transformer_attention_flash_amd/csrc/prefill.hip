@@ -15,9 +15,9 @@
 // scores: an online softmax (running row max and sum, output rescaled when
 // the max grows) walks the key axis tile by tile.
 //
-// Work decomposition: a workgroup owns BM = 128 queries of one (b, h); each
-// of its 4 wavefronts owns 32 of them and keeps its Q slice in VGPRs and its
-// 32 x D output accumulator in registers.  K and V tiles of BN = 32 keys go
+// Work decomposition: a workgroup owns BM = 32 NW queries of one (b, h) (NW =
+// 8 waves, or 4 for small problems); each wavefront owns 32 of them and keeps
+// its Q slice in VGPRs and its 32 x D output accumulator in registers.  K and V tiles of BN = 32 keys go
 // from HBM straight into a double-buffered LDS tile (global_load_lds, no
 // register staging); the next tile's transfer is in flight while the current
 // one is consumed, with one workgroup barrier per tile.  Both products run on v_mfma_f32_32x32x2_f32.
@@ -36,10 +36,7 @@
 namespace attn {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int BM = 32 * kWaves;  // queries per workgroup
-constexpr int BN = 32;           // keys per LDS tile (one 32-key MFMA sub-tile)
+constexpr int BN = 32;  // keys per LDS tile (one 32-key MFMA sub-tile)
 
 __device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -62,9 +59,12 @@ __device__ __forceinline__ void wait_vmem_all() {
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int32_t n_qtiles,
-                                                              int32_t xcd_remap) {
+// NW waves of 32 queries each: BM = 32 NW queries per workgroup.
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs a, int32_t n_qtiles,
+                                                                     int32_t xcd_remap) {
+    constexpr int kWaves = NW;
+    constexpr int BM = 32 * NW;
     constexpr int NT = D / 32;          // 32-row tiles of O^T; also floats per lane per V row
     constexpr int QV = D / 8;           // 16-byte Q/K vectors per lane
     constexpr int CPR = D / 4;          // 16-byte chunks per K/V row
@@ -258,13 +258,26 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a, int
     }
 }
 
+// Eight waves (256 queries) per workgroup halve the K/V tile transfers per
+// query; four waves keep small problems spread over the CUs.  One eight-wave
+// workgroup fills a CU, so eight waves are used when that still gives at least
+// two workgroups per CU (and D >= 64: a 32-key tile of D = 32 rows is too small
+// to split over eight waves).
 template <int D, bool CAUSAL>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
-    const int32_t n_qtiles = (a.S + BM - 1) / BM;
     const int32_t BH = a.B * a.H;
     const int32_t xcd_remap = (BH % 8 == 0) ? 1 : 0;
-    dim3 grid((unsigned)(BH * n_qtiles));
-    prefill_kernel<D, CAUSAL><<<grid, dim3(kThreads), 0, stream>>>(a, n_qtiles, xcd_remap);
+    const int32_t tiles8 = (a.S + 255) / 256;
+    if constexpr (D >= 64) {
+        if ((int64_t)BH * tiles8 >= 512) {
+            dim3 grid((unsigned)(BH * tiles8));
+            prefill_kernel<D, 8, CAUSAL><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
+            return hipGetLastError();
+        }
+    }
+    const int32_t tiles4 = (a.S + 127) / 128;
+    dim3 grid((unsigned)(BH * tiles4));
+    prefill_kernel<D, 4, CAUSAL><<<grid, dim3(kWave * 4), 0, stream>>>(a, tiles4, xcd_remap);
     return hipGetLastError();
 }
 
