@@ -61,6 +61,24 @@ template <> struct Lp<_Float16> {
     }
 };
 
+// While a wave issues its matrix instructions it runs at a raised wave
+// priority, so that the SIMD's other wave (in its softmax) does not delay
+// them: the matrix pipe stays fed and the VALU work of the other wave fills
+// the gaps.
+#ifndef ATTN_LOWP_PRIO
+#define ATTN_LOWP_PRIO 1
+#endif
+__device__ __forceinline__ void mfma_priority(int p) {
+#if ATTN_LOWP_PRIO
+    if (p)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
+#else
+    (void)p;
+#endif
+}
+
 // Key row (within a 32-key sub-tile) / output row of register v in lane-half h.
 __device__ __forceinline__ int mrow(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
@@ -238,21 +256,25 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
             // Two independent accumulation chains (even and odd k steps).
             f32x16 s1 = f32x16{};
             s[0] = f32x16{};
+            mfma_priority(1);
 #pragma unroll
             for (int kk = 0; kk < KK; kk += 2) {
                 s[0] = Lp<T>::mfma(kop[kk], qop[kk], s[0]);
                 if (kk + 1 < KK) s1 = Lp<T>::mfma(kop[kk + 1], qop[kk + 1], s1);
             }
+            mfma_priority(0);
             s[0] += s1;
         } else {
 #pragma unroll
             for (int sub = 0; sub < NSUB; ++sub) s[sub] = f32x16{};
+            mfma_priority(1);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
                 for (int sub = 0; sub < NSUB; ++sub)
                     s[sub] = Lp<T>::mfma(
                         *reinterpret_cast<const v8 *>(Ks + (32 * sub + li) * KP + 8 * lh + 16 * kk), qop[kk], s[sub]);
+            mfma_priority(0);
         }
 
         // Online softmax over the tile's BN keys in raw score units: the
@@ -329,10 +351,12 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
                 pop[t] = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
             }
             __builtin_amdgcn_sched_barrier(0);
+            mfma_priority(1);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int n = 0; n < NT; ++n) o[n] = Lp<T>::mfma(vop[t][n], pop[t], o[n]);
+            mfma_priority(0);
         }
     };
 
