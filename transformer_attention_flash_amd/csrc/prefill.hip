@@ -185,12 +185,17 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
         // S^T = K Q^T over D (k-slot lk of step (j, c) is column 8j + 4lk + c).
         f32x16 s = f32x16{};
         const float *kbase = Kt + li * D;
+        // Raised wave priority while this wave issues matrix instructions:
+        // the SIMD's other wave (in its softmax or waiting) does not delay
+        // them.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int j = 0; j < QV; ++j) {
             const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + 4 * ((2 * j + lk) ^ (li & SWZ)));
 #pragma unroll
             for (int c = 0; c < 4; ++c) s = mfma32(kv[c], qreg[j][c], s);
         }
+        __builtin_amdgcn_s_setprio(0);
 
         // Mask: keys past Sk, and (causal) keys after the query's position.
         const bool need_mask = (ks0 + 32 > Sk) || (CAUSAL && ks0 + 31 > P + qw0);
@@ -226,12 +231,14 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
 
         // O^T += V^T P^T: at key step v this lane supplies V[key][NT*li + n]
         // for n-tile n and P^T[key][my_q] = s[v].
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const vrow_t vv = *reinterpret_cast<const vrow_t *>(Vt + mrow(v, lk) * D + NT * li);
 #pragma unroll
             for (int n = 0; n < NT; ++n) o[n] = mfma32(vget<NT>(vv, n), s[v], o[n]);
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // Two-stage pipeline with one barrier per tile: after a tile's barrier every
