@@ -52,6 +52,35 @@ def test_prefill_small(case, causal):
     assert_attn_close(got, want, f"prefill {case} causal={causal}")
 
 
+DECOMPOSITIONS = [
+    # B, S, H, d -> which work decomposition the launcher picks (B*H*ceil(S/128) and
+    # B*H*ceil(S/256) decide): small non-causal problems split each workgroup's keys
+    # over 4 groups (2 at d = 128); mid-size ones use 4 waves; large ones 8 waves.
+    (1, 1500, 8, 64),     # key split, KS = 4 (the Whisper-base shape)
+    (1, 700, 4, 128),     # key split, KS = 2, ragged tail
+    (3, 70, 5, 32),       # key split with fewer key tiles than groups in some workgroups
+    (2, 1100, 16, 64),    # four waves (non-causal: 288 workgroups)
+    (2, 1000, 64, 128),   # eight waves
+]
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("case", DECOMPOSITIONS, ids=[f"B{c[0]}_S{c[1]}_H{c[2]}_d{c[3]}" for c in DECOMPOSITIONS])
+def test_prefill_decompositions(case, causal):
+    B, S, H, d = case
+    rng = np.random.default_rng(5 + S + H + d)
+    q, k, v = (rng.standard_normal((B, S, H * d), dtype=np.float32) for _ in range(3))
+    scale = wl.scale_for(d)
+    note(f"prefill decomposition B={B} S={S} H={H} d={d} causal={causal}")
+    got = run_prefill(q, k, v, B, S, H, d, scale, causal)
+    assert np.all(np.isfinite(got)), "every output element is written"
+    rows = sorted({0, 1, 31, 32, 63, 64, 127, 128, 255, 256, S // 2, S - 65, S - 64, S - 1} & set(range(S)))
+    sel = np.array([(b, i, h) for b in range(B) for i in rows for h in range(0, H, max(1, H // 8))], np.int64)
+    want = oracle.default().prefill_rows(q, k, v, sel, B, S, H, d, scale, causal)
+    got_sel = np.stack([got[b, i, h * d:(h + 1) * d] for b, i, h in sel])
+    assert_attn_close(got_sel, want, f"prefill decomposition {case} causal={causal}")
+
+
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 def test_prefill_large_scores_and_custom_scale(causal):
     B, S, H, d = 1, 333, 2, 128
