@@ -61,9 +61,10 @@ __host__ __device__ constexpr int ocol(int n, int i) {
 // span[m] keys (a multiple of 4 waves x 32 keys; the last block may be
 // shorter); workgroup start[m] + (kh * n_hblk + hb) * nkblk[m] + kblk runs one.
 struct UnitMap {
-    int32_t start[ATTN_MAX_SEQS + 1];  // first workgroup of each sequence; start[M] = grid size
-    int32_t nkblk[ATTN_MAX_SEQS];
-    int32_t span[ATTN_MAX_SEQS];
+    int32_t start[ATTN_MAX_SEQS + 1];  // first workgroup of the i-th sequence in grid order; start[M] = grid size
+    int32_t seq[ATTN_MAX_SEQS];        // the i-th sequence in grid order (longest key blocks first)
+    int32_t nkblk[ATTN_MAX_SEQS];      // per sequence
+    int32_t span[ATTN_MAX_SEQS];       // per sequence
 };
 
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
@@ -100,12 +101,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     // workgroup takes chunks w, w + 4, w + 8, ... of the key block, so the
     // four waves stream adjacent 32-key chunks of K (and of V) side by side,
     // and it owns split slot 4 * kblk + w.
-    int m = 0;
-    while (unit >= map.start[m + 1]) ++m;
+    int pos = 0;
+    while (unit >= map.start[pos + 1]) ++pos;
+    const int m = map.seq[pos];
     const int L = a.lens.v[m];
     const int span = map.span[m];
     const int nkblk = map.nkblk[m];
-    int rem = unit - map.start[m];
+    int rem = unit - map.start[pos];
     const int kblk = rem % nkblk;
     rem /= nkblk;
     const int hb = rem % n_hblk;
@@ -476,10 +478,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
     const int32_t sf = span_floor(a.max_len);
 
     UnitMap map;
-    int32_t acc = 0;
     for (int i = 0; i < a.M; ++i) {
         const int32_t L = a.lens.v[i];
-        map.start[i] = acc;
         map.nkblk[i] = 0;
         map.span[i] = sf;
         if (L == 0) continue;
@@ -490,13 +490,30 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
         if (span < sf) span = sf;
         map.span[i] = span;
         map.nkblk[i] = (L + span - 1) / span;
-        acc += map.nkblk[i] * (int32_t)units_per_seq;
     }
-    for (int i = a.M; i <= ATTN_MAX_SEQS; ++i) map.start[i] = acc;
     for (int i = a.M; i < ATTN_MAX_SEQS; ++i) {
         map.nkblk[i] = 0;
         map.span[i] = sf;
     }
+    // Grid order: sequences with the longest key blocks first, so the blocks
+    // dispatched last are the short ones and the device drains evenly.
+    for (int i = 0; i < a.M; ++i) map.seq[i] = i;
+    for (int i = 1; i < a.M; ++i) {  // insertion sort, stable, by span descending
+        const int32_t x = map.seq[i];
+        int j = i - 1;
+        while (j >= 0 && map.span[map.seq[j]] < map.span[x]) {
+            map.seq[j + 1] = map.seq[j];
+            --j;
+        }
+        map.seq[j + 1] = x;
+    }
+    for (int i = a.M; i < ATTN_MAX_SEQS; ++i) map.seq[i] = i;
+    int32_t acc = 0;
+    for (int i = 0; i < a.M; ++i) {
+        map.start[i] = acc;
+        acc += map.nkblk[map.seq[i]] * (int32_t)units_per_seq;
+    }
+    for (int i = a.M; i <= ATTN_MAX_SEQS; ++i) map.start[i] = acc;
 
     dim3 block(kThreads);
     if (acc > 0) {
