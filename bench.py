@@ -216,7 +216,14 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    per = {n: float(np.mean([e[n][0].elapsed_time(e[n][1]) for e in evs])) for n in names}
+    samples = {n: np.array([e[n][0].elapsed_time(e[n][1]) for e in evs]) for n in names}
+    per = {n: float(np.mean(samples[n])) for n in names}
+
+    def spread(n):
+        """median / min / p90 of one call's event times over the timed steps (us)."""
+        x = samples[n] * 1e3
+        return {"median_us": round(float(np.median(x)), 2), "min_us": round(float(np.min(x)), 2),
+                "p90_us": round(float(np.percentile(x, 90)), 2)}
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step; " +
         ", ".join(f"{n} {per[n] * 1e3:.1f} us" for n in names))
 
@@ -251,13 +258,14 @@ def main():
                        "sum_L": int(lens.sum())},
         },
         "decode": {"gbs": round(dec_gbs, 2), "frac_hbm": round(dec_gbs / HBM_PEAK_GBS, 4),
-                   "us": round(per["decode"] * 1e3, 2), "algorithmic_bytes": dec_bytes},
+                   "us": round(per["decode"] * 1e3, 2), **spread("decode"), "algorithmic_bytes": dec_bytes},
         "prefill": {"tflops": round(pre_tflops, 3), "frac_mfma": round(pre_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
-                    "us": round(per["prefill"] * 1e3, 2), "algorithmic_flops": pre_flops},
+                    "us": round(per["prefill"] * 1e3, 2), **spread("prefill"), "algorithmic_flops": pre_flops},
         "bulk_scatter": {"gbs": round(blk_gbs, 2), "frac_hbm": round(blk_gbs / HBM_PEAK_GBS, 4),
-                         "us": round(per["bulk_scatter"] * 1e3, 2), "algorithmic_bytes": scfg.bytes},
-        "append": {"us": round(per["append"] * 1e3, 2), "algorithmic_bytes": dcfg.append_bytes},
-        "roofline": {"kernel": "prefill_kernel<128, causal>", "bound": "mfma", "achieved": round(pre_tflops, 3),
+                         "us": round(per["bulk_scatter"] * 1e3, 2), **spread("bulk_scatter"),
+                         "algorithmic_bytes": scfg.bytes},
+        "append": {"us": round(per["append"] * 1e3, 2), **spread("append"), "algorithmic_bytes": dcfg.append_bytes},
+        "roofline": {"kernel": "prefill_kernel<128, 8 waves, causal>", "bound": "mfma", "achieved": round(pre_tflops, 3),
                      "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(pre_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic("prefill")},
@@ -267,6 +275,7 @@ def main():
                             "traffic": measured_traffic("decode")},
         "cpu_baseline": None,
         "next_rows": None,
+        "calibration": None,
     }
 
     if not args.no_next_rows:
@@ -344,6 +353,22 @@ def main():
             "algorithmic_bytes": s_bytes}
         log(f"slot copy: {s_ms * 1e3:.1f} us ({s_gbs:.0f} GB/s)")
         del dk, dv
+
+    if not args.no_next_rows:
+        # Context for the roofline peaks, measured on this device with library
+        # routines (not this package's kernels): an fp32 GEMM and a device copy.
+        a32 = torch.randn(8192, 8192, device=dev)
+        mm_ms = time_call(torch, lambda: torch.mm(a32, a32), None, warm=2, reps=5)
+        cp_src = torch.empty(1 << 28, device=dev)
+        cp_dst = torch.empty_like(cp_src)
+        cp_ms = time_call(torch, lambda: cp_dst.copy_(cp_src), None, warm=2, reps=5)
+        result["calibration"] = {
+            "torch_mm_f32_8192_tflops": round(2 * 8192 ** 3 / (mm_ms * 1e-3) / 1e12, 2),
+            "torch_copy_1GiB_gbs": round(2 * (1 << 30) / (cp_ms * 1e-3) / 1e9, 1),
+            "note": "library routines on this device, for context next to the spec peaks"}
+        log(f"calibration: fp32 GEMM {result['calibration']['torch_mm_f32_8192_tflops']} TFLOP/s, "
+            f"copy {result['calibration']['torch_copy_1GiB_gbs']} GB/s")
+        del a32, cp_src, cp_dst
 
     # Free the GPU copies before the host-side leg.
     del pq, pk, pv, pout, bk, bv, dq, dkn, dvn, dkc, dvc, dout, ws
