@@ -87,13 +87,17 @@ __device__ __forceinline__ V4 round4(f32x4 x) {
     return V4{(T)x[0], (T)x[1], (T)x[2], (T)x[3]};
 }
 
-// NW waves of 32 queries each (BM = 32 NW queries per workgroup), key tiles of
-// BN keys; two waves per SIMD either way.
-template <int D, int NW, int BN, bool CAUSAL, typename T>
+// NW waves in KS groups: the NW / KS waves of a group own 32 queries each
+// (BM = 32 NW / KS queries per workgroup) and group g walks the g-th of KS
+// contiguous ranges of the key tiles of BN keys (KS > 1 only for small
+// non-causal problems; the groups' softmax states are merged at the end).
+// Two waves per SIMD either way.
+template <int D, int NW, int KS, int BN, bool CAUSAL, typename T>
 __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(PrefillArgs a, int32_t n_qtiles,
                                                                           int32_t xcd_remap) {
-    constexpr int kThreads = kWave * NW;
-    constexpr int BM = 32 * NW;
+    constexpr int QW = NW / KS;       // query waves per group
+    constexpr int kThreads = kWave * QW;  // threads of one group (they stage its tiles)
+    constexpr int BM = 32 * QW;
     typedef typename Lp<T>::v4 v4;
     typedef typename Lp<T>::v8 v8;
     constexpr int NT = D / 32;   // 32-row tiles of O^T
@@ -105,11 +109,14 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
     constexpr int NBLK = (BN / 4) * (D / 4);
     constexpr int BPT = (NBLK + kThreads - 1) / kThreads;  // blocks per thread
     static_assert(BN == 32 || BN == 64, "tile of 32 or 64 keys");
+    static_assert(NW % KS == 0 && (KS == 1 || !CAUSAL), "key groups only without a causal mask");
 
-    __shared__ __attribute__((aligned(16))) T Ks0[BN * KP];
-    __shared__ __attribute__((aligned(16))) T Vt0[D * BN];
-    __shared__ __attribute__((aligned(16))) T Ks1[BN * KP];
-    __shared__ __attribute__((aligned(16))) T Vt1[D * BN];
+    __shared__ __attribute__((aligned(16))) T Ks0[KS * BN * KP];
+    __shared__ __attribute__((aligned(16))) T Vt0[KS * D * BN];
+    __shared__ __attribute__((aligned(16))) T Ks1[KS * BN * KP];
+    __shared__ __attribute__((aligned(16))) T Vt1[KS * D * BN];
+    constexpr int SLOT = kWave * (16 * NT + 2);  // floats of one parked wave state (merge)
+    __shared__ float Red[KS > 1 ? (KS - 1) * QW * SLOT : 1];
 
     // ---- block -> (b, h, query tile): heavy causal tiles first; with
     // xcd_remap the query tiles of one (b, h) share an XCD (and its L2).
@@ -138,8 +145,10 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
     const float *__restrict__ kg = a.k + head_base;
     const float *__restrict__ vg = a.v + head_base;
 
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int tid_all = threadIdx.x;
+    const int grp = tid_all / kThreads;   // key group of this wave
+    const int tid = tid_all % kThreads;   // thread index within the group
+    const int wave = tid >> 6;            // query wave within the group
     const int lane = tid & 63;
     const int li = lane & 31;
     const int lh = lane >> 5;
@@ -175,6 +184,8 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
 
     const int n_ktiles_all = (S + BN - 1) / BN;
     const int n_ktiles = CAUSAL ? min(n_ktiles_all, (min(q0 + BM, S) - 1) / BN + 1) : n_ktiles_all;
+    const int TG = (n_ktiles + KS - 1) / KS;  // key tiles per group; group grp owns tiles grp*TG ..
+    const int gt0 = grp * TG;
 
     // ---- staging: block blk = (key quad kq, dim chunk c).  Element offsets
     // within a tile are fixed per thread; a tile adds a uniform base, so a
@@ -193,6 +204,8 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
         for (int j = 0; j < 4; ++j) goff[u][j] = (uint32_t)((size_t)(4 * kq + j) * row_stride + 4 * c);
     }
     auto load_tile = [&](int kt) {
+        kt += gt0;
+        if (KS > 1 && kt >= n_ktiles) return;  // past this group's range (uniform per group)
         const size_t tbase = (size_t)kt * BN * row_stride;
         const float *kt_g = kg + tbase;
         const float *vt_g = vg + tbase;
@@ -215,6 +228,8 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
         }
     };
     auto write_tile = [&](T *Ks, T *Vt) {
+        Ks += grp * BN * KP;
+        Vt += grp * D * BN;
 #pragma unroll
         for (int u = 0; u < BPT; ++u) {
             const int blk = tid + kThreads * u;
@@ -235,6 +250,10 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
     };
 
     auto compute = [&](int kt, const T *Ks, const T *Vt) {
+        kt += gt0;
+        if (KS > 1 && kt >= n_ktiles) return;  // this group's range is done (uniform per group)
+        Ks += grp * BN * KP;
+        Vt += grp * D * BN;
         const int kt0 = kt * BN;  // first key of the tile
         if (CAUSAL && kt0 > qw0 + 31) return;  // wave-uniform: whole tile above this wave's diagonal
         // S^T = K Q^T for the NSUB 32-key sub-tiles at once: their MFMA chains
@@ -366,17 +385,48 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
     load_q();  // the Q and first-tile loads overlap: one memory round trip, not two
     write_tile(Ks0, Vt0);
     __syncthreads();
-    if (n_ktiles > 1) load_tile(1);
-    for (int kt = 0; kt < n_ktiles; kt += 2) {
+    if (TG > 1) load_tile(1);
+    for (int kt = 0; kt < TG; kt += 2) {
         compute(kt, Ks0, Vt0);
-        if (kt + 1 < n_ktiles) write_tile(Ks1, Vt1);
+        if (kt + 1 < TG) write_tile(Ks1, Vt1);
         __syncthreads();
-        if (kt + 2 < n_ktiles) load_tile(kt + 2);
-        if (kt + 1 < n_ktiles) {
+        if (kt + 2 < TG) load_tile(kt + 2);
+        if (kt + 1 < TG) {
             compute(kt + 1, Ks1, Vt1);
-            if (kt + 2 < n_ktiles) write_tile(Ks0, Vt0);
+            if (kt + 2 < TG) write_tile(Ks0, Vt0);
             __syncthreads();
-            if (kt + 3 < n_ktiles) load_tile(kt + 3);
+            if (kt + 3 < TG) load_tile(kt + 3);
+        }
+    }
+
+    // ---- merge the key groups: groups 1.. park (reference max, partial sum,
+    // output) of each lane, group 0 folds them in.  Every group's softmax
+    // state is relative to its own reference max m (probabilities
+    // 2^((s - m) qsa)), so the usual rescaling applies.
+    if constexpr (KS > 1) {
+        if (grp > 0) {
+            float *dst = Red + ((grp - 1) * QW + wave) * SLOT + lane;
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) dst[(16 * n + v) * kWave] = o[n][v];
+            dst[16 * NT * kWave] = m_run;
+            dst[(16 * NT + 1) * kWave] = l_run;
+        }
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll
+        for (int g = 1; g < KS; ++g) {
+            const float *src = Red + ((g - 1) * QW + wave) * SLOT + lane;
+            const float m_g = src[16 * NT * kWave];
+            const float m_new = fmaxf(m_run, m_g);
+            const float keep = fast_exp2((m_run - m_new) * qsa), take = fast_exp2((m_g - m_new) * qsa);
+            l_run = l_run * keep + src[(16 * NT + 1) * kWave] * take;
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[n][v] = o[n][v] * keep + src[(16 * n + v) * kWave] * take;
+            m_run = m_new;
         }
     }
 
@@ -405,12 +455,22 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const int32_t tiles8 = (a.S + 255) / 256;
     if ((int64_t)BH * tiles8 >= 512) {
         dim3 grid((unsigned)(BH * tiles8));
-        prefill_lowp_kernel<D, 8, 64, CAUSAL, T><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
-    } else {
-        const int32_t tiles4 = (a.S + 127) / 128;
-        dim3 grid((unsigned)(BH * tiles4));
-        prefill_lowp_kernel<D, 4, 32, CAUSAL, T><<<grid, dim3(kWave * 4), 0, stream>>>(a, tiles4, xcd_remap);
+        prefill_lowp_kernel<D, 8, 1, 64, CAUSAL, T><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
+        return hipGetLastError();
     }
+    const int32_t tiles4 = (a.S + 127) / 128;
+    if constexpr (!CAUSAL && D <= 64) {
+        if ((int64_t)BH * tiles4 < 256) {
+            // Too small to give every CU a workgroup: split each workgroup's
+            // keys over 4 groups of 2 query waves (64 queries per workgroup).
+            const int32_t tiles2 = (a.S + 63) / 64;
+            dim3 grid((unsigned)(BH * tiles2));
+            prefill_lowp_kernel<D, 8, 4, 32, false, T><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles2, xcd_remap);
+            return hipGetLastError();
+        }
+    }
+    dim3 grid((unsigned)(BH * tiles4));
+    prefill_lowp_kernel<D, 4, 1, 32, CAUSAL, T><<<grid, dim3(kWave * 4), 0, stream>>>(a, tiles4, xcd_remap);
     return hipGetLastError();
 }
 
