@@ -127,12 +127,12 @@ def test_decode_validation(lib):
 
 def test_decode_workspace_bytes(lib):
     # acc [M, H, splits, d] + (max, sum) [M, H, splits, 2] floats.  A split is
-    # one wave's share of a key block; a sequence has at most 64 key blocks of
-    # at least 128 keys (a power-of-two multiple of 128), 4 splits each.
-    assert lib.attn_decode_workspace_bytes(32, 32, 128, 4096) == 32 * 32 * 128 * 130 * 4
-    assert lib.attn_decode_workspace_bytes(16, 64, 128, 32768) == 16 * 64 * 256 * 130 * 4
-    assert lib.attn_decode_workspace_bytes(1, 1, 32, 1) == 1 * 1 * 4 * 34 * 4
-    assert lib.attn_decode_workspace_bytes(2, 4, 64, 300) == 2 * 4 * 12 * 66 * 4
+    # one key block; a sequence has at most 64 key blocks of at least 128 keys
+    # (a power-of-two multiple of 128).
+    assert lib.attn_decode_workspace_bytes(32, 32, 128, 4096) == 32 * 32 * 32 * 130 * 4
+    assert lib.attn_decode_workspace_bytes(16, 64, 128, 32768) == 16 * 64 * 64 * 130 * 4
+    assert lib.attn_decode_workspace_bytes(1, 1, 32, 1) == 1 * 1 * 1 * 34 * 4
+    assert lib.attn_decode_workspace_bytes(2, 4, 64, 300) == 2 * 4 * 3 * 66 * 4
     assert lib.attn_decode_workspace_bytes(0, 8, 128, 16) == 0
     assert lib.attn_decode_workspace_bytes(33, 8, 128, 16) == 0
     assert lib.attn_decode_workspace_bytes(2, 8, 80, 16) == 0

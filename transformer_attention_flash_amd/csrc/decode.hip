@@ -14,9 +14,9 @@
 // group is served from each load: the g query heads sharing a KV head make the
 // scores a dense [16 x d] x [d x 16] contraction per 16 keys (heads padded to
 // 16), which runs on v_mfma_f32_16x16x4_f32 and leaves the VALU free for the
-// softmax.  Each wave's running max m_s (log2 units), sum l_s and
-// unnormalised output acc_s over its chunks form one split, written to the
-// workspace.
+// softmax.  Each wave keeps a running max (log2 units), sum and unnormalised
+// output over its chunks; at the end the four waves merge theirs through LDS
+// into one split per key block, (m_s, l_s, acc_s), written to the workspace.
 //
 // Pass 2 (decode_combine_kernel): one workgroup per (m, h) merges the splits:
 // with M* = max_s m_s and w_s = 2^(m_s - M*), out = sum_s w_s acc_s /
@@ -99,8 +99,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
 
     // unit -> (m, kh, head block hb, key block kblk).  Wave w of the
     // workgroup takes chunks w, w + 4, w + 8, ... of the key block, so the
-    // four waves stream adjacent 32-key chunks of K (and of V) side by side,
-    // and it owns split slot 4 * kblk + w.
+    // four waves stream adjacent 32-key chunks of K (and of V) side by side;
+    // the workgroup writes split slot kblk.
     int pos = 0;
     while (unit >= map.start[pos + 1]) ++pos;
     const int m = map.seq[pos];
@@ -112,7 +112,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     rem /= nkblk;
     const int hb = rem % n_hblk;
     const int kh = rem / n_hblk;
-    const int s = kblk * kWavesPerBlock + wave;
 
     const int g = a.H / a.Hkv;
     const int hi = lane & 15;  // head column / key row within a tile
@@ -308,28 +307,57 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Each k-slot group summed its own keys; combine them.  A wave whose key
-    // block had no chunk for it still writes its (empty) partial: max kNegBig,
-    // sum 0, output 0, which the merge weighs by 2^(kNegBig - M*) = 0.
+    // Each k-slot group summed its own keys; combine them.
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
 
+    // Merge the four waves' states through LDS: each wave parks (m, l, O^T)
+    // in its own K tile (its last reads of that tile are behind it: a wave's
+    // LDS accesses complete in order), then wave w merges output register r = w
+    // of every lane from all four, i.e. rows 4 kq + w of O^T, and writes them.
+    // A wave that had no chunk of the key block parks max kNegBig, sum 0,
+    // output 0, which the merge weighs by 2^(kNegBig - M*) = 0 (wave 0 always
+    // has a chunk, so M* is a real maximum).
+    static_assert(16 * D + 32 <= kChunk * KROW, "parked state fits the K tile");
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kl[(4 * n + r) * kWave + lane] = o[n][r];
+    if (kq == 0) {
+        kl[16 * D + hi] = m_run;
+        kl[16 * D + 16 + hi] = l_run;
+    }
+    __syncthreads();
+    float mw[kWavesPerBlock], wt[kWavesPerBlock];
+    float mstar = kNegBig;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        mw[w] = k_lds[w][16 * D + hi];
+        mstar = fmaxf(mstar, mw[w]);
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        wt[w] = fast_exp2(mw[w] - mstar);
+        lsum += wt[w] * k_lds[w][16 * D + 16 + hi];
+    }
     if (head_ok) {
-        const size_t slot = ((size_t)m * a.H + h) * a.max_splits + s;
-        if (kq == 0) {
-            *reinterpret_cast<f32x2 *>(a.ws_ml + 2 * slot) = f32x2{m_run, l_run};
-        }
+        const size_t slot = ((size_t)m * a.H + h) * a.max_splits + kblk;
+        if (wave == 0 && kq == 0) *reinterpret_cast<f32x2 *>(a.ws_ml + 2 * slot) = f32x2{mstar, lsum};
         float *dst = a.ws_acc + slot * D;
+        const int r = wave;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 4 * kq + r;
+        for (int c = 0; c < NVV; ++c) {
+            vvec val;
 #pragma unroll
-            for (int c = 0; c < NVV; ++c) {
-                vvec val;
+            for (int e = 0; e < VW; ++e) {
+                const int n = c * VW + e;
+                float acc = 0.f;
 #pragma unroll
-                for (int e = 0; e < VW; ++e) vset<VW>(val, e, o[c * VW + e][r]);
-                *reinterpret_cast<vvec *>(dst + ocol<D>(c * VW, i)) = val;
+                for (int w = 0; w < kWavesPerBlock; ++w) acc += wt[w] * k_lds[w][(4 * n + r) * kWave + lane];
+                vset<VW>(val, e, acc);
             }
+            *reinterpret_cast<vvec *>(dst + ocol<D>(c * VW, 4 * kq + r)) = val;
         }
     }
 }
@@ -343,14 +371,14 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a, 
     __shared__ __attribute__((aligned(16))) float part_acc[kWavesPerBlock][D];
     __shared__ float part_m[kWavesPerBlock], part_l[kWavesPerBlock];
 
-    // One workgroup per (m, h); wave w merges splits w, w + 4, ... with a
-    // running max, then wave 0 merges the four results.  The order is fixed,
-    // so the output is identical from run to run.
+    // One workgroup per (m, h), one split per key block; wave w merges splits
+    // w, w + 4, ... with a running max, then wave 0 merges the four results.
+    // The order is fixed, so the output is identical from run to run.
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = blockIdx.x;
     const int m = w / a.H;
-    const int nsplit = kWavesPerBlock * map.nkblk[m];
+    const int nsplit = map.nkblk[m];
     float *dst = a.out + (size_t)w * D;
 
     if (nsplit == 0) {  // empty sequence: zeros (uniform over the block)
@@ -453,7 +481,7 @@ int32_t capacity_for(int32_t D) {
 
 int32_t decode_max_splits(int32_t max_len) {
     const int32_t sf = span_floor(max_len);
-    return kWavesPerBlock * ((max_len + sf - 1) / sf);
+    return (max_len + sf - 1) / sf;
 }
 
 size_t decode_workspace_bytes(int64_t M, int64_t H, int64_t D, int64_t max_len) {
