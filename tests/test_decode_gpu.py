@@ -5,7 +5,9 @@ last needs two 16-head blocks), every head_dim, empty sequences, lengths on
 and around split/chunk boundaries, L = max_len, M = 32, and cache rows past
 L_m filled with NaN (they must never be read).  Full-size cases run the two
 decode workloads as one step: append the new row at L_m - 1, then attend
-over L_m keys.
+over L_m keys.  Results are bitwise the same on every stream and every
+repeated call, and a decode captured into a HIP graph replays to the eager
+result.
 """
 import numpy as np
 import pytest
@@ -13,7 +15,7 @@ import pytest
 import oracle
 import transformer_attention_flash_amd as taf
 from transformer_attention_flash_amd import workloads as wl
-from gpu_common import assert_attn_close, nan_like, note, to_dev, to_host
+from gpu_common import assert_attn_close, bits, nan_like, note, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -129,3 +131,83 @@ def test_decode_step_full_size(cid):
         got_sel = np.stack([got[m, h * cfg.d:(h + 1) * cfg.d] for m, h in sel])
         assert_attn_close(got_sel, want, "cfg5 decode (sampled heads)")
         assert np.all(np.isfinite(got))
+
+
+def _decode_on(stream, q, kc, vc, lens, M, H, Hkv, d, max_len, scale):
+    import torch
+    with torch.cuda.stream(stream):
+        ws = torch.empty(taf.attn_decode_workspace_bytes(M, H, d, max_len) // 4, dtype=torch.float32,
+                         device=q.device)
+        out = torch.full((M, H * d), float("nan"), device=q.device)
+        taf.attn_decode_gqa_batched(q, kc, vc, lens, out, M, H, Hkv, d, max_len, scale, ws, stream=stream)
+    return out
+
+
+def test_decode_deterministic_across_streams():
+    """The same decode on 12 streams, twice each: identical bits every time (fixed merge order)."""
+    import torch
+    M, H, Hkv, d, max_len = 9, 16, 4, 128, 3000
+    lens = [0, 1, 127, 128, 129, 700, 2999, 3000, 1500]
+    rng = np.random.default_rng(808)
+    q = to_dev(rng.standard_normal((M, H * d), dtype=np.float32))
+    kc = to_dev(rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32))
+    vc = to_dev(rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32))
+    scale = wl.scale_for(d)
+    note("decode determinism: 12 streams x 2 calls")
+    streams = [torch.cuda.Stream() for _ in range(12)]
+    outs = [_decode_on(s, q, kc, vc, lens, M, H, Hkv, d, max_len, scale) for s in streams for _ in range(2)]
+    torch.cuda.synchronize()
+    host = [bits(to_host(o)) for o in outs]
+    for i, h in enumerate(host[1:], 1):
+        assert np.array_equal(h, host[0]), f"call {i} (stream {i // 2}) differs from call 0"
+    want = oracle.default().decode(to_host(q), to_host(kc), to_host(vc), np.asarray(lens, np.int32), M, H, Hkv,
+                                   d, max_len, scale)
+    assert_attn_close(to_host(outs[0]), want, "decode on side streams vs oracle")
+
+
+def test_decode_many_kv_heads():
+    """32 sequences x 1024 KV heads (32768 head groups, 4-row caches)."""
+    M, H, Hkv, d, max_len = 32, 1024, 1024, 32, 4
+    rng = np.random.default_rng(809)
+    lens = rng.integers(0, max_len + 1, size=M).astype(np.int32)
+    q = rng.standard_normal((M, H * d), dtype=np.float32)
+    kc = rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32)
+    vc = rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32)
+    scale = wl.scale_for(d)
+    note("decode with 32768 head groups")
+    got = run_decode(to_dev(q), to_dev(kc), to_dev(vc), lens.tolist(), M, H, Hkv, d, max_len, scale)
+    want = oracle.default().decode(q, kc, vc, lens, M, H, Hkv, d, max_len, scale)
+    assert_attn_close(got, want, "decode 32768 groups")
+
+
+def test_decode_graph_replays_match_eager():
+    """A decode captured into a HIP graph replays to the eager result, bit for bit, over several
+    replays with new queries and eager decodes in between."""
+    import torch
+    M, H, Hkv, d, max_len = 6, 32, 8, 128, 2048
+    lens = [5, 2048, 0, 1000, 129, 64]
+    rng = np.random.default_rng(810)
+    kc = to_dev(rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32))
+    vc = to_dev(rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32))
+    scale = wl.scale_for(d)
+    note("decode graph capture and replays")
+    q_static = to_dev(rng.standard_normal((M, H * d), dtype=np.float32))
+    ws = torch.empty(taf.attn_decode_workspace_bytes(M, H, d, max_len) // 4, dtype=torch.float32, device="cuda:0")
+    out_static = torch.zeros((M, H * d), device="cuda:0")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up on the capture stream (first-call host queries)
+        taf.attn_decode_gqa_batched(q_static, kc, vc, lens, out_static, M, H, Hkv, d, max_len, scale, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        taf.attn_decode_gqa_batched(q_static, kc, vc, lens, out_static, M, H, Hkv, d, max_len, scale, ws)
+    for rep in range(4):
+        q_new = to_dev(rng.standard_normal((M, H * d), dtype=np.float32))
+        q_static.copy_(q_new)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = to_host(out_static)
+        eager = run_decode(q_new, kc, vc, lens, M, H, Hkv, d, max_len, scale)
+        assert np.array_equal(bits(got), bits(eager)), f"replay {rep} differs from the eager decode"
