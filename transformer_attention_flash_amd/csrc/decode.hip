@@ -18,12 +18,11 @@
 // output over its chunks; at the end the four waves merge theirs through LDS
 // into one split per key block, (m_s, l_s, acc_s), written to the workspace.
 //
-// Pass 2 (decode_combine_kernel): one workgroup per (m, h) merges the splits:
+// Pass 2 (decode_combine_kernel): one wave per (m, h) merges the splits:
 // with M* = max_s m_s and w_s = 2^(m_s - M*), out = sum_s w_s acc_s /
-// sum_s w_s l_s, or zeros when the sequence is empty.  Each of its 4 waves
-// folds every 4th split in with a running max (the same identity applied
-// incrementally) and the 4 results are merged in a fixed order, so the
-// result is the same on every run.
+// sum_s w_s l_s, or zeros when the sequence is empty, folded split by split in
+// split order with a running max (the same identity applied incrementally),
+// so the result is the same on every run.
 //
 // Register layouts of v_mfma_f32_16x16x4_f32 (lane l, i = l % 16, k = l / 16):
 // operand A supplies A[i][k], operand B supplies B[k][i], and output register
@@ -362,75 +361,46 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     }
 }
 
+// One wave per (m, h): folds the nkblk[m] splits in split order with a
+// running max (loads of 8 splits in flight together) and writes
+// out[m][h] = acc / l, or zeros for an empty sequence.
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a, UnitMap map) {
     constexpr int PER = D >= 64 ? D / 64 : 1;  // floats per lane
     constexpr int LANES = D / PER;             // lanes holding output columns
-    constexpr int BATCH = 8;                   // splits whose loads are in flight together
+    constexpr int BATCH = 8;
     typedef typename VecN<PER>::type pvec;
-    __shared__ __attribute__((aligned(16))) float part_acc[kWavesPerBlock][D];
-    __shared__ float part_m[kWavesPerBlock], part_l[kWavesPerBlock];
-
-    // One workgroup per (m, h), one split per key block; wave w merges splits
-    // w, w + 4, ... with a running max, then wave 0 merges the four results.
-    // The order is fixed, so the output is identical from run to run.
-    const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = blockIdx.x;
+    const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (w >= a.M * a.H) return;  // no barrier below
     const int m = w / a.H;
     const int nsplit = map.nkblk[m];
-    float *dst = a.out + (size_t)w * D;
-
-    if (nsplit == 0) {  // empty sequence: zeros (uniform over the block)
-        if (wave == 0 && lane < LANES) *reinterpret_cast<pvec *>(dst + PER * lane) = pvec{};
-        return;
-    }
     const size_t slot0 = (size_t)w * a.max_splits;
     const float *ml = a.ws_ml + 2 * slot0;
     const float *accp = a.ws_acc + slot0 * D + PER * lane;
-
     float m_run = kNegBig, l_run = 0.f;
     pvec acc{};
-    for (int s0 = wave; s0 < nsplit; s0 += kWavesPerBlock * BATCH) {
-        float mv[BATCH], lv[BATCH];
+    for (int s0 = 0; s0 < nsplit; s0 += BATCH) {
+        f32x2 mlv[BATCH];
         pvec av[BATCH];
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
-            const int s = s0 + kWavesPerBlock * b;
+            const int s = s0 + b;
             const bool ok = s < nsplit;
-            mv[b] = ok ? ml[2 * s] : kNegBig;
-            lv[b] = ok ? ml[2 * s + 1] : 0.f;
+            mlv[b] = ok ? *reinterpret_cast<const f32x2 *>(ml + 2 * s) : f32x2{kNegBig, 0.f};
             av[b] = (ok && lane < LANES) ? *reinterpret_cast<const pvec *>(accp + (size_t)s * D) : pvec{};
         }
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
-            const float m_new = fmaxf(m_run, mv[b]);
-            const float keep = fast_exp2(m_run - m_new), take = fast_exp2(mv[b] - m_new);
-            l_run = l_run * keep + lv[b] * take;
+            const float m_new = fmaxf(m_run, mlv[b][0]);
+            const float keep = fast_exp2(m_run - m_new), take = fast_exp2(mlv[b][0] - m_new);
+            l_run = l_run * keep + mlv[b][1] * take;
             acc = acc * keep + av[b] * take;
             m_run = m_new;
         }
     }
-    if (lane < LANES) *reinterpret_cast<pvec *>(&part_acc[wave][PER * lane]) = acc;
-    if (lane == 0) {
-        part_m[wave] = m_run;
-        part_l[wave] = l_run;
-    }
-    __syncthreads();
-    if (wave == 0 && lane < LANES) {
-        float mstar = part_m[0];
-#pragma unroll
-        for (int i = 1; i < kWavesPerBlock; ++i) mstar = fmaxf(mstar, part_m[i]);
-        pvec tot{};
-        float ltot = 0.f;
-#pragma unroll
-        for (int i = 0; i < kWavesPerBlock; ++i) {
-            const float wgt = fast_exp2(part_m[i] - mstar);
-            tot += wgt * *reinterpret_cast<const pvec *>(&part_acc[i][PER * lane]);
-            ltot += wgt * part_l[i];
-        }
-        *reinterpret_cast<pvec *>(dst + PER * lane) = tot * (1.0f / ltot);
-    }
+    if (lane < LANES)
+        *reinterpret_cast<pvec *>(a.out + (size_t)w * D + PER * lane) = nsplit > 0 ? acc * (1.0f / l_run) : pvec{};
 }
 
 constexpr int32_t kSpanQuantum = kWavesPerBlock * kChunk;  // keys: one chunk per wave
@@ -565,7 +535,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    dim3 grid2(a.M * a.H);
+    dim3 grid2((a.M * a.H + kWavesPerBlock - 1) / kWavesPerBlock);
     switch (a.D) {
         case 32: decode_combine_kernel<32><<<grid2, block, 0, stream>>>(a, map); break;
         case 64: decode_combine_kernel<64><<<grid2, block, 0, stream>>>(a, map); break;
