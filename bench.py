@@ -19,6 +19,11 @@ written) over the decode's measured time; the prefill's algorithmic TFLOP/s
 (visible query/key pairs only) is reported next to it and, being the longest
 kernel of the step, in the ``roofline`` object.
 
+Outside the step, each timed on its own: ``next_rows`` (chunked prefill behind
+a cache, rotary append and decode, reduced-precision prefill, slot copy) and
+``other_workloads`` (the 64-token and the 1500-token non-causal prefills and
+the short-context decode, M=32, H=32, Hkv=8, max_len=4096, L_m ~ U{1..4096}).
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -275,6 +280,7 @@ def main():
                             "traffic": measured_traffic("decode")},
         "cpu_baseline": None,
         "next_rows": None,
+        "other_workloads": None,
         "calibration": None,
     }
 
@@ -353,6 +359,40 @@ def main():
             "algorithmic_bytes": s_bytes}
         log(f"slot copy: {s_ms * 1e3:.1f} us ({s_gbs:.0f} GB/s)")
         del dk, dv
+
+        # The other workloads of the same calls, each timed on its own: the two
+        # small non-causal prefills and the short-context GQA decode step.
+        others = {}
+        for cid in (1, 2):
+            c = wl.PREFILL[cid]
+            oq, ok_, ov = (up(x) for x in wl.prefill_inputs(c))
+            oo = torch.empty_like(oq)
+            o_ms = time_call(torch, lambda: taf.attn_prefill(oq, ok_, ov, oo, c.B, c.S, c.H, c.d, c.scale, c.causal),
+                             fill)
+            o_tf = c.flops / (o_ms * 1e-3) / 1e12
+            others[c.name] = {"us": round(o_ms * 1e3, 2), "tflops": round(o_tf, 3),
+                              "frac_mfma": round(o_tf / FP32_MFMA_PEAK_TFLOPS, 4), "algorithmic_flops": c.flops}
+            log(f"prefill {c.name}: {o_ms * 1e3:.1f} us, {o_tf:.1f} TFLOP/s")
+            del oq, ok_, ov, oo
+        c4 = wl.DECODE[4]
+        d4 = wl.decode_inputs(c4)
+        l4 = d4["lens"]
+        q4, kn4, vn4, kc4, vc4 = (up(d4[n]) for n in ("q", "k_new", "v_new", "k_cache", "v_cache"))
+        out4 = torch.empty((c4.M, c4.H * c4.d), device=dev)
+        ws4 = torch.empty(taf.attn_decode_workspace_bytes(c4.M, c4.H, c4.d, c4.max_len) // 4, device=dev)
+        a4_ms = time_call(torch, lambda: taf.kv_cache_scatter(kn4, vn4, kc4, vc4, (l4 - 1).tolist(), c4.M, 1, c4.Hkv,
+                                                              c4.d, c4.max_len), fill)
+        d4_ms = time_call(torch, lambda: taf.attn_decode_gqa_batched(q4, kc4, vc4, l4.tolist(), out4, c4.M, c4.H,
+                                                                     c4.Hkv, c4.d, c4.max_len, c4.scale, ws4), fill)
+        d4_bytes = c4.decode_bytes(l4)
+        d4_gbs = d4_bytes / (d4_ms * 1e-3) / 1e9
+        others[c4.name] = {"decode_us": round(d4_ms * 1e3, 2), "gbs": round(d4_gbs, 2),
+                           "frac_hbm": round(d4_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": d4_bytes,
+                           "append_us": round(a4_ms * 1e3, 2), "sum_L": int(l4.sum())}
+        log(f"decode {c4.name}: {d4_ms * 1e3:.1f} us ({d4_gbs:.0f} GB/s), append {a4_ms * 1e3:.1f} us")
+        del q4, kn4, vn4, kc4, vc4, out4, ws4
+        others["note"] = "timed separately (10 calls after 5 warm-up calls each, queued behind a prefill)"
+        result["other_workloads"] = others
 
     if not args.no_next_rows:
         # Context for the roofline peaks, measured on this device with library
