@@ -108,7 +108,7 @@ def test_decode_step_full_size(cid):
     cfg = wl.DECODE[cid]
     inp = wl.decode_inputs(cfg)
     lens = inp["lens"]
-    note(f"decode step full size cfg{cid} sum(L)={int(lens.sum())}")
+    note(f"decode step full size {cfg.name} sum(L)={int(lens.sum())}")
     kc, vc = to_dev(inp["k_cache"]), to_dev(inp["v_cache"])
     taf.kv_cache_scatter(to_dev(inp["k_new"]), to_dev(inp["v_new"]), kc, vc, (lens - 1).tolist(),
                          cfg.M, 1, cfg.Hkv, cfg.d, cfg.max_len)
@@ -121,7 +121,7 @@ def test_decode_step_full_size(cid):
     orc.scatter(inp["k_new"], inp["v_new"], k_host, v_host, lens - 1, cfg.M, 1, cfg.Hkv, cfg.d, cfg.max_len)
     if cid == 4:
         want = orc.decode(inp["q"], k_host, v_host, lens, cfg.M, cfg.H, cfg.Hkv, cfg.d, cfg.max_len, cfg.scale)
-        assert_attn_close(got, want, "cfg4 decode (all heads)")
+        assert_attn_close(got, want, f"{cfg.name} (all heads)")
     else:
         # Every sequence, 8 heads each spread over the KV groups.
         g = cfg.H // cfg.Hkv
@@ -129,7 +129,7 @@ def test_decode_step_full_size(cid):
         want = orc.decode_rows(inp["q"], k_host, v_host, lens, sel, cfg.M, cfg.H, cfg.Hkv, cfg.d,
                                cfg.max_len, cfg.scale)
         got_sel = np.stack([got[m, h * cfg.d:(h + 1) * cfg.d] for m, h in sel])
-        assert_attn_close(got_sel, want, "cfg5 decode (sampled heads)")
+        assert_attn_close(got_sel, want, f"{cfg.name} (sampled heads)")
         assert np.all(np.isfinite(got))
 
 

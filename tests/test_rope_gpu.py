@@ -193,7 +193,7 @@ def test_decode_rope_step_full_size(cid, rot, theta):
     cfg = wl.DECODE[cid]
     inp = wl.decode_inputs(cfg)
     lens = inp["lens"]
-    note(f"decode_rope step full size cfg{cid} rot={rot} theta={theta} sum(L)={int(lens.sum())}")
+    note(f"decode_rope step full size {cfg.name} rot={rot} theta={theta} sum(L)={int(lens.sum())}")
     kc, vc = to_dev(inp["k_cache"]), to_dev(inp["v_cache"])
     taf.kv_cache_scatter_rope(to_dev(inp["k_new"]), to_dev(inp["v_new"]), kc, vc, (lens - 1).tolist(),
                               cfg.M, 1, cfg.Hkv, cfg.d, cfg.max_len, rot, theta)
@@ -212,12 +212,12 @@ def test_decode_rope_step_full_size(cid, rot, theta):
     q_rot = rotated_queries(orc, inp["q"], lens, cfg.H, cfg.d, rot, theta)
     if cid == 4:
         want = orc.decode(q_rot, k_host, v_host, lens, cfg.M, cfg.H, cfg.Hkv, cfg.d, cfg.max_len, cfg.scale)
-        assert_attn_close(got, want, "cfg4 decode_rope (all heads)")
+        assert_attn_close(got, want, f"{cfg.name} rotated (all heads)")
     else:
         g = cfg.H // cfg.Hkv
         sel = np.array([(m, kh * g + (m + 3 * kh) % g) for m in range(cfg.M) for kh in range(cfg.Hkv)], np.int64)
         want = orc.decode_rows(q_rot, k_host, v_host, lens, sel, cfg.M, cfg.H, cfg.Hkv, cfg.d, cfg.max_len,
                                cfg.scale)
         got_sel = np.stack([got[m, h * cfg.d:(h + 1) * cfg.d] for m, h in sel])
-        assert_attn_close(got_sel, want, "cfg5 decode_rope (sampled heads)")
+        assert_attn_close(got_sel, want, f"{cfg.name} rotated (sampled heads)")
         assert np.all(np.isfinite(got))
