@@ -208,22 +208,31 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
         // the SIMD's other wave (in its softmax or waiting) does not delay
         // them.
         __builtin_amdgcn_s_setprio(1);
-        // Four independent accumulation chains (one per k step c), summed
-        // afterwards: back-to-back dependent MFMAs issue more slowly (two
-        // chains gave +7%, four another +5%).
+        // Independent accumulation chains, summed afterwards: back-to-back
+        // dependent MFMAs issue more slowly (two chains gave +7%, four another
+        // +5% on the causal d = 128 prefill).  The non-causal d = 128 kernels
+        // keep two: four would spill there.
+        constexpr bool kFourChains = CAUSAL || D < 128;
         f32x16 s2 = f32x16{}, s3 = f32x16{}, s4 = f32x16{};
 #pragma unroll
         for (int j = 0; j < QV; ++j) {
             const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + 4 * ((2 * j + lk) ^ (li & SWZ)));
             s = mfma32(kv[0], qreg[j][0], s);
             s2 = mfma32(kv[1], qreg[j][1], s2);
-            s3 = mfma32(kv[2], qreg[j][2], s3);
-            s4 = mfma32(kv[3], qreg[j][3], s4);
+            if constexpr (kFourChains) {
+                s3 = mfma32(kv[2], qreg[j][2], s3);
+                s4 = mfma32(kv[3], qreg[j][3], s4);
+            } else {
+                s = mfma32(kv[2], qreg[j][2], s);
+                s2 = mfma32(kv[3], qreg[j][3], s2);
+            }
         }
         __builtin_amdgcn_s_setprio(0);
         s += s2;
-        s3 += s4;
-        s += s3;
+        if constexpr (kFourChains) {
+            s3 += s4;
+            s += s3;
+        }
 
         // Mask: keys past Sk, and (causal) keys after the query's position.
         const bool need_mask = (ks0 + 32 > Sk) || (CAUSAL && ks0 + 31 > P + qw0);
