@@ -256,13 +256,11 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
         Vt += grp * D * BN;
         const int kt0 = kt * BN;  // first key of the tile
         if (CAUSAL && kt0 > qw0 + 31) return;  // wave-uniform: whole tile above this wave's diagonal
-        // S^T = K Q^T for the NSUB 32-key sub-tiles at once: their MFMA chains
-        // are independent, so interleaving them keeps the matrix pipe busy.
-        // Lane supplies K[key 32 sub + li][16 kk + 8 lh .. +7].
-        // Lane supplies K[key 32 sub + li][16 kk + 8 lh .. +7].  One sub-tile:
-        // all its K operands are read from LDS before the MFMA chain starts, so
-        // the chain does not wait on an LDS round trip per step.  Two
-        // sub-tiles: their chains are independent and interleaved instead.
+        // S^T = K Q^T for the NSUB 32-key sub-tiles of the tile; lane supplies
+        // K[key 32 sub + li][16 kk + 8 lh .. +7].  One sub-tile: all its K
+        // operands are read from LDS before the MFMA chain starts, so the chain
+        // does not wait on an LDS round trip per step.  Two sub-tiles: their
+        // chains are independent and interleaved instead.
         f32x16 s[NSUB];
         if constexpr (NSUB == 1) {
             v8 kop[KK];
