@@ -54,11 +54,12 @@ def test_prefill_small(case, causal):
 
 DECOMPOSITIONS = [
     # B, S, H, d -> which work decomposition the launcher picks (B*H*ceil(S/128) and
-    # B*H*ceil(S/256) decide): small non-causal problems split each workgroup's keys
-    # over 4 groups (2 at d = 128); mid-size ones use 4 waves; large ones 8 waves.
-    (1, 1500, 8, 64),     # key split, KS = 4 (the Whisper-base shape)
+    # B*H*ceil(S/256) decide): small non-causal problems run 16-query waves in 4 key
+    # groups (d <= 64) or split 4-wave workgroups' keys over 2 groups (d = 128);
+    # mid-size ones use 4 waves; large ones 8 waves.
+    (1, 1500, 8, 64),     # 16-query waves, 48 queries per workgroup (the Whisper-base shape)
     (1, 700, 4, 128),     # key split, KS = 2, ragged tail
-    (3, 70, 5, 32),       # key split with fewer key tiles than groups in some workgroups
+    (3, 70, 5, 32),       # 16-query waves with fewer key tiles than groups
     (2, 1100, 16, 64),    # four waves (non-causal: 288 workgroups)
     (2, 1000, 64, 128),   # eight waves
 ]
@@ -79,6 +80,46 @@ def test_prefill_decompositions(case, causal):
     want = oracle.default().prefill_rows(q, k, v, sel, B, S, H, d, scale, causal)
     got_sel = np.stack([got[b, i, h * d:(h + 1) * d] for b, i, h in sel])
     assert_attn_close(got_sel, want, f"prefill decomposition {case} causal={causal}")
+
+
+SMALL_PROBLEMS = [
+    # B, S, H, d: non-causal, d <= 64 and B*H*ceil(S/128) < 256 run the 16-query-wave
+    # kernel; the launcher picks 16, 32, 48 or 64 queries per workgroup (QW = 1..4)
+    # so that the most loaded CU has the fewest queries (with 256 CUs: noted per case).
+    (1, 1, 3, 32),       # QW 1; one key, three of the four key groups empty
+    (1, 17, 2, 64),      # QW 1; one ragged key tile
+    (2, 33, 3, 32),      # QW 1; two key tiles
+    (1, 100, 5, 64),     # QW 1; four key tiles, ragged
+    (1, 600, 8, 64),     # QW 2
+    (2, 1000, 8, 64),    # QW 4
+    (1, 1500, 8, 32),    # QW 3 (the encoder shape at d = 32)
+    (3, 250, 2, 32),     # QW 1
+]
+
+
+@pytest.mark.parametrize("case", SMALL_PROBLEMS, ids=[f"B{c[0]}_S{c[1]}_H{c[2]}_d{c[3]}" for c in SMALL_PROBLEMS])
+def test_prefill_small_problems(case):
+    B, S, H, d = case
+    rng = np.random.default_rng(900 + S + H + d)
+    q, k, v = (rng.standard_normal((B, S, H * d), dtype=np.float32) for _ in range(3))
+    scale = wl.scale_for(d)
+    note(f"prefill small problem B={B} S={S} H={H} d={d}")
+    got = run_prefill(q, k, v, B, S, H, d, scale, False)
+    want = oracle.default().prefill(q, k, v, B, S, H, d, scale, False)
+    assert_attn_close(got, want, f"prefill small problem {case}")
+
+
+def test_prefill_small_problem_large_scores():
+    """Scores spanning a wide range (q scaled by 8, a negative scale) on the 16-query-wave kernel."""
+    B, S, H, d = 1, 777, 4, 64
+    rng = np.random.default_rng(901)
+    q = (rng.standard_normal((B, S, H * d), dtype=np.float32) * 8).astype(np.float32)
+    k, v = (rng.standard_normal((B, S, H * d), dtype=np.float32) for _ in range(2))
+    note("prefill small problem, large scores")
+    for scale in (0.25, -0.2):
+        got = run_prefill(q, k, v, B, S, H, d, scale, False)
+        want = oracle.default().prefill(q, k, v, B, S, H, d, scale, False)
+        assert_attn_close(got, want, f"prefill small problem large scores scale={scale}")
 
 
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])

@@ -14,7 +14,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["attn_api.hip", "scatter.hip", "decode.hip", "prefill.hip", "prefill_lowp.hip"]
+SOURCES = ["attn_api.hip", "scatter.hip", "decode.hip", "prefill.hip", "prefill_small.hip", "prefill_lowp.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are kept out of the generated code on purpose; the

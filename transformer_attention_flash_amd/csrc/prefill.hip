@@ -30,6 +30,8 @@
 // value its lane supplies at key step v of the output product, and each lane
 // holds one query column in both, which makes the row max/sum a reduction
 // over 16 registers plus one exchange with the partner half-wave.
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -348,6 +350,20 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
 // to split over eight waves).  A non-causal problem too small to give every CU
 // a four-wave workgroup instead splits each workgroup's keys over KS groups of
 // two query waves (64 queries per workgroup, KS = 4, or 2 at D = 128 for LDS).
+// Compute units of the current device, queried once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_cus[kMaxDevices];
+int32_t device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int32_t n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const int32_t BH = a.B * a.H;
@@ -363,6 +379,7 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     }
     if constexpr (!CAUSAL) {
         if (!a.cached && (int64_t)BH * tiles4 < 256) {
+            if constexpr (D <= 64) return launch_prefill_small(a, device_cus(), stream);
             constexpr int KS = D >= 128 ? 2 : 4;
             const int32_t tiles2 = (a.S + 63) / 64;
             dim3 grid((unsigned)(BH * tiles2));

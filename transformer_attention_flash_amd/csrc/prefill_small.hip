@@ -1,0 +1,382 @@
+// prefill_small.hip -- the non-causal prefill of problems too small to give
+// every CU a workgroup of the main kernel (head_dim 32 or 64), on 16-query
+// waves and v_mfma_f32_16x16x4_f32.
+//
+// Semantics: the attention of prefill.hip (trueno-gpu 0.4.11
+// src/memory/resident/attention.rs, `batched_multihead_attention`: per head,
+// softmax(scale Q K^T) V over the interleaved [B, S, H * D] rows, no mask);
+// this file only changes how the work is cut.
+//
+// Why: the time of a small problem is that of its most loaded CU.  With
+// 32-query waves a workgroup covers at least 32 queries of one head, so a
+// head of S = 1500 queries gives units of 32 (47 per head) or 64 (24 per
+// head): 8 heads make 376 or 192 units, i.e. two units on some of the 256
+// CUs, or 192 CUs busy.  16-query waves allow units of 16, 32, 48 or 64
+// queries; 48 gives 32 units per head, 256 in all, one per CU.
+//
+// Work decomposition: a workgroup owns BM = 16 QW queries of one (b, h) and
+// has QW query waves in each of 4 key groups; group g walks the g-th quarter
+// of the key tiles (32 keys each), its QW waves sharing every tile, and the
+// groups' partial softmax states are merged through LDS at the end.  K and V
+// tiles go from HBM straight into double-buffered LDS (global_load_lds), all
+// four groups' tiles moved by all the workgroup's waves, one barrier per tile.
+//
+// Register layouts of v_mfma_f32_16x16x4_f32 (lane l, i = l % 16, k = l / 16):
+// operand A supplies A[i][k], operand B supplies B[k][i], and output register
+// r holds D[4 k + r][i].  Scores are formed transposed, S^T = K Q^T (rows =
+// keys, columns = queries), with head dim (D / 4) k + j at step j, so each lane
+// reads its K row and holds its Q row as contiguous dims.  Output register r
+// of a 16-key score tile is then the operand-B value its lane supplies at step
+// r of O^T = V^T P^T (key 4 k + r), and row 4 k + r of output tile n stands
+// for dim NT (4 k + r) + n, so a lane's V operands for one step are NT
+// contiguous floats of one V row.
+#include "device_common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int SBN = 32;  // keys per LDS tile (two 16-key MFMA tiles)
+constexpr int SKS = 4;   // key groups per workgroup
+
+__device__ __forceinline__ f32x4 mfma16x4(float a, float b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// One 16-byte global -> LDS transfer per lane (global_load_lds_dwordx4): lane l's
+// 16 bytes land at lds_base + 16 l, lds_base being uniform over the wave.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void dma16_small(const float *src, float *lds_base) {
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), (lds_void_t *)lds_base, 16, 0, 0);
+}
+
+// Cross-lane reductions over the four lanes i, i + 16, i + 32, i + 48 that
+// hold one query's scores: a swizzle swaps the 16-lane halves of each 32-lane
+// group, and v_permlane32_swap returns, in every lane l, the values of lanes
+// l and l ^ 32 (one in each result), so combining its two results needs no
+// lane mask.
+__device__ __forceinline__ float xor16(float x) {
+    return __uint_as_float(__builtin_amdgcn_ds_swizzle(__float_as_uint(x), 0x401F));  // swap 16-lane halves
+}
+__device__ __forceinline__ float max4(float x) {
+    x = fmaxf(x, xor16(x));
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum4(float x) {
+    x += xor16(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Wait until this wave has no global loads (including LDS transfers) in flight.
+__device__ __forceinline__ void wait_vmem_all_small() {
+    // s_waitcnt vmcnt(0), expcnt/lgkmcnt unconstrained (7 and 15).
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+
+template <int D, int QW>
+__global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(PrefillArgs a, int32_t n_qtiles,
+                                                                          int32_t xcd_remap) {
+    constexpr int NWV = QW * SKS;         // waves per workgroup
+    constexpr int BM = 16 * QW;           // queries per workgroup
+    constexpr int KC = D / 4;             // 16-byte chunks per K/V row
+    constexpr int RPI = kWave / KC;       // rows moved by one wave-wide 1 KiB transfer
+    constexpr int PPT = SBN / RPI;        // transfers per tensor per group tile
+    constexpr int NPIECE = SKS * 2 * PPT; // transfers per workgroup per tile step
+    constexpr int SWZ = (KC < 16 ? KC : 16) - 1;  // K chunk swizzle mask
+    constexpr int NT = D / 16;            // 16-row tiles of O^T; floats per lane per V read
+    constexpr int QJ = D / 4;             // k steps of the score product
+    typedef typename VecN<NT>::type vrow_t;
+    static_assert(D == 32 || D == 64, "head_dim 32 or 64");
+    static_assert(RPI * KC == kWave && PPT * RPI == SBN, "tile transfers");
+
+    // Double-buffered K/V tiles: each buffer holds the four groups' K tiles
+    // (SBN x D each), then their V tiles.  K chunk c of row r sits at chunk
+    // position c ^ (r & SWZ), so the 16 rows of one score operand read fall
+    // in distinct banks; V rows are read whole by 16 lanes and are stored as
+    // they are.  The two buffers are separate objects, so the compiler sees
+    // that a transfer into one does not alias reads of the other.
+    __shared__ __attribute__((aligned(16))) float KV0[2 * SKS * SBN * D];
+    __shared__ __attribute__((aligned(16))) float KV1[2 * SKS * SBN * D];
+
+    // ---- block -> (b, h, query tile); with xcd_remap the query tiles of one
+    // (b, h) stay on one XCD (blocks are dealt to the 8 XCDs round-robin).
+    const int BH = a.B * a.H;
+    int bh, qt;
+    {
+        const int bid = blockIdx.x;
+        if (xcd_remap) {
+            const int per_xcd_bh = BH / 8;
+            const int x = bid % 8, t = bid / 8;
+            bh = 8 * (t % per_xcd_bh) + x;
+            qt = t / per_xcd_bh;
+        } else {
+            bh = bid % BH;
+            qt = bid / BH;
+        }
+    }
+    const int b = bh / a.H;
+    const int h = bh % a.H;
+    const int S = a.S;
+    const size_t row_stride = (size_t)a.H * D;
+    const size_t head_base = (size_t)b * S * row_stride + (size_t)h * D;
+    const float *__restrict__ qg = a.q + head_base;
+    const float *__restrict__ kg = a.k + head_base;
+    const float *__restrict__ vg = a.v + head_base;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int li = lane & 15;   // query column / key row within a 16 x 16 tile
+    const int lk = lane >> 4;   // k-slot of the MFMA operands
+    const int qwave = wave % QW;
+    const int grp = wave / QW;
+    const int my_q = qt * BM + 16 * qwave + li;
+
+    // ---- Q operand, pre-scaled so scores are in log2 units: lane supplies
+    // Q[my_q][(D / 4) lk + j] at step j.
+    const float qs = a.scale * kLog2e;
+    float qreg[QJ];
+    {
+        const bool ok = my_q < S;
+        const float *qp = qg + (size_t)(ok ? my_q : 0) * row_stride + QJ * lk;
+#pragma unroll
+        for (int jj = 0; jj < QJ / 4; ++jj) {
+            const f32x4 v4 = ok ? *reinterpret_cast<const f32x4 *>(qp + 4 * jj) : f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qreg[4 * jj + e] = v4[e] * qs;
+        }
+    }
+
+    f32x4 o[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[n] = f32x4{0, 0, 0, 0};
+    float m_run = kNegBig;
+    float l_run = 0.f;
+
+    const int n_ktiles = (S + SBN - 1) / SBN;
+    const int T = (n_ktiles + SKS - 1) / SKS;  // tile steps; group g owns tiles g T .. g T + T - 1
+    const int gt0 = grp * T;
+
+    // Tile step kt moves tile g T + kt of every group g that has one: the
+    // workgroup's waves share the NPIECE 1 KiB transfers, wave w taking pieces
+    // w, w + NWV, ...  A piece's lane addresses only move by whole tiles from
+    // step to step, so they are set up once: the lane's source in tile 0, its
+    // row within the tile, and the piece's group and LDS offset.  Keys past S
+    // read row S - 1 (in bounds); their scores are masked and their
+    // probabilities are exactly 0, so the values never matter.
+    constexpr int MAXP = (NPIECE + NWV - 1) / NWV;  // pieces per wave at most
+    const float *psrc[MAXP];
+    int prow[MAXP];
+    int pg[MAXP], pdst[MAXP];  // pg = SKS: no such piece
+#pragma unroll
+    for (int u = 0; u < MAXP; ++u) {
+        const int p = wave + NWV * u;
+        const int g = p / (2 * PPT);
+        const int is_v = (p / PPT) % 2;
+        const int pi = p % PPT;
+        const int row = pi * RPI + lane / KC;
+        const int chunk = lane % KC;
+        prow[u] = row;
+        pg[u] = p < NPIECE ? g : SKS;
+        pdst[u] = (is_v ? SKS * SBN * D : 0) + g * SBN * D + pi * kWave * 4;
+        psrc[u] = (is_v ? vg + 4 * chunk : kg + 4 * (chunk ^ (row & SWZ)));
+    }
+    auto issue_tile = [&](int kt, float *kv_dst) {
+#pragma unroll
+        for (int u = 0; u < MAXP; ++u) {
+            if (pg[u] >= SKS) continue;
+            const int tile = pg[u] * T + kt;
+            if (tile >= n_ktiles) continue;
+            const int key = min(tile * SBN + prow[u], S - 1);
+            dma16_small(psrc[u] + (size_t)key * row_stride, kv_dst + pdst[u]);
+        }
+    };
+
+    auto compute = [&](int kt, const float *Kt, const float *Vt) {
+        const int tile = gt0 + kt;
+        if (tile >= n_ktiles) return;  // this group's range is done (wave-uniform)
+        Kt += grp * SBN * D;
+        Vt += grp * SBN * D;
+        const int ks0 = tile * SBN;
+
+        // S^T for the tile's two 16-key halves (independent chains); all K
+        // operands are read before the chains start.
+        f32x4 kv[2][QJ / 4];
+#pragma unroll
+        for (int jj = 0; jj < QJ / 4; ++jj)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int row = 16 * t + li;
+                const int chunk = (QJ / 4) * lk + jj;
+                kv[t][jj] = *reinterpret_cast<const f32x4 *>(Kt + row * D + 4 * (chunk ^ (row & SWZ)));
+            }
+        f32x4 s[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int jj = 0; jj < QJ / 4; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) s[t] = mfma16x4(kv[t][jj][e], qreg[4 * jj + e], s[t]);
+        __builtin_amdgcn_s_setprio(0);
+
+        // Keys past S are masked (the last tile only).
+        if (ks0 + SBN > S) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (ks0 + 16 * t + 4 * lk + r >= S) s[t][r] = -INFINITY;
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[t][r]);
+        mx = max4(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s[t][r] = fast_exp2(s[t][r] - m_new);
+                psum += s[t][r];
+            }
+        l_run = l_run * alpha + psum;
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) o[n] *= alpha;
+        }
+
+        // O^T += V^T P^T: step (t, r) is key 16 t + 4 lk + r for this lane.
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const vrow_t vv = *reinterpret_cast<const vrow_t *>(Vt + (16 * t + 4 * lk + r) * D + NT * li);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) o[n] = mfma16x4(vget<NT>(vv, n), s[t][r], o[n]);
+            }
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    // One barrier per tile step: after it every wave's share of step kt has
+    // landed and every wave is done with step kt - 1, whose buffer takes step
+    // kt + 1 while step kt is consumed.
+    auto step = [&](int kt, const float *KVt, float *KVn) {
+        wait_vmem_all_small();
+        __syncthreads();
+        if (kt + 1 < T) issue_tile(kt + 1, KVn);
+        compute(kt, KVt, KVt + SKS * SBN * D);
+    };
+
+    issue_tile(0, KV0);
+    for (int kt = 0; kt < T; kt += 2) {
+        step(kt, KV0, KV1);
+        if (kt + 1 < T) step(kt + 1, KV1, KV0);
+    }
+
+    // ---- merge the key groups: groups 1.. park (max, partial sum, output) of
+    // each lane in LDS, group 0 folds them in with the usual rescaling.  No
+    // transfer is in flight: the last step issued none.
+    {
+        constexpr int SLOT = kWave * (4 * NT + 2);  // floats per parked wave
+        static_assert((SKS - 1) * QW * SLOT <= 2 * SKS * SBN * D, "LDS too small to merge the key groups");
+        auto slot_ptr = [&](int sl) -> float * { return KV0 + sl * SLOT; };
+        __syncthreads();  // every wave is done with the K/V tiles
+        if (grp > 0) {
+            float *dst = slot_ptr((grp - 1) * QW + qwave) + lane;
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[(4 * n + r) * kWave] = o[n][r];
+            dst[4 * NT * kWave] = m_run;
+            dst[(4 * NT + 1) * kWave] = l_run;
+        }
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll
+        for (int g = 1; g < SKS; ++g) {
+            const float *src = slot_ptr((g - 1) * QW + qwave) + lane;
+            const float m_g = src[4 * NT * kWave];
+            const float m_new = fmaxf(m_run, m_g);
+            const float keep = fast_exp2(m_run - m_new), take = fast_exp2(m_g - m_new);
+            l_run = l_run * keep + src[(4 * NT + 1) * kWave] * take;
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[n][r] = o[n][r] * keep + src[(4 * n + r) * kWave] * take;
+            m_run = m_new;
+        }
+    }
+
+    // ---- normalise and store: lane holds query my_q, dims NT (4 lk + r) + n.
+    l_run = sum4(l_run);
+    if (my_q < S) {
+        const float inv = 1.0f / l_run;
+        float *op = a.out + head_base + (size_t)my_q * row_stride;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            vrow_t val;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) vset<NT>(val, n, o[n][r] * inv);
+            *reinterpret_cast<vrow_t *>(op + NT * (4 * lk + r)) = val;
+        }
+    }
+}
+
+template <int D, int QW>
+hipError_t launch_qw(const PrefillArgs &a, hipStream_t stream) {
+    const int32_t BH = a.B * a.H;
+    const int32_t tiles = (a.S + 16 * QW - 1) / (16 * QW);
+    const int32_t xcd_remap = (BH % 8 == 0) ? 1 : 0;
+    dim3 grid((unsigned)(BH * tiles));
+    prefill_small_kernel<D, QW><<<grid, dim3(kWave * QW * SKS), 0, stream>>>(a, tiles, xcd_remap);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const PrefillArgs &a, int32_t qw, hipStream_t stream) {
+    switch (qw) {
+        case 1: return launch_qw<D, 1>(a, stream);
+        case 2: return launch_qw<D, 2>(a, stream);
+        case 3: return launch_qw<D, 3>(a, stream);
+        default: return launch_qw<D, 4>(a, stream);
+    }
+}
+
+}  // namespace
+
+int32_t prefill_small_qw(int32_t BH, int32_t S, int32_t cus) {
+    // Queries per workgroup 16 QW: the cut whose most loaded CU (one
+    // workgroup per CU at a time) has the fewest queries; ties go to fewer,
+    // larger workgroups.
+    int32_t best = 4;
+    int64_t best_cost = -1;
+    for (int32_t qw = 4; qw >= 1; --qw) {
+        const int64_t grid = (int64_t)BH * ((S + 16 * qw - 1) / (16 * qw));
+        const int64_t cost = (grid + cus - 1) / cus * qw;
+        if (best_cost < 0 || cost < best_cost) {
+            best = qw;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+hipError_t launch_prefill_small(const PrefillArgs &a, int32_t cus, hipStream_t stream) {
+    const int32_t qw = prefill_small_qw(a.B * a.H, a.S, cus);
+    switch (a.D) {
+        case 32: return launch_d<32>(a, qw, stream);
+        case 64: return launch_d<64>(a, qw, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace attn
