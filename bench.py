@@ -116,6 +116,62 @@ def cpu_baseline(inp, cfg, target_s):
     }
 
 
+def oracle_timings(wl, gpu_us, prefill3_inputs):
+    """The oracle on each workload of the calls (one wall-clock run each; the
+    64- and 1500-token prefills also on one thread), with its speedup of the GPU
+    figure measured in the same run.  Large workloads run a sample: the causal
+    prefill a set of query rows, the long-context decode (the ``cpu_baseline``
+    object) a bounded number of sequences.
+    """
+    import oracle
+
+    orc = oracle.default()
+    threads = orc.num_threads()
+    out = {"threads": threads}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    for cid in (1, 2):
+        c = wl.PREFILL[cid]
+        q, k, v = wl.prefill_inputs(c)
+        run = lambda: orc.prefill(q, k, v, c.B, c.S, c.H, c.d, c.scale, c.causal)
+        t_all = timed(run)
+        orc.set_num_threads(1)
+        t_one = timed(run)
+        orc.set_num_threads(threads)
+        out[c.name] = {"gflops": round(c.flops / t_all / 1e9, 3), "s": round(t_all, 3),
+                       "gflops_1thread": round(c.flops / t_one / 1e9, 3), "s_1thread": round(t_one, 3),
+                       "gpu_speedup": round(t_all / (gpu_us[c.name] * 1e-6), 1)}
+    c3 = wl.PREFILL[3]
+    q, k, v = prefill3_inputs
+    rows = np.arange(0, c3.S, 64)  # every 64th query, every batch element and head
+    sel = np.array([(b, i, h) for b in range(c3.B) for i in rows for h in range(c3.H)], np.int64)
+    t3 = timed(lambda: orc.prefill_rows(q, k, v, sel, c3.B, c3.S, c3.H, c3.d, c3.scale, True))
+    f3 = int(sum(4 * c3.d * (int(i) + 1) for _, i, _ in sel))
+    out[c3.name] = {"gflops": round(f3 / t3 / 1e9, 3), "s": round(t3, 3),
+                    "sample": f"query rows 0, 64, ..., {int(rows[-1])} of every (b, h): {len(sel)} rows",
+                    "gpu_speedup": round((c3.flops / (gpu_us[c3.name] * 1e-6)) / (f3 / t3), 1)}
+    sc = wl.BULK_SCATTER
+    kc = wl.sentinel_cache((sc.M, sc.Hkv, sc.max_len, sc.d))
+    vc = kc.copy()
+    ts = timed(lambda: orc.scatter(k, v, kc, vc, np.zeros(sc.M, np.int32), sc.M, sc.n_new, sc.Hkv, sc.d,
+                                   sc.max_len))
+    out[sc.name] = {"gbs": round(sc.bytes / ts / 1e9, 3), "s": round(ts, 3),
+                    "gpu_speedup": round(ts / (gpu_us[sc.name] * 1e-6), 1)}
+    del kc, vc
+    c4 = wl.DECODE[4]
+    d4 = wl.decode_inputs(c4)
+    t4 = timed(lambda: orc.decode(d4["q"], d4["k_cache"], d4["v_cache"], d4["lens"], c4.M, c4.H, c4.Hkv, c4.d,
+                                  c4.max_len, c4.scale))
+    b4 = c4.decode_bytes(d4["lens"])
+    out[c4.name] = {"gbs": round(b4 / t4 / 1e9, 3), "s": round(t4, 3),
+                    "gpu_speedup": round(t4 / (gpu_us[c4.name] * 1e-6), 1)}
+    return out
+
+
 def time_call(torch, run, filler=None, warm=5, reps=10):
     """Mean milliseconds of `run` over `reps` calls, each bracketed by events on the current stream.
 
@@ -279,6 +335,7 @@ def main():
                             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic("decode")},
         "cpu_baseline": None,
+        "oracle_timings": None,
         "next_rows": None,
         "other_workloads": None,
         "calibration": None,
@@ -416,6 +473,13 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the decode workload ...")
         result["cpu_baseline"] = cpu_baseline(dinp, dcfg, args.cpu_seconds)
+        if result["other_workloads"] is not None:
+            ow = result["other_workloads"]
+            gpu_us = {wl.PREFILL[1].name: ow[wl.PREFILL[1].name]["us"], wl.PREFILL[2].name: ow[wl.PREFILL[2].name]["us"],
+                      pcfg.name: result["prefill"]["us"], scfg.name: result["bulk_scatter"]["us"],
+                      wl.DECODE[4].name: ow[wl.DECODE[4].name]["decode_us"]}
+            log("timing the CPU oracle on the other workloads ...")
+            result["oracle_timings"] = oracle_timings(wl, gpu_us, (q, k, v))
     print(json.dumps(result), flush=True)
 
 

@@ -78,6 +78,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_rope.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     return lib
 
 
@@ -250,6 +252,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        """Threads of the following calls (timing only; results do not depend on it)."""
+        self.lib.oracle_set_num_threads(int(n))
 
 
 _default: Oracle | None = None

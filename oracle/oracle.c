@@ -463,6 +463,19 @@ int oracle_prefill_lowp(const float *q, const float *k, const float *v, double *
     return rc;
 }
 
+/* Threads for the following parallel regions (timing only: results do not
+   depend on it, every output element is computed by one thread in the same
+   order).  n <= 0 leaves the setting as it is. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Number of OpenMP threads a parallel region would use (for reporting). */
 int oracle_num_threads(void)
 {
