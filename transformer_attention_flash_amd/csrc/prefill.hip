@@ -16,11 +16,14 @@
 // the max grows) walks the key axis tile by tile.
 //
 // Work decomposition: a workgroup owns BM = 32 NW queries of one (b, h) (NW =
-// 8 waves, or 4 for small problems); each wavefront owns 32 of them and keeps
-// its Q slice in VGPRs and its 32 x D output accumulator in registers.  K and V tiles of BN = 32 keys go
-// from HBM straight into a double-buffered LDS tile (global_load_lds, no
-// register staging); the next tile's transfer is in flight while the current
-// one is consumed, with one workgroup barrier per tile.  Both products run on v_mfma_f32_32x32x2_f32.
+// 8 waves, or 4 for smaller problems); each wavefront owns 32 of them and
+// keeps its Q slice in VGPRs and its 32 x D output accumulator in registers.
+// K and V tiles of BN = 32 keys go from HBM straight into a double-buffered
+// LDS tile (global_load_lds, no register staging); the next tile's transfer is
+// in flight while the current one is consumed, with one workgroup barrier per
+// tile.  Both products run on v_mfma_f32_32x32x2_f32.  (Non-causal problems
+// too small to fill the CUs with these workgroups run prefill_small.hip at
+// D <= 64, and a key split of this kernel at D = 128; see launch_typed.)
 //
 // Register layouts of v_mfma_f32_32x32x2_f32 (lane l, i = l % 32, k = l / 32):
 // operand A supplies A[i][k], operand B supplies B[k][i], and output register
@@ -63,8 +66,8 @@ __device__ __forceinline__ void wait_vmem_all() {
 
 // NW waves in KS groups: the NW / KS waves of a group own 32 queries each
 // (BM = 32 NW / KS queries per workgroup), and group g walks the g-th of KS
-// contiguous ranges of the key tiles; KS > 1 (small non-causal problems only)
-// merges the groups' partial softmax states at the end.
+// contiguous ranges of the key tiles; KS > 1 (small non-causal problems at
+// D = 128 only) merges the groups' partial softmax states at the end.
 template <int D, int NW, int KS, bool CAUSAL>
 __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs a, int32_t n_qtiles,
                                                                      int32_t xcd_remap) {
@@ -343,13 +346,6 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
     }
 }
 
-// Eight waves (256 queries) per workgroup halve the K/V tile transfers per
-// query; four waves keep small problems spread over the CUs.  One eight-wave
-// workgroup fills a CU, so eight waves are used when that still gives at least
-// two workgroups per CU (and D >= 64: a 32-key tile of D = 32 rows is too small
-// to split over eight waves).  A non-causal problem too small to give every CU
-// a four-wave workgroup instead splits each workgroup's keys over KS groups of
-// two query waves (64 queries per workgroup, KS = 4, or 2 at D = 128 for LDS).
 // Compute units of the current device, queried once per device.
 constexpr int kMaxDevices = 64;
 std::atomic<int32_t> g_cus[kMaxDevices];
@@ -364,6 +360,14 @@ int32_t device_cus() {
     return cus;
 }
 
+// Eight waves (256 queries) per workgroup halve the K/V tile transfers per
+// query; four waves keep small problems spread over the CUs.  One eight-wave
+// workgroup fills a CU, so eight waves are used when that still gives at least
+// two workgroups per CU (and D >= 64: a 32-key tile of D = 32 rows is too small
+// to split over eight waves).  A non-causal problem too small to give every CU
+// a four-wave workgroup runs on 16-query waves (prefill_small.hip) at D <= 64;
+// at D = 128 it splits each workgroup's keys over 2 groups of two query waves
+// (64 queries per workgroup).
 template <int D, bool CAUSAL>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const int32_t BH = a.B * a.H;
@@ -379,12 +383,14 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     }
     if constexpr (!CAUSAL) {
         if (!a.cached && (int64_t)BH * tiles4 < 256) {
-            if constexpr (D <= 64) return launch_prefill_small(a, device_cus(), stream);
-            constexpr int KS = D >= 128 ? 2 : 4;
-            const int32_t tiles2 = (a.S + 63) / 64;
-            dim3 grid((unsigned)(BH * tiles2));
-            prefill_kernel<D, 2 * KS, KS, false><<<grid, dim3(kWave * 2 * KS), 0, stream>>>(a, tiles2, xcd_remap);
-            return hipGetLastError();
+            if constexpr (D <= 64) {
+                return launch_prefill_small(a, device_cus(), stream);
+            } else {
+                const int32_t tiles2 = (a.S + 63) / 64;
+                dim3 grid((unsigned)(BH * tiles2));
+                prefill_kernel<D, 4, 2, false><<<grid, dim3(kWave * 4), 0, stream>>>(a, tiles2, xcd_remap);
+                return hipGetLastError();
+            }
         }
     }
     dim3 grid((unsigned)(BH * tiles4));
