@@ -109,6 +109,40 @@ def test_prefill_small_problems(case):
     assert_attn_close(got, want, f"prefill small problem {case}")
 
 
+SMALL_CAUSAL = [
+    # B, S, H, d, rows checked (None: all): causal small problems on the 16-query-wave
+    # kernel; the launcher simulates the heavy-first dispatch to pick QW (with 256 CUs:
+    # noted per case)
+    (1, 17, 2, 64, None),      # QW 1, one ragged key tile
+    (2, 33, 3, 32, None),      # QW 1
+    (1, 1500, 8, 32, None),    # QW 1
+    (1, 1500, 8, 64, None),    # QW 2
+    (1, 3000, 6, 64, "sampled"),   # QW 3
+    (1, 32640, 1, 64, "sampled"),  # QW 4 (255 query tiles of 128 on one head)
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CAUSAL, ids=[f"B{c[0]}_S{c[1]}_H{c[2]}_d{c[3]}" for c in SMALL_CAUSAL])
+def test_prefill_small_problems_causal(case):
+    B, S, H, d, rows = case
+    rng = np.random.default_rng(950 + S + H + d)
+    q, k, v = (rng.standard_normal((B, S, H * d), dtype=np.float32) for _ in range(3))
+    scale = wl.scale_for(d)
+    note(f"prefill small causal problem B={B} S={S} H={H} d={d}")
+    got = run_prefill(q, k, v, B, S, H, d, scale, True)
+    assert np.all(np.isfinite(got)), "every output element is written"
+    orc = oracle.default()
+    if rows is None:
+        assert_attn_close(got, orc.prefill(q, k, v, B, S, H, d, scale, True), f"prefill small causal {case}")
+        return
+    picks = sorted({0, 1, 15, 16, 17, 31, 32, 47, 48, 63, 64, S // 3, S // 2, S - 49, S - 48, S - 17, S - 16, S - 1}
+                   | set(rng.integers(0, S, 16).tolist()))
+    sel = np.array([(b, i, h) for b in range(B) for i in picks for h in range(H)], np.int64)
+    want = orc.prefill_rows(q, k, v, sel, B, S, H, d, scale, True)
+    got_sel = np.stack([got[b, i, h * d:(h + 1) * d] for b, i, h in sel])
+    assert_attn_close(got_sel, want, f"prefill small causal {case} (sampled rows)")
+
+
 def test_prefill_small_problem_large_scores():
     """Scores spanning a wide range (q scaled by 8, a negative scale) on the 16-query-wave kernel."""
     B, S, H, d = 1, 777, 4, 64

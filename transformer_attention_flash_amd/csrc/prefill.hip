@@ -381,10 +381,13 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
             return hipGetLastError();
         }
     }
+    if constexpr (D <= 64) {
+        if (!a.cached && (int64_t)BH * tiles4 < 256) return launch_prefill_small(a, device_cus(), stream);
+    }
     if constexpr (!CAUSAL) {
         if (!a.cached && (int64_t)BH * tiles4 < 256) {
             if constexpr (D <= 64) {
-                return launch_prefill_small(a, device_cus(), stream);
+                return hipErrorInvalidValue;  // taken above
             } else {
                 const int32_t tiles2 = (a.S + 63) / 64;
                 dim3 grid((unsigned)(BH * tiles2));

@@ -1,11 +1,13 @@
-// prefill_small.hip -- the non-causal prefill of problems too small to give
-// every CU a workgroup of the main kernel (head_dim 32 or 64), on 16-query
-// waves and v_mfma_f32_16x16x4_f32.
+// prefill_small.hip -- the prefill of problems too small to give every CU a
+// workgroup of the main kernel (head_dim 32 or 64), on 16-query waves and
+// v_mfma_f32_16x16x4_f32.
 //
 // Semantics: the attention of prefill.hip (trueno-gpu 0.4.11
 // src/memory/resident/attention.rs, `batched_multihead_attention`: per head,
-// softmax(scale Q K^T) V over the interleaved [B, S, H * D] rows, no mask);
-// this file only changes how the work is cut.
+// softmax(scale Q K^T) V over the interleaved [B, S, H * D] rows; with the
+// causal mask of trustformers-core 0.2.0 src/gpu_ops/cuda/oxicuda/attention.rs,
+// `attention_prefill_gpu_to_gpu`: query i sees keys 0..=i); this file only
+// changes how the work is cut.
 //
 // Why: the time of a small problem is that of its most loaded CU.  With
 // 32-query waves a workgroup covers at least 32 queries of one head, so a
@@ -16,8 +18,11 @@
 //
 // Work decomposition: a workgroup owns BM = 16 QW queries of one (b, h) and
 // has QW query waves in each of 4 key groups; group g walks the g-th quarter
-// of the key tiles (32 keys each), its QW waves sharing every tile, and the
-// groups' partial softmax states are merged through LDS at the end.  K and V
+// of the key tiles (32 keys each) the workgroup's queries can see, its QW
+// waves sharing every tile, and the groups' partial softmax states are merged
+// through LDS at the end.  With the causal mask, a wave skips the tiles wholly
+// above its diagonal, the diagonal tile is masked per element, and the
+// workgroups with the most visible keys are dispatched first.  K and V
 // tiles go from HBM straight into double-buffered LDS (global_load_lds), all
 // four groups' tiles moved by all the workgroup's waves, one barrier per tile.
 //
@@ -30,6 +35,13 @@
 // r of O^T = V^T P^T (key 4 k + r), and row 4 k + r of output tile n stands
 // for dim NT (4 k + r) + n, so a lane's V operands for one step are NT
 // contiguous floats of one V row.
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <queue>
+#include <tuple>
+#include <vector>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -75,7 +87,7 @@ __device__ __forceinline__ void wait_vmem_all_small() {
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
-template <int D, int QW>
+template <int D, int QW, bool CAUSAL>
 __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(PrefillArgs a, int32_t n_qtiles,
                                                                           int32_t xcd_remap) {
     constexpr int NWV = QW * SKS;         // waves per workgroup
@@ -100,21 +112,24 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
     __shared__ __attribute__((aligned(16))) float KV0[2 * SKS * SBN * D];
     __shared__ __attribute__((aligned(16))) float KV1[2 * SKS * SBN * D];
 
-    // ---- block -> (b, h, query tile); with xcd_remap the query tiles of one
-    // (b, h) stay on one XCD (blocks are dealt to the 8 XCDs round-robin).
+    // ---- block -> (b, h, query tile); heavy causal tiles first, and with
+    // xcd_remap the query tiles of one (b, h) stay on one XCD (blocks are
+    // dealt to the 8 XCDs round-robin).
     const int BH = a.B * a.H;
     int bh, qt;
     {
         const int bid = blockIdx.x;
+        int rank;
         if (xcd_remap) {
             const int per_xcd_bh = BH / 8;
             const int x = bid % 8, t = bid / 8;
             bh = 8 * (t % per_xcd_bh) + x;
-            qt = t / per_xcd_bh;
+            rank = t / per_xcd_bh;
         } else {
             bh = bid % BH;
-            qt = bid / BH;
+            rank = bid / BH;
         }
+        qt = CAUSAL ? n_qtiles - 1 - rank : rank;
     }
     const int b = bh / a.H;
     const int h = bh % a.H;
@@ -132,7 +147,9 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
     const int lk = lane >> 4;   // k-slot of the MFMA operands
     const int qwave = wave % QW;
     const int grp = wave / QW;
-    const int my_q = qt * BM + 16 * qwave + li;
+    const int q0 = qt * BM;               // the workgroup's first query
+    const int qw0 = q0 + 16 * qwave;      // this wave's first query
+    const int my_q = qw0 + li;
 
     // ---- Q operand, pre-scaled so scores are in log2 units: lane supplies
     // Q[my_q][(D / 4) lk + j] at step j.
@@ -155,7 +172,8 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
     float m_run = kNegBig;
     float l_run = 0.f;
 
-    const int n_ktiles = (S + SBN - 1) / SBN;
+    const int n_ktiles_all = (S + SBN - 1) / SBN;
+    const int n_ktiles = CAUSAL ? min(n_ktiles_all, (min(q0 + BM, S) - 1) / SBN + 1) : n_ktiles_all;
     const int T = (n_ktiles + SKS - 1) / SKS;  // tile steps; group g owns tiles g T .. g T + T - 1
     const int gt0 = grp * T;
 
@@ -197,6 +215,7 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
     auto compute = [&](int kt, const float *Kt, const float *Vt) {
         const int tile = gt0 + kt;
         if (tile >= n_ktiles) return;  // this group's range is done (wave-uniform)
+        if (CAUSAL && tile * SBN > qw0 + 15) return;  // whole tile above this wave's diagonal
         Kt += grp * SBN * D;
         Vt += grp * SBN * D;
         const int ks0 = tile * SBN;
@@ -222,13 +241,17 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
                 for (int t = 0; t < 2; ++t) s[t] = mfma16x4(kv[t][jj][e], qreg[4 * jj + e], s[t]);
         __builtin_amdgcn_s_setprio(0);
 
-        // Keys past S are masked (the last tile only).
-        if (ks0 + SBN > S) {
+        // Keys past S (the last tile) and, causal, keys after the query's
+        // position are masked.  A lane whose keys are all masked keeps its
+        // state: the running max stays put (finite) and the probabilities are 0.
+        if (ks0 + SBN > S || (CAUSAL && ks0 + SBN - 1 > qw0)) {
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (ks0 + 16 * t + 4 * lk + r >= S) s[t][r] = -INFINITY;
+                for (int r = 0; r < 4; ++r) {
+                    const int key = ks0 + 16 * t + 4 * lk + r;
+                    if (key >= S || (CAUSAL && key > my_q)) s[t][r] = -INFINITY;
+                }
         }
         float mx = s[0][0];
 #pragma unroll
@@ -336,8 +359,11 @@ hipError_t launch_qw(const PrefillArgs &a, hipStream_t stream) {
     const int32_t BH = a.B * a.H;
     const int32_t tiles = (a.S + 16 * QW - 1) / (16 * QW);
     const int32_t xcd_remap = (BH % 8 == 0) ? 1 : 0;
-    dim3 grid((unsigned)(BH * tiles));
-    prefill_small_kernel<D, QW><<<grid, dim3(kWave * QW * SKS), 0, stream>>>(a, tiles, xcd_remap);
+    dim3 grid((unsigned)(BH * tiles)), block(kWave * QW * SKS);
+    if (a.causal)
+        prefill_small_kernel<D, QW, true><<<grid, block, 0, stream>>>(a, tiles, xcd_remap);
+    else
+        prefill_small_kernel<D, QW, false><<<grid, block, 0, stream>>>(a, tiles, xcd_remap);
     return hipGetLastError();
 }
 
@@ -353,10 +379,66 @@ hipError_t launch_d(const PrefillArgs &a, int32_t qw, hipStream_t stream) {
 
 }  // namespace
 
+namespace {
+
+// Causal: the work of a query tile grows with its position, so the cut is
+// chosen by simulating the dispatch: workgroups in launch order (heaviest
+// first) each go to the slot that frees first, at a speed set by the waves a
+// SIMD holds (one workgroup of 4 QW waves per CU at d = 64, two at d = 32 for
+// LDS), and the cut with the earliest end wins.  The speed factors per waves
+// per SIMD (1: 0.3, 2: 0.6, 3: 0.8, 4: 1) pick the fastest cut on every shape
+// timed (S 448..2000, 6..32 heads, d 32 and 64).  Results are cached per shape.
+int32_t causal_qw(int32_t BH, int32_t S, int32_t D, int32_t cus) {
+    static const double kSpeed[5] = {0.0, 0.3, 0.6, 0.8, 1.0};
+    const int32_t per_cu = D == 32 ? 2 : 1;
+    int32_t best = 1;
+    double best_end = -1.0;
+    for (int32_t qw = 1; qw <= 4; ++qw) {
+        const int64_t bm = 16 * qw;
+        const int64_t n = (S + bm - 1) / bm;
+        const double speed = kSpeed[std::min<int32_t>(4, qw * per_cu)] / per_cu;
+        std::priority_queue<double, std::vector<double>, std::greater<double>> slots;
+        for (int32_t i = 0; i < cus * per_cu; ++i) slots.push(0.0);
+        double end = 0.0;
+        for (int64_t qt = n - 1; qt >= 0; --qt) {
+            const double work = (double)(bm * std::min<int64_t>((qt + 1) * bm, S)) / speed;
+            for (int32_t h = 0; h < BH; ++h) {
+                const double t = slots.top() + work;
+                slots.pop();
+                slots.push(t);
+                end = std::max(end, t);
+            }
+        }
+        if (best_end < 0 || end < best_end) {
+            best = qw;
+            best_end = end;
+        }
+    }
+    return best;
+}
+
+std::mutex g_causal_mu;
+std::map<std::tuple<int32_t, int32_t, int32_t, int32_t>, int32_t> g_causal_qw;
+
+}  // namespace
+
+int32_t prefill_small_qw_causal(int32_t BH, int32_t S, int32_t D, int32_t cus) {
+    const auto key = std::make_tuple(BH, S, D, cus);
+    {
+        std::lock_guard<std::mutex> lock(g_causal_mu);
+        const auto it = g_causal_qw.find(key);
+        if (it != g_causal_qw.end()) return it->second;
+    }
+    const int32_t qw = causal_qw(BH, S, D, cus);
+    std::lock_guard<std::mutex> lock(g_causal_mu);
+    if (g_causal_qw.size() < 4096) g_causal_qw[key] = qw;
+    return qw;
+}
+
 int32_t prefill_small_qw(int32_t BH, int32_t S, int32_t cus) {
-    // Queries per workgroup 16 QW: the cut whose most loaded CU (one
-    // workgroup per CU at a time) has the fewest queries; ties go to fewer,
-    // larger workgroups.
+    // Non-causal: queries per workgroup 16 QW, the cut whose most loaded CU
+    // (one workgroup per CU at a time) has the fewest queries; ties go to
+    // fewer, larger workgroups.
     int32_t best = 4;
     int64_t best_cost = -1;
     for (int32_t qw = 4; qw >= 1; --qw) {
@@ -371,7 +453,8 @@ int32_t prefill_small_qw(int32_t BH, int32_t S, int32_t cus) {
 }
 
 hipError_t launch_prefill_small(const PrefillArgs &a, int32_t cus, hipStream_t stream) {
-    const int32_t qw = prefill_small_qw(a.B * a.H, a.S, cus);
+    const int32_t qw = a.causal ? prefill_small_qw_causal(a.B * a.H, a.S, a.D, cus)
+                                : prefill_small_qw(a.B * a.H, a.S, cus);
     switch (a.D) {
         case 32: return launch_d<32>(a, qw, stream);
         case 64: return launch_d<64>(a, qw, stream);
