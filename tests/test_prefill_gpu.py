@@ -54,11 +54,10 @@ def test_prefill_small(case, causal):
 
 DECOMPOSITIONS = [
     # B, S, H, d -> which work decomposition the launcher picks (B*H*ceil(S/128) and
-    # B*H*ceil(S/256) decide): small non-causal problems run 16-query waves in 4 key
-    # groups (d <= 64) or split 4-wave workgroups' keys over 2 groups (d = 128);
+    # B*H*ceil(S/256) decide): small problems run 16-query waves in 4 key groups;
     # mid-size ones use 4 waves; large ones 8 waves.
     (1, 1500, 8, 64),     # 16-query waves, 48 queries per workgroup (the Whisper-base shape)
-    (1, 700, 4, 128),     # key split, KS = 2, ragged tail
+    (1, 700, 4, 128),     # 16-query waves on 16-key tiles, ragged tail
     (3, 70, 5, 32),       # 16-query waves with fewer key tiles than groups
     (2, 1100, 16, 64),    # four waves (non-causal: 288 workgroups)
     (2, 1000, 64, 128),   # eight waves
@@ -83,9 +82,10 @@ def test_prefill_decompositions(case, causal):
 
 
 SMALL_PROBLEMS = [
-    # B, S, H, d: non-causal, d <= 64 and B*H*ceil(S/128) < 256 run the 16-query-wave
+    # B, S, H, d: non-causal problems with B*H*ceil(S/128) < 256 run the 16-query-wave
     # kernel; the launcher picks 16, 32, 48 or 64 queries per workgroup (QW = 1..4)
     # so that the most loaded CU has the fewest queries (with 256 CUs: noted per case).
+    # At d = 128 a key tile is one 16-key MFMA tile and QW 4 reads K chunk by chunk.
     (1, 1, 3, 32),       # QW 1; one key, three of the four key groups empty
     (1, 17, 2, 64),      # QW 1; one ragged key tile
     (2, 33, 3, 32),      # QW 1; two key tiles
@@ -94,6 +94,11 @@ SMALL_PROBLEMS = [
     (2, 1000, 8, 64),    # QW 4
     (1, 1500, 8, 32),    # QW 3 (the encoder shape at d = 32)
     (3, 250, 2, 32),     # QW 1
+    (1, 1, 3, 128),      # QW 1; one key
+    (2, 100, 3, 128),    # QW 1; seven key tiles, ragged
+    (1, 600, 8, 128),    # QW 2
+    (1, 1500, 8, 128),   # QW 3
+    (1, 1024, 16, 128),  # QW 4
 ]
 
 
@@ -119,6 +124,9 @@ SMALL_CAUSAL = [
     (1, 1500, 8, 64, None),    # QW 2
     (1, 3000, 6, 64, "sampled"),   # QW 3
     (1, 32640, 1, 64, "sampled"),  # QW 4 (255 query tiles of 128 on one head)
+    (1, 17, 2, 128, None),     # QW 1
+    (1, 512, 32, 128, None),   # QW 2
+    (2, 700, 8, 128, "sampled"),   # QW 2
 ]
 
 

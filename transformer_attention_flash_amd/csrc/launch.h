@@ -58,8 +58,8 @@ struct PrefillArgs {
     SeqInts pos;
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
-// The uncached prefill of a small problem (head_dim 32 or 64) on 16-query
-// waves; `cus` = compute units of the device.
+// The uncached prefill of a small problem (head_dim 32, 64 or 128) on
+// 16-query waves; `cus` = compute units of the device.
 hipError_t launch_prefill_small(const PrefillArgs &a, int32_t cus, hipStream_t stream);
 // Query waves per workgroup (16 queries each) it picks for B*H heads of S
 // queries, without and with the causal mask.

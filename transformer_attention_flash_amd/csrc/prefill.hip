@@ -21,9 +21,9 @@
 // K and V tiles of BN = 32 keys go from HBM straight into a double-buffered
 // LDS tile (global_load_lds, no register staging); the next tile's transfer is
 // in flight while the current one is consumed, with one workgroup barrier per
-// tile.  Both products run on v_mfma_f32_32x32x2_f32.  (Non-causal problems
-// too small to fill the CUs with these workgroups run prefill_small.hip at
-// D <= 64, and a key split of this kernel at D = 128; see launch_typed.)
+// tile.  Both products run on v_mfma_f32_32x32x2_f32.  (Uncached problems too
+// small to fill the CUs with these workgroups run prefill_small.hip; see
+// launch_typed.)
 //
 // Register layouts of v_mfma_f32_32x32x2_f32 (lane l, i = l % 32, k = l / 32):
 // operand A supplies A[i][k], operand B supplies B[k][i], and output register
@@ -64,14 +64,12 @@ __device__ __forceinline__ void wait_vmem_all() {
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
-// NW waves in KS groups: the NW / KS waves of a group own 32 queries each
-// (BM = 32 NW / KS queries per workgroup), and group g walks the g-th of KS
-// contiguous ranges of the key tiles; KS > 1 (small non-causal problems at
-// D = 128 only) merges the groups' partial softmax states at the end.
-template <int D, int NW, int KS, bool CAUSAL>
+// NW waves of 32 queries each (BM = 32 NW queries per workgroup) walk all of
+// their key tiles together.
+template <int D, int NW, bool CAUSAL>
 __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs a, int32_t n_qtiles,
                                                                      int32_t xcd_remap) {
-    constexpr int QW = NW / KS;  // query waves per group
+    constexpr int QW = NW;  // query waves per workgroup
     constexpr int BM = 32 * QW;
     constexpr int NT = D / 32;          // 32-row tiles of O^T; also floats per lane per V row
     constexpr int QV = D / 8;           // 16-byte Q/K vectors per lane
@@ -80,8 +78,7 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
     constexpr int XPW = BN / RPI / QW;  // transfers per wave per tensor per tile
     constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;  // K chunk swizzle mask
     typedef typename VecN<NT>::type vrow_t;
-    static_assert(XPW >= 1 && XPW * RPI * QW == BN, "tile must split evenly over a group's waves");
-    static_assert(NW % KS == 0 && (KS == 1 || !CAUSAL), "key groups only without a causal mask");
+    static_assert(XPW >= 1 && XPW * RPI * QW == BN, "tile must split evenly over the waves");
 
     // Double-buffered K/V tiles.  K chunk c of row r sits at chunk position
     // c ^ (r & SWZ), so the 16 rows of one half-wave operand read hit distinct
@@ -89,10 +86,10 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
     // Separate objects (not one [2][..] array) so the compiler can see that a
     // transfer into one buffer does not alias reads of the other and does not
     // make those reads wait for it.
-    __shared__ __attribute__((aligned(16))) float Ks0[KS * BN * D];
-    __shared__ __attribute__((aligned(16))) float Vs0[KS * BN * D];
-    __shared__ __attribute__((aligned(16))) float Ks1[KS * BN * D];
-    __shared__ __attribute__((aligned(16))) float Vs1[KS * BN * D];
+    __shared__ __attribute__((aligned(16))) float Ks0[BN * D];
+    __shared__ __attribute__((aligned(16))) float Vs0[BN * D];
+    __shared__ __attribute__((aligned(16))) float Ks1[BN * D];
+    __shared__ __attribute__((aligned(16))) float Vs1[BN * D];
 
     // ---- block -> (b, h, query tile); heavy causal tiles first, and with
     // xcd_remap the query tiles of one (b, h) stay on one XCD (blocks are
@@ -139,8 +136,7 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
     const int lane = tid & 63;
     const int li = lane & 31;  // query column of this lane
     const int lk = lane >> 5;  // half-wave (MFMA k-slot)
-    const int qwave = wave % QW;     // query slice of this wave
-    const int grp = wave / QW;       // key group of this wave
+    const int qwave = wave;          // query slice of this wave
     const int q0 = qt * BM;
     const int qw0 = q0 + 32 * qwave;  // first query of this wave
     const int my_q = qw0 + li;
@@ -167,18 +163,12 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
 
     const int n_ktiles_all = (Sk + BN - 1) / BN;
     const int n_ktiles = CAUSAL ? min(n_ktiles_all, (P + min(q0 + BM, S) - 1) / BN + 1) : n_ktiles_all;
-    const int T = (n_ktiles + KS - 1) / KS;  // key tiles per group; group grp owns tiles grp*T ..
-    const int gt0 = grp * T;                 // this group's first key tile
-    const int goff = grp * BN * D;           // this group's slice of each LDS buffer
+    const int T = n_ktiles;
 
     // Each wave moves XPW 1 KiB pieces of the K tile and of the V tile straight
     // into LDS.  Keys past Sk read row Sk - 1 (in bounds); their scores are
     // masked and their probabilities are exactly 0, so the values never matter.
     auto issue_tile = [&](int kt, float *kdst, float *vdst) {
-        if (KS > 1 && gt0 + kt >= n_ktiles) return;  // past this group's range (wave-uniform)
-        kt += gt0;
-        kdst += goff;
-        vdst += goff;
 #pragma unroll
         for (int u = 0; u < XPW; ++u) {
             const int piece = qwave * XPW + u;
@@ -196,12 +186,6 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
         wait_vmem_all();  // this wave's share of tile kt has landed
         __syncthreads();  // ... and every other wave's; all are done with tile kt-1
         if (kt + 1 < T) issue_tile(kt + 1, Kn, Vn);
-        if (KS > 1) {
-            if (gt0 + kt >= n_ktiles) return;  // this group's range is done (wave-uniform)
-            kt += gt0;
-            Kt += goff;
-            Vt += goff;
-        }
 
         const int ks0 = kt * BN;  // first key of the tile
         if (CAUSAL && ks0 > P + qw0 + 31) return;  // whole tile above this wave's diagonal
@@ -292,45 +276,6 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
         if (kt + 1 < T) step(kt + 1, Ks1, Vs1, Ks0, Vs0);
     }
 
-    // ---- merge the key groups: groups 1.. park (max, partial sum, output) of
-    // each lane in LDS, group 0 folds them in with the usual rescaling.  No
-    // transfer is in flight: the last step issued none.
-    if constexpr (KS > 1) {
-        constexpr int SLOT = kWave * (16 * NT + 2);   // floats per parked wave
-        constexpr int PER = (KS * BN * D) / SLOT;     // parked waves per LDS buffer
-        static_assert(PER * 4 >= (KS - 1) * QW, "LDS too small to merge the key groups");
-        auto slot_ptr = [&](int sl) -> float * {
-            const int which = sl / PER;
-            float *buf = which == 0 ? Ks0 : which == 1 ? Vs0 : which == 2 ? Ks1 : Vs1;
-            return buf + (sl % PER) * SLOT;
-        };
-        __syncthreads();  // every wave is done with the K/V tiles
-        if (grp > 0) {
-            float *dst = slot_ptr((grp - 1) * QW + qwave) + lane;
-#pragma unroll
-            for (int n = 0; n < NT; ++n)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) dst[(16 * n + v) * kWave] = o[n][v];
-            dst[16 * NT * kWave] = m_run;
-            dst[(16 * NT + 1) * kWave] = l_run;
-        }
-        __syncthreads();
-        if (grp > 0) return;
-#pragma unroll
-        for (int g = 1; g < KS; ++g) {
-            const float *src = slot_ptr((g - 1) * QW + qwave) + lane;
-            const float m_g = src[16 * NT * kWave];
-            const float m_new = fmaxf(m_run, m_g);
-            const float keep = fast_exp2(m_run - m_new), take = fast_exp2(m_g - m_new);
-            l_run = l_run * keep + src[(16 * NT + 1) * kWave] * take;
-#pragma unroll
-            for (int n = 0; n < NT; ++n)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) o[n][v] = o[n][v] * keep + src[(16 * n + v) * kWave] * take;
-            m_run = m_new;
-        }
-    }
-
     // ---- normalise and store: lane holds query my_q, columns NT*row + n.
     l_run += __shfl_xor(l_run, 32);
     if (my_q < S) {
@@ -364,10 +309,9 @@ int32_t device_cus() {
 // query; four waves keep small problems spread over the CUs.  One eight-wave
 // workgroup fills a CU, so eight waves are used when that still gives at least
 // two workgroups per CU (and D >= 64: a 32-key tile of D = 32 rows is too small
-// to split over eight waves).  A non-causal problem too small to give every CU
-// a four-wave workgroup runs on 16-query waves (prefill_small.hip) at D <= 64;
-// at D = 128 it splits each workgroup's keys over 2 groups of two query waves
-// (64 queries per workgroup).
+// to split over eight waves).  An uncached problem too small to give every CU
+// a four-wave workgroup runs on 16-query waves whose workgroups split the keys
+// four ways (prefill_small.hip).
 template <int D, bool CAUSAL>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const int32_t BH = a.B * a.H;
@@ -377,27 +321,13 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     if constexpr (D >= 64) {
         if ((int64_t)BH * tiles8 >= 512) {
             dim3 grid((unsigned)(BH * tiles8));
-            prefill_kernel<D, 8, 1, CAUSAL><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
+            prefill_kernel<D, 8, CAUSAL><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
             return hipGetLastError();
         }
     }
-    if constexpr (D <= 64) {
-        if (!a.cached && (int64_t)BH * tiles4 < 256) return launch_prefill_small(a, device_cus(), stream);
-    }
-    if constexpr (!CAUSAL) {
-        if (!a.cached && (int64_t)BH * tiles4 < 256) {
-            if constexpr (D <= 64) {
-                return hipErrorInvalidValue;  // taken above
-            } else {
-                const int32_t tiles2 = (a.S + 63) / 64;
-                dim3 grid((unsigned)(BH * tiles2));
-                prefill_kernel<D, 4, 2, false><<<grid, dim3(kWave * 4), 0, stream>>>(a, tiles2, xcd_remap);
-                return hipGetLastError();
-            }
-        }
-    }
+    if (!a.cached && (int64_t)BH * tiles4 < 256) return launch_prefill_small(a, device_cus(), stream);
     dim3 grid((unsigned)(BH * tiles4));
-    prefill_kernel<D, 4, 1, CAUSAL><<<grid, dim3(kWave * 4), 0, stream>>>(a, tiles4, xcd_remap);
+    prefill_kernel<D, 4, CAUSAL><<<grid, dim3(kWave * 4), 0, stream>>>(a, tiles4, xcd_remap);
     return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 // prefill_small.hip -- the prefill of problems too small to give every CU a
-// workgroup of the main kernel (head_dim 32 or 64), on 16-query waves and
+// workgroup of the main kernel (head_dim 32, 64 or 128), on 16-query waves and
 // v_mfma_f32_16x16x4_f32.
 //
 // Semantics: the attention of prefill.hip (trueno-gpu 0.4.11
@@ -18,9 +18,9 @@
 //
 // Work decomposition: a workgroup owns BM = 16 QW queries of one (b, h) and
 // has QW query waves in each of 4 key groups; group g walks the g-th quarter
-// of the key tiles (32 keys each) the workgroup's queries can see, its QW
-// waves sharing every tile, and the groups' partial softmax states are merged
-// through LDS at the end.  With the causal mask, a wave skips the tiles wholly
+// of the key tiles (32 keys each, 16 at head_dim 128) the workgroup's queries
+// can see, its QW waves sharing every tile, and the groups' partial softmax
+// states are merged through LDS at the end.  With the causal mask, a wave skips the tiles wholly
 // above its diagonal, the diagonal tile is masked per element, and the
 // workgroups with the most visible keys are dispatched first.  K and V
 // tiles go from HBM straight into double-buffered LDS (global_load_lds), all
@@ -32,9 +32,10 @@
 // keys, columns = queries), with head dim (D / 4) k + j at step j, so each lane
 // reads its K row and holds its Q row as contiguous dims.  Output register r
 // of a 16-key score tile is then the operand-B value its lane supplies at step
-// r of O^T = V^T P^T (key 4 k + r), and row 4 k + r of output tile n stands
-// for dim NT (4 k + r) + n, so a lane's V operands for one step are NT
-// contiguous floats of one V row.
+// r of O^T = V^T P^T (key 4 k + r).  Row i of output tile n (NT = D / 16
+// tiles) stands for dim NT i + n, or at head_dim 128 for dim
+// 4 i + 64 (n / 4) + n % 4, so a lane's V operands for one step are NT
+// contiguous floats of one V row, or two runs of 4.
 #include <algorithm>
 #include <map>
 #include <mutex>
@@ -48,8 +49,18 @@
 namespace attn {
 namespace {
 
-constexpr int SBN = 32;  // keys per LDS tile (two 16-key MFMA tiles)
-constexpr int SKS = 4;   // key groups per workgroup
+constexpr int SKS = 4;  // key groups per workgroup
+
+// Keys per LDS tile: two 16-key MFMA tiles at d <= 64, one at d = 128 (LDS:
+// the four groups' double-buffered K and V tiles take 128 KiB either way).
+template <int D>
+constexpr int tile_keys() { return D == 128 ? 16 : 32; }
+
+// Head dim that row i of 16-row output tile n stands for (NT = D / 16 tiles).
+template <int D>
+__device__ __forceinline__ constexpr int odim(int i, int n) {
+    return D >= 64 ? 4 * i + 64 * (n / 4) + (n % 4) : 2 * i + n;
+}
 
 __device__ __forceinline__ f32x4 mfma16x4(float a, float b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -90,6 +101,8 @@ __device__ __forceinline__ void wait_vmem_all_small() {
 template <int D, int QW, bool CAUSAL>
 __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(PrefillArgs a, int32_t n_qtiles,
                                                                           int32_t xcd_remap) {
+    constexpr int SBN = tile_keys<D>();  // keys per LDS tile
+    constexpr int TPT = SBN / 16;        // 16-key MFMA tiles per LDS tile
     constexpr int NWV = QW * SKS;         // waves per workgroup
     constexpr int BM = 16 * QW;           // queries per workgroup
     constexpr int KC = D / 4;             // 16-byte chunks per K/V row
@@ -97,11 +110,15 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
     constexpr int PPT = SBN / RPI;        // transfers per tensor per group tile
     constexpr int NPIECE = SKS * 2 * PPT; // transfers per workgroup per tile step
     constexpr int SWZ = (KC < 16 ? KC : 16) - 1;  // K chunk swizzle mask
-    constexpr int NT = D / 16;            // 16-row tiles of O^T; floats per lane per V read
+    constexpr int NT = D / 16;            // 16-row tiles of O^T; floats per lane per V row
     constexpr int QJ = D / 4;             // k steps of the score product
-    typedef typename VecN<NT>::type vrow_t;
-    static_assert(D == 32 || D == 64, "head_dim 32 or 64");
+    constexpr int VW = NT < 4 ? NT : 4;   // floats per V / output vector
+    constexpr int NVW = NT / VW;          // vectors per lane per V row
+    typedef typename VecN<VW>::type vec_t;
+    static_assert(D == 32 || D == 64 || D == 128, "head_dim 32, 64 or 128");
     static_assert(RPI * KC == kWave && PPT * RPI == SBN, "tile transfers");
+    constexpr bool kPreloadK = !(D == 128 && QW == 4);
+    static_assert(kPreloadK || TPT == 1, "chunk-by-chunk K reads use one 16-key tile");
 
     // Double-buffered K/V tiles: each buffer holds the four groups' K tiles
     // (SBN x D each), then their V tiles.  K chunk c of row r sits at chunk
@@ -220,33 +237,56 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
         Vt += grp * SBN * D;
         const int ks0 = tile * SBN;
 
-        // S^T for the tile's two 16-key halves (independent chains); all K
-        // operands are read before the chains start.
-        f32x4 kv[2][QJ / 4];
+        // S^T for the tile's 16-key MFMA tiles in two independent chains (the
+        // two tiles, or with one tile its even and odd k steps).  The K
+        // operands are read before the chains start, or at d = 128 with 16
+        // waves (128 registers a lane) chunk by chunk.
+        auto kchunk = [&](int t, int jj) -> f32x4 {
+            const int row = 16 * t + li;
+            const int chunk = (QJ / 4) * lk + jj;
+            return *reinterpret_cast<const f32x4 *>(Kt + row * D + 4 * (chunk ^ (row & SWZ)));
+        };
+        f32x4 acc[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+        if constexpr (kPreloadK) {
+            f32x4 kv[TPT][QJ / 4];
 #pragma unroll
-        for (int jj = 0; jj < QJ / 4; ++jj)
+            for (int jj = 0; jj < QJ / 4; ++jj)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int row = 16 * t + li;
-                const int chunk = (QJ / 4) * lk + jj;
-                kv[t][jj] = *reinterpret_cast<const f32x4 *>(Kt + row * D + 4 * (chunk ^ (row & SWZ)));
+                for (int t = 0; t < TPT; ++t) kv[t][jj] = kchunk(t, jj);
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int jj = 0; jj < QJ / 4; ++jj)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int t = 0; t < TPT; ++t) {
+                        const int c = TPT == 2 ? t : (jj & 1);
+                        acc[c] = mfma16x4(kv[t][jj][e], qreg[4 * jj + e], acc[c]);
+                    }
+        } else {
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int jj = 0; jj < QJ / 4; ++jj) {
+                const f32x4 k4 = kchunk(0, jj);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[jj & 1] = mfma16x4(k4[e], qreg[4 * jj + e], acc[jj & 1]);
             }
-        f32x4 s[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int jj = 0; jj < QJ / 4; ++jj)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) s[t] = mfma16x4(kv[t][jj][e], qreg[4 * jj + e], s[t]);
+        }
         __builtin_amdgcn_s_setprio(0);
+        f32x4 s[TPT];
+        if constexpr (TPT == 2) {
+            s[0] = acc[0];
+            s[1] = acc[1];
+        } else {
+            s[0] = acc[0] + acc[1];
+        }
 
         // Keys past S (the last tile) and, causal, keys after the query's
         // position are masked.  A lane whose keys are all masked keeps its
         // state: the running max stays put (finite) and the probabilities are 0.
         if (ks0 + SBN > S || (CAUSAL && ks0 + SBN - 1 > qw0)) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < TPT; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = ks0 + 16 * t + 4 * lk + r;
@@ -255,7 +295,7 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
         }
         float mx = s[0][0];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < TPT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[t][r]);
         mx = max4(mx);
@@ -264,7 +304,7 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
         m_run = m_new;
         float psum = 0.f;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < TPT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 s[t][r] = fast_exp2(s[t][r] - m_new);
@@ -276,15 +316,19 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
             for (int n = 0; n < NT; ++n) o[n] *= alpha;
         }
 
-        // O^T += V^T P^T: step (t, r) is key 16 t + 4 lk + r for this lane.
+        // O^T += V^T P^T: step (t, r) is key 16 t + 4 lk + r for this lane,
+        // which supplies V[key][odim(li, n)] for output tile n.
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < TPT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const vrow_t vv = *reinterpret_cast<const vrow_t *>(Vt + (16 * t + 4 * lk + r) * D + NT * li);
+                const float *vrow = Vt + (16 * t + 4 * lk + r) * D + odim<D>(li, 0);
+                vec_t vv[NVW];
 #pragma unroll
-                for (int n = 0; n < NT; ++n) o[n] = mfma16x4(vget<NT>(vv, n), s[t][r], o[n]);
+                for (int w = 0; w < NVW; ++w) vv[w] = *reinterpret_cast<const vec_t *>(vrow + 64 * w);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) o[n] = mfma16x4(vget<VW>(vv[n / VW], n % VW), s[t][r], o[n]);
             }
         __builtin_amdgcn_s_setprio(0);
     };
@@ -310,8 +354,9 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
     // transfer is in flight: the last step issued none.
     {
         constexpr int SLOT = kWave * (4 * NT + 2);  // floats per parked wave
-        static_assert((SKS - 1) * QW * SLOT <= 2 * SKS * SBN * D, "LDS too small to merge the key groups");
-        auto slot_ptr = [&](int sl) -> float * { return KV0 + sl * SLOT; };
+        constexpr int PER = (2 * SKS * SBN * D) / SLOT;  // parked waves per buffer
+        static_assert(2 * PER >= (SKS - 1) * QW, "LDS too small to merge the key groups");
+        auto slot_ptr = [&](int sl) -> float * { return (sl < PER ? KV0 : KV1) + (sl % PER) * SLOT; };
         __syncthreads();  // every wave is done with the K/V tiles
         if (grp > 0) {
             float *dst = slot_ptr((grp - 1) * QW + qwave) + lane;
@@ -339,18 +384,20 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
         }
     }
 
-    // ---- normalise and store: lane holds query my_q, dims NT (4 lk + r) + n.
+    // ---- normalise and store: lane holds query my_q, dims odim(4 lk + r, n).
     l_run = sum4(l_run);
     if (my_q < S) {
         const float inv = 1.0f / l_run;
         float *op = a.out + head_base + (size_t)my_q * row_stride;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            vrow_t val;
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int n = 0; n < NT; ++n) vset<NT>(val, n, o[n][r] * inv);
-            *reinterpret_cast<vrow_t *>(op + NT * (4 * lk + r)) = val;
-        }
+            for (int w = 0; w < NVW; ++w) {
+                vec_t val;
+#pragma unroll
+                for (int e = 0; e < VW; ++e) vset<VW>(val, e, o[VW * w + e][r] * inv);
+                *reinterpret_cast<vec_t *>(op + odim<D>(4 * lk + r, VW * w)) = val;
+            }
     }
 }
 
@@ -384,10 +431,11 @@ namespace {
 // Causal: the work of a query tile grows with its position, so the cut is
 // chosen by simulating the dispatch: workgroups in launch order (heaviest
 // first) each go to the slot that frees first, at a speed set by the waves a
-// SIMD holds (one workgroup of 4 QW waves per CU at d = 64, two at d = 32 for
-// LDS), and the cut with the earliest end wins.  The speed factors per waves
-// per SIMD (1: 0.3, 2: 0.6, 3: 0.8, 4: 1) pick the fastest cut on every shape
-// timed (S 448..2000, 6..32 heads, d 32 and 64).  Results are cached per shape.
+// SIMD holds (one workgroup of 4 QW waves per CU at d = 64 and 128, two at
+// d = 32 for LDS), and the cut with the earliest end wins.  The speed factors
+// per waves per SIMD (1: 0.3, 2: 0.6, 3: 0.8, 4: 1) pick the fastest cut, or
+// one within 5% of it, on every shape timed (S 200..4000, 4..32 heads, d 32,
+// 64 and 128).  Results are cached per shape.
 int32_t causal_qw(int32_t BH, int32_t S, int32_t D, int32_t cus) {
     static const double kSpeed[5] = {0.0, 0.3, 0.6, 0.8, 1.0};
     const int32_t per_cu = D == 32 ? 2 : 1;
@@ -458,6 +506,7 @@ hipError_t launch_prefill_small(const PrefillArgs &a, int32_t cus, hipStream_t s
     switch (a.D) {
         case 32: return launch_d<32>(a, qw, stream);
         case 64: return launch_d<64>(a, qw, stream);
+        case 128: return launch_d<128>(a, qw, stream);
         default: return hipErrorInvalidValue;
     }
 }
