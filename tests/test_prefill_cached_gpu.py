@@ -6,7 +6,8 @@ head_dim, NaN in the cache rows not yet written (they must never be read).
 Both outputs are checked: the attention (abs 1e-4, normwise rel 1e-3) and the
 appended caches (bit-exact against the oracle's append).  GPU-side relations:
 an empty cache with Hkv = H gives the causal prefill; two chunks give the same
-outputs as one.  Full size: the second half of the causal prefill workload
+outputs as one.  Mid-size chunks that take each of the launcher's kernels are
+checked on sampled rows.  Full size: the second half of the causal prefill workload
 behind its first half (M=4, H=32, d=128, 2048 cached + 2048 new of 4096), and
 a 512-token chunk behind long GQA contexts (M=16, H=64, Hkv=8, 16K-32K cached),
 both on sampled rows.
@@ -102,6 +103,34 @@ def test_prefill_cached_two_chunks_equal_one():
     assert np.max(np.abs(np.concatenate(parts, axis=1) - whole)) <= 2e-5
     want = oracle.default().prefill_cached(q, kn, vn, kc, vc, lens0, M, S, H, Hkv, d, max_len, scale)
     assert_attn_close(whole, want, "whole chunk vs oracle")
+
+
+CACHED_DECOMPOSITIONS = [
+    # M, n, H, Hkv, d, max_len, lens: which kernel the launcher picks (M*H*ceil(n/128)
+    # four-wave workgroups and the mean cached length P decide), checked on sampled rows
+    (2, 1100, 16, 4, 64, 1600, [100, 480]),   # 288 workgroups, P < n: 16-query waves
+    (1, 700, 32, 8, 128, 2000, [1200]),       # 192 workgroups: 16-query waves behind a long cache
+    (2, 300, 64, 8, 128, 1300, [600, 950]),   # 384 workgroups, P > n: four waves
+    (2, 200, 64, 8, 64, 900, [500, 700]),     # 256 workgroups, P > n: four waves at d = 64
+    (1, 2100, 48, 16, 32, 2200, [64]),        # 816 workgroups at d = 32, P < n: 16-query waves
+]
+
+
+@pytest.mark.parametrize("case", CACHED_DECOMPOSITIONS,
+                         ids=[f"M{c[0]}_n{c[1]}_H{c[2]}_Hkv{c[3]}_d{c[4]}" for c in CACHED_DECOMPOSITIONS])
+def test_prefill_cached_decompositions(case):
+    M, n, H, Hkv, d, max_len, lens = case
+    lens, q, kn, vn, kc, vc = make_case(11 * M + n + d, M, n, H, Hkv, d, max_len, lens)
+    scale = wl.scale_for(d)
+    note(f"prefill_cached decomposition M={M} n={n} H={H} Hkv={Hkv} d={d} lens={lens.tolist()}")
+    got, _, _ = run_gpu(lens, q, kn, vn, kc, vc, M, n, H, Hkv, d, max_len, scale)
+    assert np.all(np.isfinite(got)), "every output element is written"
+    rng = np.random.default_rng(n + H)
+    sel = _sample_rows(rng, M, n, H, 12)
+    sel = np.concatenate([sel, [(m, r, h) for m in range(M) for r in (15, 16, 47, 48, 63, 64, n - 17, n - 16)
+                                for h in (0, H - 1)]]).astype(np.int64)
+    want = oracle.default().prefill_cached_rows(q, kn, vn, kc, vc, lens, sel, M, n, H, Hkv, d, max_len, scale)
+    assert_attn_close(np.stack([got[m, r, h * d:(h + 1) * d] for m, r, h in sel]), want, f"prefill_cached {case}")
 
 
 def _sample_rows(rng, M, n, H, count):

@@ -54,12 +54,13 @@ def test_prefill_small(case, causal):
 
 DECOMPOSITIONS = [
     # B, S, H, d -> which work decomposition the launcher picks (B*H*ceil(S/128) and
-    # B*H*ceil(S/256) decide): small problems run 16-query waves in 4 key groups;
-    # mid-size ones use 4 waves; large ones 8 waves.
+    # B*H*ceil(S/256) decide): small problems, and causal ones below 1024 four-wave
+    # workgroups, run 16-query waves in 4 key groups; mid-size ones use 4 waves; large
+    # ones 8 waves (d >= 64).
     (1, 1500, 8, 64),     # 16-query waves, 48 queries per workgroup (the Whisper-base shape)
     (1, 700, 4, 128),     # 16-query waves on 16-key tiles, ragged tail
     (3, 70, 5, 32),       # 16-query waves with fewer key tiles than groups
-    (2, 1100, 16, 64),    # four waves (non-causal: 288 workgroups)
+    (2, 1100, 16, 64),    # 288 workgroups: four waves, causal 16-query waves
     (2, 1000, 64, 128),   # eight waves
 ]
 
@@ -149,6 +150,32 @@ def test_prefill_small_problems_causal(case):
     want = orc.prefill_rows(q, k, v, sel, B, S, H, d, scale, True)
     got_sel = np.stack([got[b, i, h * d:(h + 1) * d] for b, i, h in sel])
     assert_attn_close(got_sel, want, f"prefill small causal {case} (sampled rows)")
+
+
+CAUSAL_MID = [
+    # B, S, H, d: causal problems between the small and the eight-wave ones, sampled rows
+    (1, 4096, 8, 128),    # 256 four-wave workgroups: 16-query waves
+    (1, 2000, 12, 64),    # 192 / 96: 16-query waves (eight-wave needs 512)
+    (1, 2048, 32, 32),    # 512: 16-query waves
+    (2, 2048, 32, 32),    # 1024 at d = 32: four waves
+]
+
+
+@pytest.mark.parametrize("case", CAUSAL_MID, ids=[f"B{c[0]}_S{c[1]}_H{c[2]}_d{c[3]}" for c in CAUSAL_MID])
+def test_prefill_causal_mid_size(case):
+    B, S, H, d = case
+    rng = np.random.default_rng(970 + S + H + d)
+    q, k, v = (rng.standard_normal((B, S, H * d), dtype=np.float32) for _ in range(3))
+    scale = wl.scale_for(d)
+    note(f"prefill causal mid-size B={B} S={S} H={H} d={d}")
+    got = run_prefill(q, k, v, B, S, H, d, scale, True)
+    assert np.all(np.isfinite(got)), "every output element is written"
+    picks = sorted({0, 1, 15, 16, 63, 64, 127, 128, S // 2, S - 65, S - 64, S - 17, S - 16, S - 1}
+                   | set(rng.integers(0, S, 10).tolist()))
+    sel = np.array([(b, i, h) for b in range(B) for i in picks for h in (0, H // 2, H - 1)], np.int64)
+    want = oracle.default().prefill_rows(q, k, v, sel, B, S, H, d, scale, True)
+    got_sel = np.stack([got[b, i, h * d:(h + 1) * d] for b, i, h in sel])
+    assert_attn_close(got_sel, want, f"prefill causal mid-size {case} (sampled rows)")
 
 
 def test_prefill_small_problem_large_scores():

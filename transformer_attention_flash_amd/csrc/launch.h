@@ -58,13 +58,12 @@ struct PrefillArgs {
     SeqInts pos;
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
-// The uncached prefill of a small problem (head_dim 32, 64 or 128) on
-// 16-query waves; `cus` = compute units of the device.
+// The prefill of a small problem (head_dim 32, 64 or 128) on 16-query waves
+// whose workgroups split the keys four ways; `cus` = compute units of the
+// device.
 hipError_t launch_prefill_small(const PrefillArgs &a, int32_t cus, hipStream_t stream);
-// Query waves per workgroup (16 queries each) it picks for B*H heads of S
-// queries, without and with the causal mask.
-int32_t prefill_small_qw(int32_t BH, int32_t S, int32_t cus);
-int32_t prefill_small_qw_causal(int32_t BH, int32_t S, int32_t D, int32_t cus);
+// Mean cached length over the batch (0 without a cache).
+int32_t prefill_cached_rows(const PrefillArgs &a);
 // The same attention (cached must be 0) on 16-bit MFMA operands:
 // precision ATTN_PREC_FP16 or ATTN_PREC_BF16.
 hipError_t launch_prefill_lowp(const PrefillArgs &a, int32_t precision, hipStream_t stream);

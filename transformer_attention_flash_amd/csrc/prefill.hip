@@ -309,9 +309,13 @@ int32_t device_cus() {
 // query; four waves keep small problems spread over the CUs.  One eight-wave
 // workgroup fills a CU, so eight waves are used when that still gives at least
 // two workgroups per CU (and D >= 64: a 32-key tile of D = 32 rows is too small
-// to split over eight waves).  An uncached problem too small to give every CU
-// a four-wave workgroup runs on 16-query waves whose workgroups split the keys
-// four ways (prefill_small.hip).
+// to split over eight waves).  A problem too small to give every CU a
+// four-wave workgroup runs on 16-query waves whose workgroups split the keys
+// four ways (prefill_small.hip), and so does a causal one with fewer than
+// four four-wave workgroups per CU unless a cache longer than the chunk makes
+// its work nearly uniform: the heaviest query tiles then set the time, and
+// splitting their keys shortens them (4096 tokens x 8 heads at d = 128:
+// 549 -> 329 us; 2048 x 16 at d = 64: 159 -> 90 us).
 template <int D, bool CAUSAL>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const int32_t BH = a.B * a.H;
@@ -325,7 +329,9 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
             return hipGetLastError();
         }
     }
-    if (!a.cached && (int64_t)BH * tiles4 < 256) return launch_prefill_small(a, device_cus(), stream);
+    const int64_t units4 = (int64_t)BH * tiles4;
+    if (units4 < 256 || (CAUSAL && units4 < 1024 && prefill_cached_rows(a) < a.S))
+        return launch_prefill_small(a, device_cus(), stream);
     dim3 grid((unsigned)(BH * tiles4));
     prefill_kernel<D, 4, CAUSAL><<<grid, dim3(kWave * 4), 0, stream>>>(a, tiles4, xcd_remap);
     return hipGetLastError();

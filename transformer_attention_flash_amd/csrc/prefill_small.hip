@@ -154,8 +154,20 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
     const size_t row_stride = (size_t)a.H * D;
     const size_t head_base = (size_t)b * S * row_stride + (size_t)h * D;
     const float *__restrict__ qg = a.q + head_base;
-    const float *__restrict__ kg = a.k + head_base;
-    const float *__restrict__ vg = a.v + head_base;
+    // Keys: the interleaved activations (key j = token j), or the cache slab of
+    // KV head h / (H / Hkv) (key j = cache row j, queries offset by P).
+    const int P = a.cached ? a.pos.v[b] : 0;  // key index of query 0
+    const int Sk = P + S;                      // keys a query can reach at most
+    size_t kv_stride, kv_base;
+    if (a.cached) {
+        kv_stride = D;
+        kv_base = ((size_t)b * a.Hkv + h / (a.H / a.Hkv)) * (size_t)a.max_len * D;
+    } else {
+        kv_stride = row_stride;
+        kv_base = head_base;
+    }
+    const float *__restrict__ kg = a.k + kv_base;
+    const float *__restrict__ vg = a.v + kv_base;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -189,8 +201,8 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
     float m_run = kNegBig;
     float l_run = 0.f;
 
-    const int n_ktiles_all = (S + SBN - 1) / SBN;
-    const int n_ktiles = CAUSAL ? min(n_ktiles_all, (min(q0 + BM, S) - 1) / SBN + 1) : n_ktiles_all;
+    const int n_ktiles_all = (Sk + SBN - 1) / SBN;
+    const int n_ktiles = CAUSAL ? min(n_ktiles_all, (P + min(q0 + BM, S) - 1) / SBN + 1) : n_ktiles_all;
     const int T = (n_ktiles + SKS - 1) / SKS;  // tile steps; group g owns tiles g T .. g T + T - 1
     const int gt0 = grp * T;
 
@@ -198,8 +210,8 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
     // workgroup's waves share the NPIECE 1 KiB transfers, wave w taking pieces
     // w, w + NWV, ...  A piece's lane addresses only move by whole tiles from
     // step to step, so they are set up once: the lane's source in tile 0, its
-    // row within the tile, and the piece's group and LDS offset.  Keys past S
-    // read row S - 1 (in bounds); their scores are masked and their
+    // row within the tile, and the piece's group and LDS offset.  Keys past Sk
+    // read row Sk - 1 (in bounds); their scores are masked and their
     // probabilities are exactly 0, so the values never matter.
     constexpr int MAXP = (NPIECE + NWV - 1) / NWV;  // pieces per wave at most
     const float *psrc[MAXP];
@@ -224,15 +236,15 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
             if (pg[u] >= SKS) continue;
             const int tile = pg[u] * T + kt;
             if (tile >= n_ktiles) continue;
-            const int key = min(tile * SBN + prow[u], S - 1);
-            dma16_small(psrc[u] + (size_t)key * row_stride, kv_dst + pdst[u]);
+            const int key = min(tile * SBN + prow[u], Sk - 1);
+            dma16_small(psrc[u] + (size_t)key * kv_stride, kv_dst + pdst[u]);
         }
     };
 
     auto compute = [&](int kt, const float *Kt, const float *Vt) {
         const int tile = gt0 + kt;
         if (tile >= n_ktiles) return;  // this group's range is done (wave-uniform)
-        if (CAUSAL && tile * SBN > qw0 + 15) return;  // whole tile above this wave's diagonal
+        if (CAUSAL && tile * SBN > P + qw0 + 15) return;  // whole tile above this wave's diagonal
         Kt += grp * SBN * D;
         Vt += grp * SBN * D;
         const int ks0 = tile * SBN;
@@ -281,16 +293,17 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
             s[0] = acc[0] + acc[1];
         }
 
-        // Keys past S (the last tile) and, causal, keys after the query's
-        // position are masked.  A lane whose keys are all masked keeps its
-        // state: the running max stays put (finite) and the probabilities are 0.
-        if (ks0 + SBN > S || (CAUSAL && ks0 + SBN - 1 > qw0)) {
+        // Keys past Sk (the last tile) and, causal, keys after the query's
+        // position P + q are masked.  A lane whose keys are all masked keeps
+        // its state: the running max stays put (finite) and the probabilities
+        // are 0.
+        if (ks0 + SBN > Sk || (CAUSAL && ks0 + SBN - 1 > P + qw0)) {
 #pragma unroll
             for (int t = 0; t < TPT; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int key = ks0 + 16 * t + 4 * lk + r;
-                    if (key >= S || (CAUSAL && key > my_q)) s[t][r] = -INFINITY;
+                    if (key >= Sk || (CAUSAL && key > P + my_q)) s[t][r] = -INFINITY;
                 }
         }
         float mx = s[0][0];
@@ -434,9 +447,10 @@ namespace {
 // SIMD holds (one workgroup of 4 QW waves per CU at d = 64 and 128, two at
 // d = 32 for LDS), and the cut with the earliest end wins.  The speed factors
 // per waves per SIMD (1: 0.3, 2: 0.6, 3: 0.8, 4: 1) pick the fastest cut, or
-// one within 5% of it, on every shape timed (S 200..4000, 4..32 heads, d 32,
-// 64 and 128).  Results are cached per shape.
-int32_t causal_qw(int32_t BH, int32_t S, int32_t D, int32_t cus) {
+// one within 5% of it, on every shape timed (S 200..16384, 4..32 heads, d 32,
+// 64 and 128).  Behind a cache of P rows every query tile has P more keys.
+// Results are cached per shape.
+int32_t causal_qw(int32_t BH, int32_t S, int32_t D, int32_t P, int32_t cus) {
     static const double kSpeed[5] = {0.0, 0.3, 0.6, 0.8, 1.0};
     const int32_t per_cu = D == 32 ? 2 : 1;
     int32_t best = 1;
@@ -449,7 +463,7 @@ int32_t causal_qw(int32_t BH, int32_t S, int32_t D, int32_t cus) {
         for (int32_t i = 0; i < cus * per_cu; ++i) slots.push(0.0);
         double end = 0.0;
         for (int64_t qt = n - 1; qt >= 0; --qt) {
-            const double work = (double)(bm * std::min<int64_t>((qt + 1) * bm, S)) / speed;
+            const double work = (double)(bm * (P + std::min<int64_t>((qt + 1) * bm, S))) / speed;
             for (int32_t h = 0; h < BH; ++h) {
                 const double t = slots.top() + work;
                 slots.pop();
@@ -466,18 +480,16 @@ int32_t causal_qw(int32_t BH, int32_t S, int32_t D, int32_t cus) {
 }
 
 std::mutex g_causal_mu;
-std::map<std::tuple<int32_t, int32_t, int32_t, int32_t>, int32_t> g_causal_qw;
+std::map<std::tuple<int32_t, int32_t, int32_t, int32_t, int32_t>, int32_t> g_causal_qw;
 
-}  // namespace
-
-int32_t prefill_small_qw_causal(int32_t BH, int32_t S, int32_t D, int32_t cus) {
-    const auto key = std::make_tuple(BH, S, D, cus);
+int32_t prefill_small_qw_causal(int32_t BH, int32_t S, int32_t D, int32_t P, int32_t cus) {
+    const auto key = std::make_tuple(BH, S, D, P, cus);
     {
         std::lock_guard<std::mutex> lock(g_causal_mu);
         const auto it = g_causal_qw.find(key);
         if (it != g_causal_qw.end()) return it->second;
     }
-    const int32_t qw = causal_qw(BH, S, D, cus);
+    const int32_t qw = causal_qw(BH, S, D, P, cus);
     std::lock_guard<std::mutex> lock(g_causal_mu);
     if (g_causal_qw.size() < 4096) g_causal_qw[key] = qw;
     return qw;
@@ -500,8 +512,19 @@ int32_t prefill_small_qw(int32_t BH, int32_t S, int32_t cus) {
     return best;
 }
 
+}  // namespace
+
+int32_t prefill_cached_rows(const PrefillArgs &a) {
+    if (!a.cached) return 0;
+    int64_t sum = 0;
+    for (int32_t b = 0; b < a.B; ++b) sum += a.pos.v[b];
+    return (int32_t)(sum / a.B);
+}
+
 hipError_t launch_prefill_small(const PrefillArgs &a, int32_t cus, hipStream_t stream) {
-    const int32_t qw = a.causal ? prefill_small_qw_causal(a.B * a.H, a.S, a.D, cus)
+    // The cut for a cache behind the chunk is chosen as if every sequence had
+    // the mean cached length, rounded down to 64 rows (few distinct shapes).
+    const int32_t qw = a.causal ? prefill_small_qw_causal(a.B * a.H, a.S, a.D, prefill_cached_rows(a) / 64 * 64, cus)
                                 : prefill_small_qw(a.B * a.H, a.S, cus);
     switch (a.D) {
         case 32: return launch_d<32>(a, qw, stream);
