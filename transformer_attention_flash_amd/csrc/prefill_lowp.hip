@@ -29,9 +29,11 @@
 // of BN keys are loaded as f32 into registers one tile ahead, rounded, and
 // written to a double-buffered LDS tile: K row-major (rows padded by 16 bytes:
 // the 16-byte operand reads of 8 consecutive rows hit distinct banks), V
-// transposed to [D][BN] with its 8-byte key groups XOR-swizzled by dimension
-// (conflict-free operand reads).  One workgroup barrier per tile.  The
-// softmax rescales lazily (see kLazy).
+// transposed to [D][BN] with its 4-key groups paired and XOR-swizzled by
+// dimension (one conflict-free 16-byte read per operand, see vswz).  One
+// workgroup barrier per tile.  The softmax rescales lazily (see kLazy).
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -87,6 +89,19 @@ __device__ __forceinline__ V4 round4(f32x4 x) {
     return V4{(T)x[0], (T)x[1], (T)x[2], (T)x[3]};
 }
 
+// V^T layout in LDS: row dim holds the tile's BN keys in 4-key groups, group
+// kq stored at position kq with bits 0 and 1 swapped, so the two groups one
+// lane needs for a P.V step (4t + lh and 4t + 2 + lh of a 32-key sub-tile,
+// see the layout note above) are adjacent; each such 16-byte pair p is
+// stored at pair position p ^ vswz(dim % 32), which puts the 16-byte reads of
+// any 8 or 16 consecutive dims (one LDS cycle) in distinct banks.  The
+// swizzle repeats every 32 dims, so a lane's reads for its dims li + 32 n
+// differ by constant offsets.
+template <int BN>
+__device__ __forceinline__ int vswz(int d) {
+    return BN == 64 ? ((d ^ (d >> 3)) & 7) : (((d >> 1) ^ (d >> 3)) & 3);
+}
+
 // NW waves in KS groups: the NW / KS waves of a group own 32 queries each
 // (BM = 32 NW / KS queries per workgroup) and group g walks the g-th of KS
 // contiguous ranges of the key tiles of BN keys (KS > 1 only for small
@@ -104,7 +119,6 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
     constexpr int KK = D / 16;   // k steps of the score product
     constexpr int NSUB = BN / 32;  // 32-key sub-tiles per tile
     constexpr int KP = D + 8;    // LDS pitch of a K row (elements)
-    constexpr int U = BN / 4;    // 8-byte key groups per V^T row
     // Staging: a thread moves blocks of 4 keys x 4 dims of K and of V.
     constexpr int NBLK = (BN / 4) * (D / 4);
     constexpr int BPT = (NBLK + kThreads - 1) / kThreads;  // blocks per thread
@@ -193,15 +207,15 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
     // rows past S read row S - 1 (in bounds; their scores are masked and their
     // probabilities are exactly 0).
     f32x4 kst[BPT][4], vst[BPT][4];
-    uint32_t goff[BPT][4];  // element offset of row 4 kq + j, chunk c, within a tile
-    int rowq[BPT];          // 4 kq
+    uint32_t goff[BPT];  // element offset of row 4 kq, chunk c, within a tile (row 4 kq + j: + j row_stride)
+    int rowq[BPT];       // 4 kq
+    const uint32_t rs32 = (uint32_t)row_stride;
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
         const int blk = tid + kThreads * u;
         const int c = blk % (D / 4), kq = blk / (D / 4);
         rowq[u] = 4 * kq;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) goff[u][j] = (uint32_t)((size_t)(4 * kq + j) * row_stride + 4 * c);
+        goff[u] = (uint32_t)((size_t)(4 * kq) * row_stride + 4 * c);
     }
     auto load_tile = [&](int kt) {
         kt += gt0;
@@ -216,7 +230,7 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
             if (NBLK % kThreads == 0 || blk < NBLK) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    uint32_t off = goff[u][j];
+                    uint32_t off = goff[u] + (uint32_t)j * rs32;
                     if (partial) {
                         const int over = kt * BN + rowq[u] + j - (S - 1);
                         if (over > 0) off -= (uint32_t)((size_t)over * row_stride);
@@ -238,12 +252,13 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     *reinterpret_cast<v4 *>(Ks + (4 * kq + j) * KP + 4 * c) = round4<T, v4>(kst[u][j]);
+                const int pq = (kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int dim = 4 * c + e;
-                    const int swz = (U == 16) ? (dim & 15) : ((dim >> 1) & 7);
                     const f32x4 col = {vst[u][0][e], vst[u][1][e], vst[u][2][e], vst[u][3][e]};
-                    *reinterpret_cast<v4 *>(Vt + dim * BN + 4 * (kq ^ swz)) = round4<T, v4>(col);
+                    *reinterpret_cast<v4 *>(Vt + dim * BN + 8 * ((pq >> 1) ^ vswz<BN>(dim & 31)) + 4 * (pq & 1)) =
+                        round4<T, v4>(col);
                 }
             }
         }
@@ -328,15 +343,33 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
         }
         const float mb = m_run * qsa;
         float psum = 0.f;
+        // Probabilities: summed in f32 and rounded at once to the P.V operands
+        // (score registers 8t .. 8t + 7 of a sub-tile are the k slots of its
+        // step t).  Masked scores give exact zeros (also for scale 0, where the
+        // exponent alone would not); tiles without masked keys skip the test.
+        v8 pop[NSUB][2];
+        auto probabilities = [&](auto masked) {
 #pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub)
+            for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float pv = fast_exp2(fmaf(s[sub][v], qsa, -mb));
-                if (need_mask) pv = (s[sub][v] == -INFINITY) ? 0.f : pv;  // exact zeros, also for scale 0
-                s[sub][v] = pv;
-                psum += pv;
-            }
+                for (int t = 0; t < 2; ++t) {
+                    f32x4 pr[2];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float sv = s[sub][8 * t + j];
+                        float pv = fast_exp2(fmaf(sv, qsa, -mb));
+                        if constexpr (decltype(masked)::value) pv = (sv == -INFINITY) ? 0.f : pv;
+                        pr[j / 4][j % 4] = pv;
+                        psum += pv;
+                    }
+                    pop[sub][t] = __builtin_shufflevector(round4<T, v4>(pr[0]), round4<T, v4>(pr[1]), 0, 1, 2, 3, 4,
+                                                          5, 6, 7);
+                }
+        };
+        if (need_mask)
+            probabilities(std::true_type{});
+        else
+            probabilities(std::false_type{});
         l_run += psum;
 
         // O^T += V^T P^T over the 16-key halves t of each sub-tile: this lane's
@@ -344,35 +377,23 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
         // V operands of a sub-tile are read before its MFMAs, as for K.
 #pragma unroll
         for (int sub = 0; sub < NSUB; ++sub) {
+            __builtin_amdgcn_sched_barrier(0);  // not above the previous sub-tile's MFMAs (registers)
             v8 vop[2][NT];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const int g0 = 8 * sub + 4 * t + lh;  // 8-byte key groups of the tile
-                const int g1 = g0 + 2;
+                const int pair = 4 * sub + 2 * t + lh;  // key groups 4t + lh and 4t + 2 + lh of the sub-tile
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
                     const int dim = 32 * n + li;
-                    const int swz = (U == 16) ? (dim & 15) : ((dim >> 1) & 7);
-                    const v4 a0 = *reinterpret_cast<const v4 *>(Vt + dim * BN + 4 * (g0 ^ swz));
-                    const v4 a1 = *reinterpret_cast<const v4 *>(Vt + dim * BN + 4 * (g1 ^ swz));
-                    vop[t][n] = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    vop[t][n] = *reinterpret_cast<const v8 *>(Vt + dim * BN + 8 * (pair ^ vswz<BN>(li)));
                 }
-            }
-            v8 pop[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const v4 p0 = round4<T, v4>(f32x4{s[sub][8 * t + 0], s[sub][8 * t + 1], s[sub][8 * t + 2],
-                                                  s[sub][8 * t + 3]});
-                const v4 p1 = round4<T, v4>(f32x4{s[sub][8 * t + 4], s[sub][8 * t + 5], s[sub][8 * t + 6],
-                                                  s[sub][8 * t + 7]});
-                pop[t] = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
             }
             __builtin_amdgcn_sched_barrier(0);
             mfma_priority(1);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int n = 0; n < NT; ++n) o[n] = Lp<T>::mfma(vop[t][n], pop[t], o[n]);
+                for (int n = 0; n < NT; ++n) o[n] = Lp<T>::mfma(vop[t][n], pop[sub][t], o[n]);
             mfma_priority(0);
         }
     };
