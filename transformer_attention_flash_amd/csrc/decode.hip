@@ -71,16 +71,9 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
 }
 
 // Cache rows are read exactly once per call: stream them past the caches.
-#ifndef ATTN_DECODE_NT_LOADS
-#define ATTN_DECODE_NT_LOADS 1
-#endif
 template <typename T>
 __device__ __forceinline__ T load_stream(const T *p) {
-#if ATTN_DECODE_NT_LOADS
     return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
 }
 
 template <int D, bool ROPE>
@@ -414,11 +407,12 @@ int32_t span_floor(int32_t max_len) {
     return s;
 }
 
+// The decode grid is this many times what the device holds at once (one
+// round, or three or more, measured slower).
+constexpr int kDecodeRounds = 2;
+
 // Workgroups of decode_split_kernel<D> that fit on the device at once (CUs x
 // resident blocks per CU), queried once per device and head_dim.
-#ifndef ATTN_DECODE_ROUNDS
-#define ATTN_DECODE_ROUNDS 2
-#endif
 constexpr int kMaxDevices = 64;
 std::atomic<int32_t> g_capacity[kMaxDevices][3];
 
@@ -465,14 +459,14 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
     const int64_t units_per_seq = (int64_t)a.Hkv * n_hblk;
 
     // Balance: cut every sequence's keys into key blocks of (nearly) equal
-    // size, sized so the whole grid is ATTN_DECODE_ROUNDS times what the device
+    // size, sized so the whole grid is kDecodeRounds times what the device
     // holds at once.  Equal blocks finish together, so no lone partial round
     // runs at the end.  Spans are multiples of 4 x 32 keys and at least
     // span_floor(max_len), which bounds the workspace.
     int64_t total = 0;
     for (int i = 0; i < a.M; ++i) total += a.lens.v[i];
     total *= units_per_seq;
-    const double target = (double)capacity_for(a.D) * ATTN_DECODE_ROUNDS;
+    const double target = (double)capacity_for(a.D) * kDecodeRounds;
     const int32_t sf = span_floor(a.max_len);
 
     UnitMap map;

@@ -67,18 +67,11 @@ template <> struct Lp<_Float16> {
 // priority, so that the SIMD's other wave (in its softmax) does not delay
 // them: the matrix pipe stays fed and the VALU work of the other wave fills
 // the gaps.
-#ifndef ATTN_LOWP_PRIO
-#define ATTN_LOWP_PRIO 1
-#endif
 __device__ __forceinline__ void mfma_priority(int p) {
-#if ATTN_LOWP_PRIO
     if (p)
         __builtin_amdgcn_s_setprio(1);
     else
         __builtin_amdgcn_s_setprio(0);
-#else
-    (void)p;
-#endif
 }
 
 // Key row (within a 32-key sub-tile) / output row of register v in lane-half h.

@@ -149,13 +149,7 @@ hipError_t launch_typed(const ScatterArgs &a, const RopeParams &rp, hipStream_t 
 // Slot copy: grid (vector blocks of one head, Hkv, 2 = K/V).  A head's live
 // rows are seq_len * D contiguous floats in both caches, so this is a straight
 // streaming copy per head at two different base offsets.
-#ifndef ATTN_SLOT_VEC
-#define ATTN_SLOT_VEC 4
-#endif
-#ifndef ATTN_SLOT_NT
-#define ATTN_SLOT_NT 1
-#endif
-constexpr int kSlotVec = ATTN_SLOT_VEC;
+constexpr int kSlotVec = 4;  // 16-byte vectors per thread
 
 __global__ __launch_bounds__(kThreads) void slot_copy_kernel(SlotCopyArgs a, uint32_t per_head_vec) {
     const int kh = blockIdx.y;
@@ -170,20 +164,12 @@ __global__ __launch_bounds__(kThreads) void slot_copy_kernel(SlotCopyArgs a, uin
 #pragma unroll
     for (int u = 0; u < kSlotVec; ++u) {
         const uint32_t i = first + u * kThreads;
-#if ATTN_SLOT_NT
         if (i < per_head_vec) buf[u] = __builtin_nontemporal_load(src + i);
-#else
-        if (i < per_head_vec) buf[u] = src[i];
-#endif
     }
 #pragma unroll
     for (int u = 0; u < kSlotVec; ++u) {
         const uint32_t i = first + u * kThreads;
-#if ATTN_SLOT_NT
         if (i < per_head_vec) __builtin_nontemporal_store(buf[u], dst + i);
-#else
-        if (i < per_head_vec) dst[i] = buf[u];
-#endif
     }
 }
 
