@@ -241,12 +241,17 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
         }
     };
 
-    auto compute = [&](int kt, const float *Kt, const float *Vt) {
+    // This lane's V operand offset within a buffer (group, k-slot and column
+    // folded in once): the reads below are then one variable and one
+    // constant step from the buffer itself, which keeps the compiler able to
+    // see which buffer they read (and not wait for the other buffer's
+    // transfers in flight).
+    const int vlane = SKS * SBN * D + grp * SBN * D + 4 * lk * D + odim<D>(li, 0);
+    auto compute = [&](int kt, const float *Kt, const float *KVb) {
         const int tile = gt0 + kt;
         if (tile >= n_ktiles) return;  // this group's range is done (wave-uniform)
         if (CAUSAL && tile * SBN > P + qw0 + 15) return;  // whole tile above this wave's diagonal
         Kt += grp * SBN * D;
-        Vt += grp * SBN * D;
         const int ks0 = tile * SBN;
 
         // S^T for the tile's 16-key MFMA tiles in two independent chains (the
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
         for (int t = 0; t < TPT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float *vrow = Vt + (16 * t + 4 * lk + r) * D + odim<D>(li, 0);
+                const float *vrow = KVb + vlane + (16 * t + r) * D;
                 vec_t vv[NVW];
 #pragma unroll
                 for (int w = 0; w < NVW; ++w) vv[w] = *reinterpret_cast<const vec_t *>(vrow + 64 * w);
@@ -353,7 +358,7 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
         wait_vmem_all_small();
         __syncthreads();
         if (kt + 1 < T) issue_tile(kt + 1, KVn);
-        compute(kt, KVt, KVt + SKS * SBN * D);
+        compute(kt, KVt, KVt);
     };
 
     issue_tile(0, KV0);
