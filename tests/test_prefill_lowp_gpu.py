@@ -9,8 +9,9 @@ bfloat16) on top of f32 rounding; the contract asserted here is
     max |gpu - oracle_lowp| <= 2 u max|v_rounded| + 1e-5.
 
 Cases: ragged S across 32/64-key and 128/256-query tiles, every head_dim,
-batch > 1, causal and not, both work decompositions (4 and 8 waves per
-workgroup, chosen by problem size), a non-default and a negative scale with
+batch > 1, causal and not, the three work decompositions (4 and 8 waves per
+workgroup, and for small problems at d <= 64 key tiles split over 4 groups of
+2 query waves, causal too), a non-default and a negative scale with
 large scores, both formats, and the three prefill workloads at full size
 (sampled rows for the causal one).  The
 error against the exact f32-input attention is printed for reference (it is
@@ -71,6 +72,29 @@ def test_prefill_lowp_small(case, causal, fmt):
     orc = oracle.default()
     want = orc.prefill_lowp(q, k, v, B, S, H, d, scale, causal, prec)
     check(got, want, orc.round16(v, prec), u, f"{fmt} {case} causal={causal}")
+
+
+SMALL_CAUSAL = [
+    # B, S, H, d: causal problems with B*H*ceil(S/128) < 256 at d <= 64 split each
+    # 64-query workgroup's visible key tiles over 4 groups of 2 query waves
+    (1, 1500, 8, 64),
+    (2, 1000, 8, 32),
+]
+
+
+@pytest.mark.parametrize("fmt", list(FORMATS))
+@pytest.mark.parametrize("case", SMALL_CAUSAL, ids=[f"B{c[0]}_S{c[1]}_H{c[2]}_d{c[3]}" for c in SMALL_CAUSAL])
+def test_prefill_lowp_small_causal_key_groups(case, fmt):
+    B, S, H, d = case
+    prec, u = FORMATS[fmt]
+    rng = np.random.default_rng(23 + S + H + d)
+    q, k, v = (rng.standard_normal((B, S, H * d), dtype=np.float32) for _ in range(3))
+    scale = wl.scale_for(d)
+    note(f"prefill_lowp {fmt} causal key groups B={B} S={S} H={H} d={d}")
+    got = run_lowp(q, k, v, B, S, H, d, scale, True, prec)
+    orc = oracle.default()
+    want = orc.prefill_lowp(q, k, v, B, S, H, d, scale, True, prec)
+    check(got, want, orc.round16(v, prec), u, f"{fmt} {case} causal key groups")
 
 
 EIGHT_WAVE = [

@@ -98,7 +98,7 @@ __device__ __forceinline__ int vswz(int d) {
 // NW waves in KS groups: the NW / KS waves of a group own 32 queries each
 // (BM = 32 NW / KS queries per workgroup) and group g walks the g-th of KS
 // contiguous ranges of the key tiles of BN keys (KS > 1 only for small
-// non-causal problems; the groups' softmax states are merged at the end).
+// problems; the groups' softmax states are merged at the end).
 // Two waves per SIMD either way.
 template <int D, int NW, int KS, int BN, bool CAUSAL, typename T>
 __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(PrefillArgs a, int32_t n_qtiles,
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
     constexpr int NBLK = (BN / 4) * (D / 4);
     constexpr int BPT = (NBLK + kThreads - 1) / kThreads;  // blocks per thread
     static_assert(BN == 32 || BN == 64, "tile of 32 or 64 keys");
-    static_assert(NW % KS == 0 && (KS == 1 || !CAUSAL), "key groups only without a causal mask");
+    static_assert(NW % KS == 0, "key groups of whole query waves");
 
     __shared__ __attribute__((aligned(16))) T Ks0[KS * BN * KP];
     __shared__ __attribute__((aligned(16))) T Vt0[KS * D * BN];
@@ -471,13 +471,15 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
         return hipGetLastError();
     }
     const int32_t tiles4 = (a.S + 127) / 128;
-    if constexpr (!CAUSAL && D <= 64) {
+    if constexpr (D <= 64) {
         if ((int64_t)BH * tiles4 < 256) {
             // Too small to give every CU a workgroup: split each workgroup's
-            // keys over 4 groups of 2 query waves (64 queries per workgroup).
+            // keys over 4 groups of 2 query waves (64 queries per workgroup;
+            // causal: the groups split the tiles the workgroup's queries see,
+            // heaviest workgroups first).
             const int32_t tiles2 = (a.S + 63) / 64;
             dim3 grid((unsigned)(BH * tiles2));
-            prefill_lowp_kernel<D, 8, 4, 32, false, T><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles2, xcd_remap);
+            prefill_lowp_kernel<D, 8, 4, 32, CAUSAL, T><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles2, xcd_remap);
             return hipGetLastError();
         }
     }
