@@ -11,7 +11,8 @@ bfloat16) on top of f32 rounding; the contract asserted here is
 Cases: ragged S across 32/64-key and 128/256-query tiles, every head_dim,
 batch > 1, causal and not, the three work decompositions (4 and 8 waves per
 workgroup, and for small problems at d <= 64 key tiles split over 4 groups of
-2 query waves, causal too), a non-default and a negative scale with
+2 query waves, at d = 128 over 2 groups of 4, causal too), a non-default and a
+negative scale with
 large scores, both formats, and the three prefill workloads at full size
 (sampled rows for the causal one).  The
 error against the exact f32-input attention is printed for reference (it is
@@ -75,10 +76,12 @@ def test_prefill_lowp_small(case, causal, fmt):
 
 
 SMALL_CAUSAL = [
-    # B, S, H, d: causal problems with B*H*ceil(S/128) < 256 at d <= 64 split each
-    # 64-query workgroup's visible key tiles over 4 groups of 2 query waves
+    # B, S, H, d: causal problems with B*H*ceil(S/128) < 256 split each workgroup's
+    # visible key tiles over groups of query waves (d <= 64: 4 groups of 2 waves,
+    # 64 queries per workgroup; d = 128: 2 groups of 4 waves, 128 queries)
     (1, 1500, 8, 64),
     (2, 1000, 8, 32),
+    (1, 2048, 8, 128),
 ]
 
 

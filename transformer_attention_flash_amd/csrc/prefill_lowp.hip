@@ -122,8 +122,13 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
     __shared__ __attribute__((aligned(16))) T Vt0[KS * D * BN];
     __shared__ __attribute__((aligned(16))) T Ks1[KS * BN * KP];
     __shared__ __attribute__((aligned(16))) T Vt1[KS * D * BN];
-    constexpr int SLOT = kWave * (16 * NT + 2);  // floats of one parked wave state (merge)
-    __shared__ float Red[KS > 1 ? (KS - 1) * QW * SLOT : 1];
+    // Key-group merge: the parked wave states go to the K/V tile buffers
+    // when they fit there, else to an array of their own.
+    constexpr int SLOT = kWave * (16 * NT + 2);  // floats of one parked wave state
+    constexpr int PK = (int)(KS * BN * KP * sizeof(T)) / (SLOT * 4);  // slots per K buffer
+    constexpr int PV = (int)(KS * D * BN * sizeof(T)) / (SLOT * 4);   // slots per V buffer
+    constexpr bool kParkInTiles = 2 * (PK + PV) >= (KS - 1) * QW;
+    __shared__ float Red[KS > 1 && !kParkInTiles ? (KS - 1) * QW * SLOT : 1];
 
     // ---- block -> (b, h, query tile): heavy causal tiles first; with
     // xcd_remap the query tiles of one (b, h) share an XCD (and its L2).
@@ -416,8 +421,18 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
     // state is relative to its own reference max m (probabilities
     // 2^((s - m) qsa)), so the usual rescaling applies.
     if constexpr (KS > 1) {
+        // The tile buffers are free: the last tile step ended in a barrier.
+        auto slot_ptr = [&](int sl) -> float * {
+            if (!kParkInTiles) return Red + sl * SLOT;
+            if (sl < PK) return reinterpret_cast<float *>(Ks0) + sl * SLOT;
+            sl -= PK;
+            if (sl < PV) return reinterpret_cast<float *>(Vt0) + sl * SLOT;
+            sl -= PV;
+            if (sl < PK) return reinterpret_cast<float *>(Ks1) + sl * SLOT;
+            return reinterpret_cast<float *>(Vt1) + (sl - PK) * SLOT;
+        };
         if (grp > 0) {
-            float *dst = Red + ((grp - 1) * QW + wave) * SLOT + lane;
+            float *dst = slot_ptr((grp - 1) * QW + wave) + lane;
 #pragma unroll
             for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -429,7 +444,7 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
         if (grp > 0) return;
 #pragma unroll
         for (int g = 1; g < KS; ++g) {
-            const float *src = Red + ((g - 1) * QW + wave) * SLOT + lane;
+            const float *src = slot_ptr((g - 1) * QW + wave) + lane;
             const float m_g = src[16 * NT * kWave];
             const float m_new = fmaxf(m_run, m_g);
             const float keep = fast_exp2((m_run - m_new) * qsa), take = fast_exp2((m_g - m_new) * qsa);
@@ -471,17 +486,21 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
         return hipGetLastError();
     }
     const int32_t tiles4 = (a.S + 127) / 128;
-    if constexpr (D <= 64) {
-        if ((int64_t)BH * tiles4 < 256) {
-            // Too small to give every CU a workgroup: split each workgroup's
-            // keys over 4 groups of 2 query waves (64 queries per workgroup;
-            // causal: the groups split the tiles the workgroup's queries see,
-            // heaviest workgroups first).
+    if ((int64_t)BH * tiles4 < 256) {
+        // Too small to give every CU a workgroup: split each workgroup's keys
+        // over groups of query waves (causal: the groups split the tiles the
+        // workgroup's queries see, heaviest workgroups first).  d <= 64: 4
+        // groups of 2 waves (64 queries per workgroup); d = 128: 2 groups of 4
+        // (128 queries; 4 groups would need twice the staging registers).
+        if constexpr (D <= 64) {
             const int32_t tiles2 = (a.S + 63) / 64;
             dim3 grid((unsigned)(BH * tiles2));
             prefill_lowp_kernel<D, 8, 4, 32, CAUSAL, T><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles2, xcd_remap);
-            return hipGetLastError();
+        } else {
+            dim3 grid((unsigned)(BH * tiles4));
+            prefill_lowp_kernel<D, 8, 2, 32, CAUSAL, T><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles4, xcd_remap);
         }
+        return hipGetLastError();
     }
     dim3 grid((unsigned)(BH * tiles4));
     prefill_lowp_kernel<D, 4, 1, 32, CAUSAL, T><<<grid, dim3(kWave * 4), 0, stream>>>(a, tiles4, xcd_remap);
