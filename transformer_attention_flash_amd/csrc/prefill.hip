@@ -42,6 +42,7 @@ namespace attn {
 namespace {
 
 constexpr int BN = 32;  // keys per LDS tile (one 32-key MFMA sub-tile)
+constexpr float kLazy = 8.0f;  // log2 headroom of the lazily rescaled softmax
 
 __device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16 &c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -202,6 +203,9 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
         // +5% on the causal d = 128 prefill).  The non-causal d = 128 kernels
         // keep two: four would spill there.
         constexpr bool kFourChains = CAUSAL || D < 128;
+        // The causal d = 128 kernels have no registers to spare for the lazy
+        // update's longer live ranges (it spilled there and ran 3% slower).
+        constexpr bool kLazyRescale = !(CAUSAL && D == 128);
         f32x16 s2 = f32x16{}, s3 = f32x16{}, s4 = f32x16{};
 #pragma unroll
         for (int j = 0; j < QV; ++j) {
@@ -238,21 +242,45 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
 #pragma unroll
         for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        float psum = 0.f;
+        if constexpr (kLazyRescale) {
+            // Lazy rescaling: the reference maximum m_run moves (and O and l
+            // are rescaled) only when a lane's scores would exceed it by more
+            // than 2^kLazy; otherwise the probabilities are taken against the
+            // stale reference (below 2^kLazy, exact enough in f32).  The
+            // decision is wave-uniform, so most tiles skip the 16 * NT
+            // multiplies.
+            if (__any(mx - m_run > kLazy)) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            s[v] = fast_exp2(s[v] - m_new);
-            psum += s[v];
-        }
-        l_run = l_run * alpha + psum;
-        // Once the running maxima settle, alpha is 1 in every lane: skip the
-        // 16*NT multiplies then (a wave-uniform branch).
-        if (__any(alpha != 1.0f)) {
+                for (int n = 0; n < NT; ++n) o[n] *= alpha;
+            }
+            float psum = 0.f;
 #pragma unroll
-            for (int n = 0; n < NT; ++n) o[n] *= alpha;
+            for (int v = 0; v < 16; ++v) {
+                s[v] = fast_exp2(s[v] - m_run);
+                psum += s[v];
+            }
+            l_run += psum;
+        } else {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            float psum = 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                s[v] = fast_exp2(s[v] - m_new);
+                psum += s[v];
+            }
+            l_run = l_run * alpha + psum;
+            // Once the running maxima settle, alpha is 1 in every lane: skip
+            // the 16*NT multiplies then (a wave-uniform branch).
+            if (__any(alpha != 1.0f)) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n) o[n] *= alpha;
+            }
         }
 
         // O^T += V^T P^T: at key step v this lane supplies V[key][NT*li + n]
