@@ -50,6 +50,7 @@ namespace attn {
 namespace {
 
 constexpr int SKS = 4;  // key groups per workgroup
+constexpr float kLazySmall = 8.0f;  // log2 headroom of the lazily rescaled softmax
 
 // Keys per LDS tile: two 16-key MFMA tiles at d <= 64, one at d = 128 (LDS:
 // the four groups' double-buffered K and V tiles take 128 KiB either way).
@@ -317,22 +318,28 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
 #pragma unroll
             for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[t][r]);
         mx = max4(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
+        // Lazy rescaling: the reference maximum m_run moves (and O and l are
+        // rescaled) only when a lane's scores would exceed it by more than
+        // 2^kLazySmall; otherwise the probabilities are taken against the
+        // stale reference (below 2^kLazySmall, exact enough in f32).  The
+        // decision is wave-uniform, so most tiles skip the rescale.
+        if (__any(mx - m_run > kLazySmall)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int n = 0; n < NT; ++n) o[n] *= alpha;
+        }
         float psum = 0.f;
 #pragma unroll
         for (int t = 0; t < TPT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                s[t][r] = fast_exp2(s[t][r] - m_new);
+                s[t][r] = fast_exp2(s[t][r] - m_run);
                 psum += s[t][r];
             }
-        l_run = l_run * alpha + psum;
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) o[n] *= alpha;
-        }
+        l_run += psum;
 
         // O^T += V^T P^T: step (t, r) is key 16 t + 4 lk + r for this lane,
         // which supplies V[key][odim(li, n)] for output tile n.
