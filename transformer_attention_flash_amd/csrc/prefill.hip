@@ -200,31 +200,51 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
         __builtin_amdgcn_s_setprio(1);
         // Independent accumulation chains, summed afterwards: back-to-back
         // dependent MFMAs issue more slowly (two chains gave +7%, four another
-        // +5% on the causal d = 128 prefill).  The non-causal d = 128 kernels
-        // keep two: four would spill there.
-        constexpr bool kFourChains = CAUSAL || D < 128;
-        // The causal d = 128 kernels have no registers to spare for the lazy
-        // update's longer live ranges (it spilled there and ran 3% slower).
-        constexpr bool kLazyRescale = !(CAUSAL && D == 128);
+        // +5% on the causal d = 128 prefill, before the lazy softmax update
+        // below).  The causal d = 128 kernels now use three: four leave no
+        // registers for the lazy update, and three with it beat four without
+        // it by 3-4%.  The non-causal d = 128 kernels keep two (three gave
+        // nothing there, four spill).
         f32x16 s2 = f32x16{}, s3 = f32x16{}, s4 = f32x16{};
+        if constexpr (CAUSAL && D == 128) {
 #pragma unroll
-        for (int j = 0; j < QV; ++j) {
-            const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + 4 * ((2 * j + lk) ^ (li & SWZ)));
-            s = mfma32(kv[0], qreg[j][0], s);
-            s2 = mfma32(kv[1], qreg[j][1], s2);
-            if constexpr (kFourChains) {
-                s3 = mfma32(kv[2], qreg[j][2], s3);
-                s4 = mfma32(kv[3], qreg[j][3], s4);
-            } else {
-                s = mfma32(kv[2], qreg[j][2], s);
-                s2 = mfma32(kv[3], qreg[j][3], s2);
+            for (int j = 0; j < QV; ++j) {
+                const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + 4 * ((2 * j + lk) ^ (li & SWZ)));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = (4 * j + e) % 3;  // compile-time after unrolling
+                    if (c == 0)
+                        s = mfma32(kv[e], qreg[j][e], s);
+                    else if (c == 1)
+                        s2 = mfma32(kv[e], qreg[j][e], s2);
+                    else
+                        s3 = mfma32(kv[e], qreg[j][e], s3);
+                }
             }
-        }
-        __builtin_amdgcn_s_setprio(0);
-        s += s2;
-        if constexpr (kFourChains) {
-            s3 += s4;
+            __builtin_amdgcn_s_setprio(0);
+            s += s2;
             s += s3;
+        } else {
+            constexpr bool kFourChains = CAUSAL || D < 128;
+#pragma unroll
+            for (int j = 0; j < QV; ++j) {
+                const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + 4 * ((2 * j + lk) ^ (li & SWZ)));
+                s = mfma32(kv[0], qreg[j][0], s);
+                s2 = mfma32(kv[1], qreg[j][1], s2);
+                if constexpr (kFourChains) {
+                    s3 = mfma32(kv[2], qreg[j][2], s3);
+                    s4 = mfma32(kv[3], qreg[j][3], s4);
+                } else {
+                    s = mfma32(kv[2], qreg[j][2], s);
+                    s2 = mfma32(kv[3], qreg[j][3], s2);
+                }
+            }
+            __builtin_amdgcn_s_setprio(0);
+            s += s2;
+            if constexpr (kFourChains) {
+                s3 += s4;
+                s += s3;
+            }
         }
 
         // Mask: keys past Sk, and (causal) keys after the query's position.
@@ -242,46 +262,26 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
 #pragma unroll
         for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if constexpr (kLazyRescale) {
-            // Lazy rescaling: the reference maximum m_run moves (and O and l
-            // are rescaled) only when a lane's scores would exceed it by more
-            // than 2^kLazy; otherwise the probabilities are taken against the
-            // stale reference (below 2^kLazy, exact enough in f32).  The
-            // decision is wave-uniform, so most tiles skip the 16 * NT
-            // multiplies.
-            if (__any(mx - m_run > kLazy)) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = fast_exp2(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int n = 0; n < NT; ++n) o[n] *= alpha;
-            }
-            float psum = 0.f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                s[v] = fast_exp2(s[v] - m_run);
-                psum += s[v];
-            }
-            l_run += psum;
-        } else {
+        // Lazy rescaling: the reference maximum m_run moves (and O and l are
+        // rescaled) only when a lane's scores would exceed it by more than
+        // 2^kLazy; otherwise the probabilities are taken against the stale
+        // reference (below 2^kLazy, exact enough in f32).  The decision is
+        // wave-uniform, so most tiles skip the 16 * NT multiplies.
+        if (__any(mx - m_run > kLazy)) {
             const float m_new = fmaxf(m_run, mx);
             const float alpha = fast_exp2(m_run - m_new);
             m_run = m_new;
-            float psum = 0.f;
+            l_run *= alpha;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                s[v] = fast_exp2(s[v] - m_new);
-                psum += s[v];
-            }
-            l_run = l_run * alpha + psum;
-            // Once the running maxima settle, alpha is 1 in every lane: skip
-            // the 16*NT multiplies then (a wave-uniform branch).
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int n = 0; n < NT; ++n) o[n] *= alpha;
-            }
+            for (int n = 0; n < NT; ++n) o[n] *= alpha;
         }
+        float psum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            s[v] = fast_exp2(s[v] - m_run);
+            psum += s[v];
+        }
+        l_run += psum;
 
         // O^T += V^T P^T: at key step v this lane supplies V[key][NT*li + n]
         // for n-tile n and P^T[key][my_q] = s[v].
