@@ -6,8 +6,8 @@ head_dim, NaN in the cache rows not yet written (they must never be read).
 Both outputs are checked: the attention (abs 1e-4, normwise rel 1e-3) and the
 appended caches (bit-exact against the oracle's append).  GPU-side relations:
 an empty cache with Hkv = H gives the causal prefill; two chunks give the same
-outputs as one.  Mid-size chunks that take each of the launcher's kernels are
-checked on sampled rows.  Full size: the second half of the causal prefill workload
+outputs as one; a captured HIP graph replays to the eager result.  Mid-size
+chunks that take each of the launcher's kernels are checked on sampled rows.  Full size: the second half of the causal prefill workload
 behind its first half (M=4, H=32, d=128, 2048 cached + 2048 new of 4096), and
 a 512-token chunk behind long GQA contexts (M=16, H=64, Hkv=8, 16K-32K cached),
 both on sampled rows.
@@ -178,3 +178,42 @@ def test_prefill_cached_long_gqa_context_full_size():
     want = oracle.default().prefill_cached_rows(q, kn, vn, inp["k_cache"], inp["v_cache"], lens, sel, M, n, H, Hkv,
                                                 d, max_len, cfg.scale)
     assert_attn_close(np.stack([got[m, r, h * d:(h + 1) * d] for m, r, h in sel]), want, "512 behind long contexts")
+
+
+def test_prefill_cached_graph_replays_match_eager():
+    """Append + attention of a chunk captured into a HIP graph: every replay (new chunk
+    contents, same cached lengths) gives the eager outputs and caches, bit for bit."""
+    import torch
+    M, n, H, Hkv, d, max_len = 2, 300, 16, 4, 64, 1000
+    lens = [250, 600]
+    rng = np.random.default_rng(890)
+    scale = wl.scale_for(d)
+    kc0 = rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32)
+    vc0 = rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32)
+    qs = (M, n, H * d)
+    ns = (M, n, Hkv * d)
+    q_s, kn_s, vn_s = to_dev(np.zeros(qs, np.float32)), to_dev(np.zeros(ns, np.float32)), to_dev(np.zeros(ns, np.float32))
+    kc_s, vc_s = to_dev(kc0), to_dev(vc0)
+    out_s = torch.zeros(qs, device="cuda:0")
+    note("prefill_cached graph capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        taf.attn_prefill_cached(q_s, kn_s, vn_s, kc_s, vc_s, lens, out_s, M, n, H, Hkv, d, max_len, scale)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        taf.attn_prefill_cached(q_s, kn_s, vn_s, kc_s, vc_s, lens, out_s, M, n, H, Hkv, d, max_len, scale)
+    for rep in range(3):
+        q = rng.standard_normal(qs, dtype=np.float32)
+        kn = rng.standard_normal(ns, dtype=np.float32)
+        vn = rng.standard_normal(ns, dtype=np.float32)
+        for dst, src in ((q_s, q), (kn_s, kn), (vn_s, vn)):
+            dst.copy_(to_dev(src))
+        graph.replay()
+        torch.cuda.synchronize()
+        got, got_kc = to_host(out_s), to_host(kc_s)
+        eager, eager_kc, _ = run_gpu(np.asarray(lens, np.int32), q, kn, vn, kc0, vc0, M, n, H, Hkv, d, max_len, scale)
+        assert np.array_equal(bits(got), bits(eager)), f"replay {rep}: attention differs from the eager call"
+        assert np.array_equal(bits(got_kc), bits(to_host(eager_kc))), f"replay {rep}: K cache differs"

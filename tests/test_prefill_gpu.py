@@ -7,6 +7,10 @@ and not, non-default scales and large scores.  Outputs start as NaN so an
 unwritten element fails.  The full-size cases are the three prefill
 workloads: all outputs for the two non-causal ones, sampled rows (first and
 last queries, tile edges, random) for the causal B=4, S=2048, H=32, d=128 one.
+Every work decomposition the launcher picks has cases of its own (the small
+and mid-size ones on 16-query waves, causal and not, at every head_dim), and
+each is also captured into a HIP graph whose replays must match eager calls
+bit for bit.
 """
 import numpy as np
 import pytest
@@ -227,3 +231,44 @@ def test_prefill_full_size_causal_sampled():
     want = oracle.default().prefill_rows(q, k, v, sel, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, True)
     got_sel = np.stack([got[b, i, h * cfg.d:(h + 1) * cfg.d] for b, i, h in sel])
     assert_attn_close(got_sel, want, "causal full-size sampled rows")
+
+
+GRAPH_CASES = [
+    # B, S, H, d, causal: one capture per work decomposition
+    (1, 300, 4, 64, True),      # 16-query waves, causal
+    (1, 700, 4, 128, False),    # 16-query waves on 16-key tiles
+    (2, 1024, 32, 128, True),   # eight-wave workgroups (512 of them)
+]
+
+
+@pytest.mark.parametrize("case", GRAPH_CASES, ids=[f"B{c[0]}_S{c[1]}_H{c[2]}_d{c[3]}_c{int(c[4])}" for c in GRAPH_CASES])
+def test_prefill_graph_replays_match_eager(case):
+    """A prefill captured into a HIP graph replays to the eager result, bit for bit, over several
+    replays with new inputs and eager prefills in between."""
+    import torch
+    from gpu_common import bits
+    B, S, H, d, causal = case
+    rng = np.random.default_rng(880 + S + H)
+    scale = wl.scale_for(d)
+    shape = (B, S, H * d)
+    q_s, k_s, v_s = (to_dev(rng.standard_normal(shape, dtype=np.float32)) for _ in range(3))
+    out_s = torch.zeros(shape, device="cuda:0")
+    note(f"prefill graph capture B={B} S={S} H={H} d={d} causal={causal}")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up on the capture stream (first-call host queries)
+        taf.attn_prefill(q_s, k_s, v_s, out_s, B, S, H, d, scale, causal)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        taf.attn_prefill(q_s, k_s, v_s, out_s, B, S, H, d, scale, causal)
+    for rep in range(3):
+        q, k, v = (rng.standard_normal(shape, dtype=np.float32) for _ in range(3))
+        for dst, src in ((q_s, q), (k_s, k), (v_s, v)):
+            dst.copy_(to_dev(src))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = to_host(out_s)
+        eager = run_prefill(q, k, v, B, S, H, d, scale, causal)
+        assert np.array_equal(bits(got), bits(eager)), f"replay {rep} differs from the eager prefill"
