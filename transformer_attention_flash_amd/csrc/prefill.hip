@@ -9,11 +9,12 @@
 // 0..=i, masked probabilities exactly zero).  The same kernel also runs a
 // chunk of queries behind an existing KV cache (the case that page leaves to
 // other paths): keys then come from the GQA cache slab [max_len, D] of the
-// query head's KV head and query i of the chunk sees cache rows 0..P+i.  Instead of the pages' per-head
-// extract / transpose / GEMM / softmax / GEMM chain, one kernel reads the
-// head's columns straight out of the interleaved rows and never materialises
-// scores: an online softmax (running row max and sum, output rescaled when
-// the max grows) walks the key axis tile by tile.
+// query head's KV head and query i of the chunk sees cache rows 0..P+i.
+// Instead of the pages' per-head extract / transpose / GEMM / softmax / GEMM
+// chain, one kernel reads the head's columns straight out of the interleaved
+// rows and never materialises scores: an online softmax (running row sum
+// against a reference maximum, output rescaled when that reference moves)
+// walks the key axis tile by tile.
 //
 // Work decomposition: a workgroup owns BM = 32 NW queries of one (b, h) (NW =
 // 8 waves, or 4 for smaller problems); each wavefront owns 32 of them and
@@ -21,9 +22,9 @@
 // K and V tiles of BN = 32 keys go from HBM straight into a double-buffered
 // LDS tile (global_load_lds, no register staging); the next tile's transfer is
 // in flight while the current one is consumed, with one workgroup barrier per
-// tile.  Both products run on v_mfma_f32_32x32x2_f32.  (Uncached problems too
-// small to fill the CUs with these workgroups run prefill_small.hip; see
-// launch_typed.)
+// tile.  Both products run on v_mfma_f32_32x32x2_f32.  (Problems too small to
+// fill the CUs with these workgroups, and mid-size causal ones, run
+// prefill_small.hip; see launch_typed.)
 //
 // Register layouts of v_mfma_f32_32x32x2_f32 (lane l, i = l % 32, k = l / 32):
 // operand A supplies A[i][k], operand B supplies B[k][i], and output register

@@ -23,9 +23,10 @@
 // are that lane's k slots, the probabilities go from score registers to
 // operand registers with a conversion only, and V^T is read at the same keys.
 //
-// Work decomposition as in prefill.hip: a workgroup owns BM = 32 NW queries
-// of one (b, h) (NW = 8 waves, or 4 for small problems), each wave 32 of them
-// with its Q slice (16-bit) and its 32 x D f32 output in registers.  K/V tiles
+// Work decomposition as in prefill.hip: a workgroup owns 32 queries per
+// query wave of one (b, h) (8 waves, or 4 for mid-size problems; small ones
+// split 8 waves into key groups, see launch_typed), each wave with its Q slice
+// (16-bit) and its 32 x D f32 output in registers.  K/V tiles
 // of BN keys are loaded as f32 into registers one tile ahead, rounded, and
 // written to a double-buffered LDS tile: K row-major (rows padded by 16 bytes:
 // the 16-byte operand reads of 8 consecutive rows hit distinct banks), V
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
 }
 
 // Eight waves (256 queries) per workgroup halve the K/V reads and conversions
-// per query; four waves keep small problems spread over the 256 CUs.  One
+// per query; four waves keep smaller problems spread over the CUs.  One
 // eight-wave workgroup fills a CU, so eight waves are used when that still
 // gives at least two workgroups per CU.
 template <int D, bool CAUSAL, typename T>

@@ -1,13 +1,14 @@
 // prefill_small.hip -- the prefill of problems too small to give every CU a
-// workgroup of the main kernel (head_dim 32, 64 or 128), on 16-query waves and
-// v_mfma_f32_16x16x4_f32.
+// workgroup of the main kernel, and of mid-size causal ones (head_dim 32, 64
+// or 128; behind a KV cache too), on 16-query waves and v_mfma_f32_16x16x4_f32.
 //
 // Semantics: the attention of prefill.hip (trueno-gpu 0.4.11
 // src/memory/resident/attention.rs, `batched_multihead_attention`: per head,
 // softmax(scale Q K^T) V over the interleaved [B, S, H * D] rows; with the
 // causal mask of trustformers-core 0.2.0 src/gpu_ops/cuda/oxicuda/attention.rs,
-// `attention_prefill_gpu_to_gpu`: query i sees keys 0..=i); this file only
-// changes how the work is cut.
+// `attention_prefill_gpu_to_gpu`: query i sees keys 0..=i; behind a cache of
+// P rows, keys from the cache slab and query i sees rows 0..P+i); this file
+// only changes how the work is cut.
 //
 // Why: the time of a small problem is that of its most loaded CU.  With
 // 32-query waves a workgroup covers at least 32 queries of one head, so a
@@ -20,9 +21,11 @@
 // has QW query waves in each of 4 key groups; group g walks the g-th quarter
 // of the key tiles (32 keys each, 16 at head_dim 128) the workgroup's queries
 // can see, its QW waves sharing every tile, and the groups' partial softmax
-// states are merged through LDS at the end.  With the causal mask, a wave skips the tiles wholly
-// above its diagonal, the diagonal tile is masked per element, and the
-// workgroups with the most visible keys are dispatched first.  K and V
+// states are merged through LDS at the end.  With the causal mask, a wave
+// skips the tiles wholly above its diagonal, the diagonal tile is masked per
+// element, and the workgroups with the most visible keys are dispatched
+// first (for mid-size causal problems the key split also shortens the
+// heaviest workgroups, which set the time there).  K and V
 // tiles go from HBM straight into double-buffered LDS (global_load_lds), all
 // four groups' tiles moved by all the workgroup's waves, one barrier per tile.
 //
