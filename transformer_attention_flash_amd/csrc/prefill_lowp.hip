@@ -101,7 +101,11 @@ __device__ __forceinline__ int vswz(int d) {
 // contiguous ranges of the key tiles of BN keys (KS > 1 only for small
 // problems; the groups' softmax states are merged at the end).
 // Two waves per SIMD either way.
-template <int D, int NW, int KS, int BN, bool CAUSAL, typename T>
+//
+// HM: head-major launch order (the query tiles of one (b, h) run next to each
+// other, so they stream its K/V through the same L2 at about the same time);
+// otherwise query-tile-major, heaviest causal tiles first.
+template <int D, int NW, int KS, int BN, bool CAUSAL, typename T, bool HM = false>
 __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(PrefillArgs a, int32_t n_qtiles,
                                                                           int32_t xcd_remap) {
     constexpr int QW = NW / KS;       // query waves per group
@@ -141,11 +145,11 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
         if (xcd_remap) {
             const int per_xcd_bh = BH / 8;
             const int x = bid % 8, t = bid / 8;
-            bh = 8 * (t % per_xcd_bh) + x;
-            rank = t / per_xcd_bh;
+            bh = 8 * (HM ? t / n_qtiles : t % per_xcd_bh) + x;
+            rank = HM ? t % n_qtiles : t / per_xcd_bh;
         } else {
-            bh = bid % BH;
-            rank = bid / BH;
+            bh = HM ? bid / n_qtiles : bid % BH;
+            rank = HM ? bid % n_qtiles : bid / BH;
         }
         qt = CAUSAL ? n_qtiles - 1 - rank : rank;
     }
@@ -482,8 +486,12 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const int32_t xcd_remap = (BH % 8 == 0) ? 1 : 0;
     const int32_t tiles8 = (a.S + 255) / 256;
     if ((int64_t)BH * tiles8 >= 512) {
+        // Non-causal: head-major order (a (b, h)'s query tiles share its K/V in
+        // L2: B=4 S=2048 H=32 d=128 412 -> 363 us).  Causal: heaviest tiles
+        // first (head-major makes the heavy tiles of the last heads run last).
         dim3 grid((unsigned)(BH * tiles8));
-        prefill_lowp_kernel<D, 8, 1, 64, CAUSAL, T><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
+        prefill_lowp_kernel<D, 8, 1, 64, CAUSAL, T, !CAUSAL><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8,
+                                                                                                  xcd_remap);
         return hipGetLastError();
     }
     const int32_t tiles4 = (a.S + 127) / 128;
