@@ -265,8 +265,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
                 sc[t][r] = live ? sc[t][r] : -INFINITY;
                 mx = fmaxf(mx, sc[t][r]);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max4(mx);
         const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
@@ -300,8 +299,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     }
 
     // Each k-slot group summed its own keys; combine them.
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = sum4(l_run);
 
     // Merge the four waves' states through LDS: each wave parks (m, l, O^T)
     // in its own K tile (its last reads of that tile are behind it: a wave's

@@ -46,4 +46,23 @@ __device__ __forceinline__ void vset(typename VecN<N>::type &x, int i, float val
     }
 }
 
+// Cross-lane combines without an LDS round trip.  v_permlane32_swap returns,
+// in every lane l, the values of lanes l and l ^ 32 (one in each result), so
+// combining its two results needs no lane mask; a swizzle swaps the 16-lane
+// halves of each 32-lane group.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16(float x) {
+    return __uint_as_float(__builtin_amdgcn_ds_swizzle(__float_as_uint(x), 0x401F));  // lane l ^ 16
+}
+// Over the four lanes i, i + 16, i + 32, i + 48.
+__device__ __forceinline__ float max4(float x) { return max_xor32(fmaxf(x, xor16(x))); }
+__device__ __forceinline__ float sum4(float x) { return sum_xor32(x + xor16(x)); }
+
 }  // namespace attn

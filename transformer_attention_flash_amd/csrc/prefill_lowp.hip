@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
         for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
             for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sub][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_xor32(mx);
         // Lazy rescaling: the reference maximum m_run moves (and O and l are
         // rescaled) only when a lane's scores would exceed it by more than
         // 2^kLazy; otherwise the probabilities are taken against the stale
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
     }
 
     // ---- normalise and store: lane holds query my_q, dims 32 n + 8 g + 4 lh + (0..3).
-    l_run += __shfl_xor(l_run, 32);
+    l_run = sum_xor32(l_run);
     if (my_q < S) {
         const float inv = 1.0f / l_run;
         float *op = a.out + head_base + (size_t)my_q * row_stride + 4 * lh;

@@ -77,25 +77,6 @@ __device__ __forceinline__ void dma16_small(const float *src, float *lds_base) {
     __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), (lds_void_t *)lds_base, 16, 0, 0);
 }
 
-// Cross-lane reductions over the four lanes i, i + 16, i + 32, i + 48 that
-// hold one query's scores: a swizzle swaps the 16-lane halves of each 32-lane
-// group, and v_permlane32_swap returns, in every lane l, the values of lanes
-// l and l ^ 32 (one in each result), so combining its two results needs no
-// lane mask.
-__device__ __forceinline__ float xor16(float x) {
-    return __uint_as_float(__builtin_amdgcn_ds_swizzle(__float_as_uint(x), 0x401F));  // swap 16-lane halves
-}
-__device__ __forceinline__ float max4(float x) {
-    x = fmaxf(x, xor16(x));
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum4(float x) {
-    x += xor16(x);
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // Wait until this wave has no global loads (including LDS transfers) in flight.
 __device__ __forceinline__ void wait_vmem_all_small() {
     // s_waitcnt vmcnt(0), expcnt/lgkmcnt unconstrained (7 and 15).
