@@ -11,7 +11,9 @@ bfloat16) on top of f32 rounding; the contract asserted here is
 Cases: ragged S across 32/64-key and 128/256-query tiles, every head_dim,
 batch > 1, causal and not, the three work decompositions (4 and 8 waves per
 workgroup, and for small problems at d <= 64 key tiles split over 4 groups of
-2 query waves, at d = 128 over 2 groups of 4, causal too), a non-default and a
+2 query waves, at d = 128 over 2 groups of 4, causal too), the two causal
+eight-wave schedules (pairs of query tiles, one of them walking its keys
+downwards, and single tiles heaviest first), a non-default and a
 negative scale with
 large scores, both formats, and the three prefill workloads at full size
 (sampled rows for the causal one).  The
@@ -101,10 +103,14 @@ def test_prefill_lowp_small_causal_key_groups(case, fmt):
 
 
 EIGHT_WAVE = [
-    # B, S, H, d: B*H*ceil(S/256) >= 512 runs the 256-query, 64-key-tile path; ragged S
+    # B, S, H, d: B*H*ceil(S/256) >= 512 runs the 256-query, 64-key-tile path; ragged S.
+    # Causal, the first three run as pairs of query tiles (T-1-j upwards, then j
+    # downwards from its diagonal); the last, with 3 query tiles per (b, h), as
+    # single tiles heaviest first.
     (2, 1000, 64, 128),
     (4, 777, 32, 64),
     (16, 300, 32, 32),
+    (4, 600, 64, 32),
 ]
 
 
@@ -179,3 +185,44 @@ def test_prefill_lowp_full_size_causal_sampled(fmt):
     want = orc.prefill_rows(rq, rk, rv, sel, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, True)
     got_sel = np.stack([got[b, i, h * cfg.d:(h + 1) * cfg.d] for b, i, h in sel])
     check(got_sel, want, rv, u, f"{fmt} causal full-size sampled rows")
+
+
+LOWP_GRAPH_CASES = [
+    # B, S, H, d: causal eight-wave schedules (pairs of query tiles; single tiles)
+    (16, 300, 32, 32),
+    (4, 600, 64, 32),
+]
+
+
+@pytest.mark.parametrize("case", LOWP_GRAPH_CASES, ids=[f"B{c[0]}_S{c[1]}_H{c[2]}_d{c[3]}" for c in LOWP_GRAPH_CASES])
+def test_prefill_lowp_graph_replays_match_eager(case):
+    """A causal reduced-precision prefill captured into a HIP graph replays to the eager result,
+    bit for bit, over several replays with new inputs and eager prefills in between."""
+    import torch
+    from gpu_common import bits
+    B, S, H, d = case
+    prec, _ = FORMATS["bf16"]
+    rng = np.random.default_rng(990 + S + H)
+    scale = wl.scale_for(d)
+    shape = (B, S, H * d)
+    q_s, k_s, v_s = (to_dev(rng.standard_normal(shape, dtype=np.float32)) for _ in range(3))
+    out_s = torch.zeros(shape, device="cuda:0")
+    note(f"prefill_lowp graph capture B={B} S={S} H={H} d={d}")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up on the capture stream (first-call host queries)
+        taf.attn_prefill_lowp(q_s, k_s, v_s, out_s, B, S, H, d, scale, True, prec)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        taf.attn_prefill_lowp(q_s, k_s, v_s, out_s, B, S, H, d, scale, True, prec)
+    for rep in range(3):
+        q, k, v = (rng.standard_normal(shape, dtype=np.float32) for _ in range(3))
+        for dst, src in ((q_s, q), (k_s, k), (v_s, v)):
+            dst.copy_(to_dev(src))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = to_host(out_s)
+        eager = run_lowp(q, k, v, B, S, H, d, scale, True, prec)
+        assert np.array_equal(bits(got), bits(eager)), f"replay {rep} differs from the eager prefill"

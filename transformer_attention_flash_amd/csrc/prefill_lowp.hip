@@ -105,7 +105,7 @@ __device__ __forceinline__ int vswz(int d) {
 // HM: head-major launch order (the query tiles of one (b, h) run next to each
 // other, so they stream its K/V through the same L2 at about the same time);
 // otherwise query-tile-major, heaviest causal tiles first.
-template <int D, int NW, int KS, int BN, bool CAUSAL, typename T, bool HM = false>
+template <int D, int NW, int KS, int BN, bool CAUSAL, typename T, bool HM = false, bool PAIR = false>
 __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(PrefillArgs a, int32_t n_qtiles,
                                                                           int32_t xcd_remap) {
     constexpr int QW = NW / KS;       // query waves per group
@@ -137,21 +137,43 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
 
     // ---- block -> (b, h, query tile): heavy causal tiles first; with
     // xcd_remap the query tiles of one (b, h) share an XCD (and its L2).
+    // PAIR (causal): the workgroup takes query tiles T-1-j and j of one (b, h)
+    // (T = n_qtiles), so every workgroup has the same number of key tiles, and
+    // the P = ceil(T/2) workgroups of a (b, h) run side by side on one XCD.
+    // The first tile of the pair walks its keys upwards and the second
+    // downwards from its diagonal: all P workgroups then read the same K/V
+    // tile at about the same time in both phases, and it comes from HBM once.
+    static_assert(!PAIR || (CAUSAL && KS == 1), "pairs: causal, one key group");
     const int BH = a.B * a.H;
-    int bh, qt;
+    int bh, qt_first, qt_second = -1;
     {
         const int bid = blockIdx.x;
-        int rank;
-        if (xcd_remap) {
-            const int per_xcd_bh = BH / 8;
-            const int x = bid % 8, t = bid / 8;
-            bh = 8 * (HM ? t / n_qtiles : t % per_xcd_bh) + x;
-            rank = HM ? t % n_qtiles : t / per_xcd_bh;
+        if constexpr (PAIR) {
+            const int P = (n_qtiles + 1) / 2;
+            int j;
+            if (xcd_remap) {
+                const int x = bid % 8, t = bid / 8;
+                bh = 8 * (t / P) + x;
+                j = t % P;
+            } else {
+                bh = bid / P;
+                j = bid % P;
+            }
+            qt_first = n_qtiles - 1 - j;
+            if (j < qt_first) qt_second = j;
         } else {
-            bh = HM ? bid / n_qtiles : bid % BH;
-            rank = HM ? bid % n_qtiles : bid / BH;
+            int rank;
+            if (xcd_remap) {
+                const int per_xcd_bh = BH / 8;
+                const int x = bid % 8, t = bid / 8;
+                bh = 8 * (HM ? t / n_qtiles : t % per_xcd_bh) + x;
+                rank = HM ? t % n_qtiles : t / per_xcd_bh;
+            } else {
+                bh = HM ? bid / n_qtiles : bid % BH;
+                rank = HM ? bid % n_qtiles : bid / BH;
+            }
+            qt_first = CAUSAL ? n_qtiles - 1 - rank : rank;
         }
-        qt = CAUSAL ? n_qtiles - 1 - rank : rank;
     }
     const int b = bh / a.H;
     const int hd = bh % a.H;
@@ -169,310 +191,320 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
     const int lane = tid & 63;
     const int li = lane & 31;
     const int lh = lane >> 5;
-    const int q0 = qt * BM;
-    const int qw0 = q0 + 32 * wave;
-    const int my_q = qw0 + li;
+    constexpr int NPH = PAIR ? 2 : 1;
+#pragma unroll 1
+    for (int ph = 0; ph < NPH; ++ph) {
+        const int qt = ph == 0 ? qt_first : qt_second;
+        if (qt < 0) break;
+        const bool desc = PAIR && ph == 1;  // walk the key tiles from the last one down
+        const int q0 = qt * BM;
+        const int qw0 = q0 + 32 * wave;
+        const int my_q = qw0 + li;
 
-    // ---- Q^T operand: query my_q, dims 16 kk + 8 lh .. +7, rounded.  For a
-    // negative scale the query is negated first (rounding is symmetric, so
-    // the scores are exactly negated) and |scale| is used: the softmax then
-    // always multiplies by a non-negative factor and can take its maximum on
-    // the raw scores.
-    const float qsign = a.scale < 0.f ? -1.f : 1.f;
-    const float qsa = fabsf(a.scale) * kLog2e;  // raw scores to log2 units
-    v8 qop[KK];  // filled below, once the first K/V tile's loads are in flight
-    auto load_q = [&]() {
-        const bool ok = my_q < S;
-        const float *qp = qg + (size_t)(ok ? my_q : 0) * row_stride + 8 * lh;
+        // ---- Q^T operand: query my_q, dims 16 kk + 8 lh .. +7, rounded.  For a
+        // negative scale the query is negated first (rounding is symmetric, so
+        // the scores are exactly negated) and |scale| is used: the softmax then
+        // always multiplies by a non-negative factor and can take its maximum on
+        // the raw scores.
+        const float qsign = a.scale < 0.f ? -1.f : 1.f;
+        const float qsa = fabsf(a.scale) * kLog2e;  // raw scores to log2 units
+        v8 qop[KK];  // filled below, once the first K/V tile's loads are in flight
+        auto load_q = [&]() {
+            const bool ok = my_q < S;
+            const float *qp = qg + (size_t)(ok ? my_q : 0) * row_stride + 8 * lh;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const f32x4 x0 = ok ? *reinterpret_cast<const f32x4 *>(qp + 16 * kk) : f32x4{0, 0, 0, 0};
-            const f32x4 x1 = ok ? *reinterpret_cast<const f32x4 *>(qp + 16 * kk + 4) : f32x4{0, 0, 0, 0};
-            const v4 r0 = round4<T, v4>(x0 * qsign), r1 = round4<T, v4>(x1 * qsign);
-            qop[kk] = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-    };
+            for (int kk = 0; kk < KK; ++kk) {
+                const f32x4 x0 = ok ? *reinterpret_cast<const f32x4 *>(qp + 16 * kk) : f32x4{0, 0, 0, 0};
+                const f32x4 x1 = ok ? *reinterpret_cast<const f32x4 *>(qp + 16 * kk + 4) : f32x4{0, 0, 0, 0};
+                const v4 r0 = round4<T, v4>(x0 * qsign), r1 = round4<T, v4>(x1 * qsign);
+                qop[kk] = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        };
 
-    f32x16 o[NT];
+        f32x16 o[NT];
 #pragma unroll
-    for (int n = 0; n < NT; ++n) o[n] = f32x16{};
-    float m_run = kNegBig;
-    float l_run = 0.f;
+        for (int n = 0; n < NT; ++n) o[n] = f32x16{};
+        float m_run = kNegBig;
+        float l_run = 0.f;
 
-    const int n_ktiles_all = (S + BN - 1) / BN;
-    const int n_ktiles = CAUSAL ? min(n_ktiles_all, (min(q0 + BM, S) - 1) / BN + 1) : n_ktiles_all;
-    const int TG = (n_ktiles + KS - 1) / KS;  // key tiles per group; group grp owns tiles grp*TG ..
-    const int gt0 = grp * TG;
+        const int n_ktiles_all = (S + BN - 1) / BN;
+        const int n_ktiles = CAUSAL ? min(n_ktiles_all, (min(q0 + BM, S) - 1) / BN + 1) : n_ktiles_all;
+        const int TG = (n_ktiles + KS - 1) / KS;  // key tiles per group; group grp owns tiles grp*TG ..
+        const int gt0 = grp * TG;
 
-    // ---- staging: block blk = (key quad kq, dim chunk c).  Element offsets
-    // within a tile are fixed per thread; a tile adds a uniform base, so a
-    // load is a 32-bit offset from a scalar base.  In the last, partial tile
-    // rows past S read row S - 1 (in bounds; their scores are masked and their
-    // probabilities are exactly 0).
-    f32x4 kst[BPT][4], vst[BPT][4];
-    uint32_t goff[BPT];  // element offset of row 4 kq, chunk c, within a tile (row 4 kq + j: + j row_stride)
-    int rowq[BPT];       // 4 kq
-    const uint32_t rs32 = (uint32_t)row_stride;
-#pragma unroll
-    for (int u = 0; u < BPT; ++u) {
-        const int blk = tid + kThreads * u;
-        const int c = blk % (D / 4), kq = blk / (D / 4);
-        rowq[u] = 4 * kq;
-        goff[u] = (uint32_t)((size_t)(4 * kq) * row_stride + 4 * c);
-    }
-    auto load_tile = [&](int kt) {
-        kt += gt0;
-        if (KS > 1 && kt >= n_ktiles) return;  // past this group's range (uniform per group)
-        const size_t tbase = (size_t)kt * BN * row_stride;
-        const float *kt_g = kg + tbase;
-        const float *vt_g = vg + tbase;
-        const bool partial = kt * BN + BN > S;  // uniform
+        // ---- staging: block blk = (key quad kq, dim chunk c).  Element offsets
+        // within a tile are fixed per thread; a tile adds a uniform base, so a
+        // load is a 32-bit offset from a scalar base.  In the last, partial tile
+        // rows past S read row S - 1 (in bounds; their scores are masked and their
+        // probabilities are exactly 0).
+        f32x4 kst[BPT][4], vst[BPT][4];
+        uint32_t goff[BPT];  // element offset of row 4 kq, chunk c, within a tile (row 4 kq + j: + j row_stride)
+        int rowq[BPT];       // 4 kq
+        const uint32_t rs32 = (uint32_t)row_stride;
 #pragma unroll
         for (int u = 0; u < BPT; ++u) {
             const int blk = tid + kThreads * u;
-            if (NBLK % kThreads == 0 || blk < NBLK) {
+            const int c = blk % (D / 4), kq = blk / (D / 4);
+            rowq[u] = 4 * kq;
+            goff[u] = (uint32_t)((size_t)(4 * kq) * row_stride + 4 * c);
+        }
+        auto load_tile = [&](int kt) {
+            kt += gt0;
+            if (desc) kt = n_ktiles - 1 - kt;
+            if (KS > 1 && kt >= n_ktiles) return;  // past this group's range (uniform per group)
+            const size_t tbase = (size_t)kt * BN * row_stride;
+            const float *kt_g = kg + tbase;
+            const float *vt_g = vg + tbase;
+            const bool partial = kt * BN + BN > S;  // uniform
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    uint32_t off = goff[u] + (uint32_t)j * rs32;
-                    if (partial) {
-                        const int over = kt * BN + rowq[u] + j - (S - 1);
-                        if (over > 0) off -= (uint32_t)((size_t)over * row_stride);
+            for (int u = 0; u < BPT; ++u) {
+                const int blk = tid + kThreads * u;
+                if (NBLK % kThreads == 0 || blk < NBLK) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        uint32_t off = goff[u] + (uint32_t)j * rs32;
+                        if (partial) {
+                            const int over = kt * BN + rowq[u] + j - (S - 1);
+                            if (over > 0) off -= (uint32_t)((size_t)over * row_stride);
+                        }
+                        kst[u][j] = *reinterpret_cast<const f32x4 *>(kt_g + off);
+                        vst[u][j] = *reinterpret_cast<const f32x4 *>(vt_g + off);
                     }
-                    kst[u][j] = *reinterpret_cast<const f32x4 *>(kt_g + off);
-                    vst[u][j] = *reinterpret_cast<const f32x4 *>(vt_g + off);
                 }
             }
-        }
-    };
-    auto write_tile = [&](T *Ks, T *Vt) {
-        Ks += grp * BN * KP;
-        Vt += grp * D * BN;
+        };
+        auto write_tile = [&](T *Ks, T *Vt) {
+            Ks += grp * BN * KP;
+            Vt += grp * D * BN;
 #pragma unroll
-        for (int u = 0; u < BPT; ++u) {
-            const int blk = tid + kThreads * u;
-            if (NBLK % kThreads == 0 || blk < NBLK) {
-                const int c = blk % (D / 4), kq = blk / (D / 4);
+            for (int u = 0; u < BPT; ++u) {
+                const int blk = tid + kThreads * u;
+                if (NBLK % kThreads == 0 || blk < NBLK) {
+                    const int c = blk % (D / 4), kq = blk / (D / 4);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *reinterpret_cast<v4 *>(Ks + (4 * kq + j) * KP + 4 * c) = round4<T, v4>(kst[u][j]);
-                const int pq = (kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1);
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<v4 *>(Ks + (4 * kq + j) * KP + 4 * c) = round4<T, v4>(kst[u][j]);
+                    const int pq = (kq & ~3) | ((kq & 1) << 1) | ((kq >> 1) & 1);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int dim = 4 * c + e;
-                    const f32x4 col = {vst[u][0][e], vst[u][1][e], vst[u][2][e], vst[u][3][e]};
-                    *reinterpret_cast<v4 *>(Vt + dim * BN + 8 * ((pq >> 1) ^ vswz<BN>(dim & 31)) + 4 * (pq & 1)) =
-                        round4<T, v4>(col);
+                    for (int e = 0; e < 4; ++e) {
+                        const int dim = 4 * c + e;
+                        const f32x4 col = {vst[u][0][e], vst[u][1][e], vst[u][2][e], vst[u][3][e]};
+                        *reinterpret_cast<v4 *>(Vt + dim * BN + 8 * ((pq >> 1) ^ vswz<BN>(dim & 31)) + 4 * (pq & 1)) =
+                            round4<T, v4>(col);
+                    }
                 }
             }
-        }
-    };
+        };
 
-    auto compute = [&](int kt, const T *Ks, const T *Vt) {
-        kt += gt0;
-        if (KS > 1 && kt >= n_ktiles) return;  // this group's range is done (uniform per group)
-        Ks += grp * BN * KP;
-        Vt += grp * D * BN;
-        const int kt0 = kt * BN;  // first key of the tile
-        if (CAUSAL && kt0 > qw0 + 31) return;  // wave-uniform: whole tile above this wave's diagonal
-        // S^T = K Q^T for the NSUB 32-key sub-tiles of the tile; lane supplies
-        // K[key 32 sub + li][16 kk + 8 lh .. +7].  One sub-tile: all its K
-        // operands are read from LDS before the MFMA chain starts, so the chain
-        // does not wait on an LDS round trip per step.  Two sub-tiles: their
-        // chains are independent and interleaved instead.
-        f32x16 s[NSUB];
-        if constexpr (NSUB == 1) {
-            v8 kop[KK];
+        auto compute = [&](int kt, const T *Ks, const T *Vt) {
+            kt += gt0;
+            if (desc) kt = n_ktiles - 1 - kt;
+            if (KS > 1 && kt >= n_ktiles) return;  // this group's range is done (uniform per group)
+            Ks += grp * BN * KP;
+            Vt += grp * D * BN;
+            const int kt0 = kt * BN;  // first key of the tile
+            if (CAUSAL && kt0 > qw0 + 31) return;  // wave-uniform: whole tile above this wave's diagonal
+            // S^T = K Q^T for the NSUB 32-key sub-tiles of the tile; lane supplies
+            // K[key 32 sub + li][16 kk + 8 lh .. +7].  One sub-tile: all its K
+            // operands are read from LDS before the MFMA chain starts, so the chain
+            // does not wait on an LDS round trip per step.  Two sub-tiles: their
+            // chains are independent and interleaved instead.
+            f32x16 s[NSUB];
+            if constexpr (NSUB == 1) {
+                v8 kop[KK];
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                kop[kk] = *reinterpret_cast<const v8 *>(Ks + li * KP + 8 * lh + 16 * kk);
-            // Keep the reads ahead of the chain (the scheduler would otherwise
-            // sink each read next to its MFMA to save registers).
-            __builtin_amdgcn_sched_barrier(0);
-            // Two independent accumulation chains (even and odd k steps).
-            f32x16 s1 = f32x16{};
-            s[0] = f32x16{};
-            mfma_priority(1);
+                for (int kk = 0; kk < KK; ++kk)
+                    kop[kk] = *reinterpret_cast<const v8 *>(Ks + li * KP + 8 * lh + 16 * kk);
+                // Keep the reads ahead of the chain (the scheduler would otherwise
+                // sink each read next to its MFMA to save registers).
+                __builtin_amdgcn_sched_barrier(0);
+                // Two independent accumulation chains (even and odd k steps).
+                f32x16 s1 = f32x16{};
+                s[0] = f32x16{};
+                mfma_priority(1);
 #pragma unroll
-            for (int kk = 0; kk < KK; kk += 2) {
-                s[0] = Lp<T>::mfma(kop[kk], qop[kk], s[0]);
-                if (kk + 1 < KK) s1 = Lp<T>::mfma(kop[kk + 1], qop[kk + 1], s1);
+                for (int kk = 0; kk < KK; kk += 2) {
+                    s[0] = Lp<T>::mfma(kop[kk], qop[kk], s[0]);
+                    if (kk + 1 < KK) s1 = Lp<T>::mfma(kop[kk + 1], qop[kk + 1], s1);
+                }
+                mfma_priority(0);
+                s[0] += s1;
+            } else {
+#pragma unroll
+                for (int sub = 0; sub < NSUB; ++sub) s[sub] = f32x16{};
+                mfma_priority(1);
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+                    for (int sub = 0; sub < NSUB; ++sub)
+                        s[sub] = Lp<T>::mfma(
+                            *reinterpret_cast<const v8 *>(Ks + (32 * sub + li) * KP + 8 * lh + 16 * kk), qop[kk],
+                            s[sub]);
+                mfma_priority(0);
             }
-            mfma_priority(0);
-            s[0] += s1;
-        } else {
-#pragma unroll
-            for (int sub = 0; sub < NSUB; ++sub) s[sub] = f32x16{};
-            mfma_priority(1);
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
+
+            // Online softmax over the tile's BN keys in raw score units: the
+            // scale (>= 0, see qsa) is folded into the exponent's FMA.
+            const bool need_mask = (kt0 + BN > S) || (CAUSAL && kt0 + BN - 1 > qw0);
+            if (need_mask) {
 #pragma unroll
                 for (int sub = 0; sub < NSUB; ++sub)
-                    s[sub] = Lp<T>::mfma(
-                        *reinterpret_cast<const v8 *>(Ks + (32 * sub + li) * KP + 8 * lh + 16 * kk), qop[kk], s[sub]);
-            mfma_priority(0);
-        }
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = kt0 + 32 * sub + mrow(v, lh);
+                        if (key >= S || (CAUSAL && key > my_q)) s[sub][v] = -INFINITY;
+                    }
+            }
+            float mx = s[0][0];
+#pragma unroll
+            for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sub][v]);
+            mx = max_xor32(mx);
+            // Lazy rescaling: the reference maximum m_run moves (and O and l are
+            // rescaled) only when a lane's scores would exceed it by more than
+            // 2^kLazy; otherwise the probabilities are taken against the stale
+            // reference and stay below 2^kLazy, well inside f32 and both 16-bit
+            // formats.  The decision is wave-uniform, so most tiles skip the
+            // 16 * NT multiplies of the rescale.
+            if (__any((mx - m_run) * qsa > kLazy)) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = fast_exp2((m_run - m_new) * qsa);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int n = 0; n < NT; ++n) o[n] *= alpha;
+            }
+            const float mb = m_run * qsa;
+            float psum = 0.f;
+            // Probabilities: summed in f32 and rounded at once to the P.V operands
+            // (score registers 8t .. 8t + 7 of a sub-tile are the k slots of its
+            // step t).  Masked scores give exact zeros (also for scale 0, where the
+            // exponent alone would not); tiles without masked keys skip the test.
+            v8 pop[NSUB][2];
+            auto probabilities = [&](auto masked) {
+#pragma unroll
+                for (int sub = 0; sub < NSUB; ++sub)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        f32x4 pr[2];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float sv = s[sub][8 * t + j];
+                            float pv = fast_exp2(fmaf(sv, qsa, -mb));
+                            if constexpr (decltype(masked)::value) pv = (sv == -INFINITY) ? 0.f : pv;
+                            pr[j / 4][j % 4] = pv;
+                            psum += pv;
+                        }
+                        pop[sub][t] = __builtin_shufflevector(round4<T, v4>(pr[0]), round4<T, v4>(pr[1]), 0, 1, 2, 3, 4,
+                                                              5, 6, 7);
+                    }
+            };
+            if (need_mask)
+                probabilities(std::true_type{});
+            else
+                probabilities(std::false_type{});
+            l_run += psum;
 
-        // Online softmax over the tile's BN keys in raw score units: the
-        // scale (>= 0, see qsa) is folded into the exponent's FMA.
-        const bool need_mask = (kt0 + BN > S) || (CAUSAL && kt0 + BN - 1 > qw0);
-        if (need_mask) {
+            // O^T += V^T P^T over the 16-key halves t of each sub-tile: this lane's
+            // k slots are keys 16t + 4lh + (0..3) and 16t + 8 + 4lh + (0..3).  All
+            // V operands of a sub-tile are read before its MFMAs, as for K.
 #pragma unroll
-            for (int sub = 0; sub < NSUB; ++sub)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int key = kt0 + 32 * sub + mrow(v, lh);
-                    if (key >= S || (CAUSAL && key > my_q)) s[sub][v] = -INFINITY;
-                }
-        }
-        float mx = s[0][0];
-#pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sub][v]);
-        mx = max_xor32(mx);
-        // Lazy rescaling: the reference maximum m_run moves (and O and l are
-        // rescaled) only when a lane's scores would exceed it by more than
-        // 2^kLazy; otherwise the probabilities are taken against the stale
-        // reference and stay below 2^kLazy, well inside f32 and both 16-bit
-        // formats.  The decision is wave-uniform, so most tiles skip the
-        // 16 * NT multiplies of the rescale.
-        if (__any((mx - m_run) * qsa > kLazy)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = fast_exp2((m_run - m_new) * qsa);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int n = 0; n < NT; ++n) o[n] *= alpha;
-        }
-        const float mb = m_run * qsa;
-        float psum = 0.f;
-        // Probabilities: summed in f32 and rounded at once to the P.V operands
-        // (score registers 8t .. 8t + 7 of a sub-tile are the k slots of its
-        // step t).  Masked scores give exact zeros (also for scale 0, where the
-        // exponent alone would not); tiles without masked keys skip the test.
-        v8 pop[NSUB][2];
-        auto probabilities = [&](auto masked) {
-#pragma unroll
-            for (int sub = 0; sub < NSUB; ++sub)
+            for (int sub = 0; sub < NSUB; ++sub) {
+                __builtin_amdgcn_sched_barrier(0);  // not above the previous sub-tile's MFMAs (registers)
+                v8 vop[2][NT];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    f32x4 pr[2];
+                    const int pair = 4 * sub + 2 * t + lh;  // key groups 4t + lh and 4t + 2 + lh of the sub-tile
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float sv = s[sub][8 * t + j];
-                        float pv = fast_exp2(fmaf(sv, qsa, -mb));
-                        if constexpr (decltype(masked)::value) pv = (sv == -INFINITY) ? 0.f : pv;
-                        pr[j / 4][j % 4] = pv;
-                        psum += pv;
+                    for (int n = 0; n < NT; ++n) {
+                        const int dim = 32 * n + li;
+                        vop[t][n] = *reinterpret_cast<const v8 *>(Vt + dim * BN + 8 * (pair ^ vswz<BN>(li)));
                     }
-                    pop[sub][t] = __builtin_shufflevector(round4<T, v4>(pr[0]), round4<T, v4>(pr[1]), 0, 1, 2, 3, 4,
-                                                          5, 6, 7);
                 }
-        };
-        if (need_mask)
-            probabilities(std::true_type{});
-        else
-            probabilities(std::false_type{});
-        l_run += psum;
-
-        // O^T += V^T P^T over the 16-key halves t of each sub-tile: this lane's
-        // k slots are keys 16t + 4lh + (0..3) and 16t + 8 + 4lh + (0..3).  All
-        // V operands of a sub-tile are read before its MFMAs, as for K.
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_priority(1);
 #pragma unroll
-        for (int sub = 0; sub < NSUB; ++sub) {
-            __builtin_amdgcn_sched_barrier(0);  // not above the previous sub-tile's MFMAs (registers)
-            v8 vop[2][NT];
+                for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int pair = 4 * sub + 2 * t + lh;  // key groups 4t + lh and 4t + 2 + lh of the sub-tile
-#pragma unroll
-                for (int n = 0; n < NT; ++n) {
-                    const int dim = 32 * n + li;
-                    vop[t][n] = *reinterpret_cast<const v8 *>(Vt + dim * BN + 8 * (pair ^ vswz<BN>(li)));
-                }
+                    for (int n = 0; n < NT; ++n) o[n] = Lp<T>::mfma(vop[t][n], pop[sub][t], o[n]);
+                mfma_priority(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_priority(1);
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int n = 0; n < NT; ++n) o[n] = Lp<T>::mfma(vop[t][n], pop[sub][t], o[n]);
-            mfma_priority(0);
-        }
-    };
-
-    // ---- pipeline: tile kt+1 is in registers while tile kt is consumed from
-    // LDS; after the barrier that ends tile kt, tile kt+2's loads go out.
-    load_tile(0);
-    load_q();  // the Q and first-tile loads overlap: one memory round trip, not two
-    write_tile(Ks0, Vt0);
-    __syncthreads();
-    if (TG > 1) load_tile(1);
-    for (int kt = 0; kt < TG; kt += 2) {
-        compute(kt, Ks0, Vt0);
-        if (kt + 1 < TG) write_tile(Ks1, Vt1);
-        __syncthreads();
-        if (kt + 2 < TG) load_tile(kt + 2);
-        if (kt + 1 < TG) {
-            compute(kt + 1, Ks1, Vt1);
-            if (kt + 2 < TG) write_tile(Ks0, Vt0);
-            __syncthreads();
-            if (kt + 3 < TG) load_tile(kt + 3);
-        }
-    }
-
-    // ---- merge the key groups: groups 1.. park (reference max, partial sum,
-    // output) of each lane, group 0 folds them in.  Every group's softmax
-    // state is relative to its own reference max m (probabilities
-    // 2^((s - m) qsa)), so the usual rescaling applies.
-    if constexpr (KS > 1) {
-        // The tile buffers are free: the last tile step ended in a barrier.
-        auto slot_ptr = [&](int sl) -> float * {
-            if (!kParkInTiles) return Red + sl * SLOT;
-            if (sl < PK) return reinterpret_cast<float *>(Ks0) + sl * SLOT;
-            sl -= PK;
-            if (sl < PV) return reinterpret_cast<float *>(Vt0) + sl * SLOT;
-            sl -= PV;
-            if (sl < PK) return reinterpret_cast<float *>(Ks1) + sl * SLOT;
-            return reinterpret_cast<float *>(Vt1) + (sl - PK) * SLOT;
         };
-        if (grp > 0) {
-            float *dst = slot_ptr((grp - 1) * QW + wave) + lane;
-#pragma unroll
-            for (int n = 0; n < NT; ++n)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) dst[(16 * n + v) * kWave] = o[n][v];
-            dst[16 * NT * kWave] = m_run;
-            dst[(16 * NT + 1) * kWave] = l_run;
-        }
-        __syncthreads();
-        if (grp > 0) return;
-#pragma unroll
-        for (int g = 1; g < KS; ++g) {
-            const float *src = slot_ptr((g - 1) * QW + wave) + lane;
-            const float m_g = src[16 * NT * kWave];
-            const float m_new = fmaxf(m_run, m_g);
-            const float keep = fast_exp2((m_run - m_new) * qsa), take = fast_exp2((m_g - m_new) * qsa);
-            l_run = l_run * keep + src[(16 * NT + 1) * kWave] * take;
-#pragma unroll
-            for (int n = 0; n < NT; ++n)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) o[n][v] = o[n][v] * keep + src[(16 * n + v) * kWave] * take;
-            m_run = m_new;
-        }
-    }
 
-    // ---- normalise and store: lane holds query my_q, dims 32 n + 8 g + 4 lh + (0..3).
-    l_run = sum_xor32(l_run);
-    if (my_q < S) {
-        const float inv = 1.0f / l_run;
-        float *op = a.out + head_base + (size_t)my_q * row_stride + 4 * lh;
+        // ---- pipeline: tile kt+1 is in registers while tile kt is consumed from
+        // LDS; after the barrier that ends tile kt, tile kt+2's loads go out.
+        load_tile(0);
+        load_q();  // the Q and first-tile loads overlap: one memory round trip, not two
+        write_tile(Ks0, Vt0);
+        __syncthreads();
+        if (TG > 1) load_tile(1);
+        for (int kt = 0; kt < TG; kt += 2) {
+            compute(kt, Ks0, Vt0);
+            if (kt + 1 < TG) write_tile(Ks1, Vt1);
+            __syncthreads();
+            if (kt + 2 < TG) load_tile(kt + 2);
+            if (kt + 1 < TG) {
+                compute(kt + 1, Ks1, Vt1);
+                if (kt + 2 < TG) write_tile(Ks0, Vt0);
+                __syncthreads();
+                if (kt + 3 < TG) load_tile(kt + 3);
+            }
+        }
+
+        // ---- merge the key groups: groups 1.. park (reference max, partial sum,
+        // output) of each lane, group 0 folds them in.  Every group's softmax
+        // state is relative to its own reference max m (probabilities
+        // 2^((s - m) qsa)), so the usual rescaling applies.
+        if constexpr (KS > 1) {
+            // The tile buffers are free: the last tile step ended in a barrier.
+            auto slot_ptr = [&](int sl) -> float * {
+                if (!kParkInTiles) return Red + sl * SLOT;
+                if (sl < PK) return reinterpret_cast<float *>(Ks0) + sl * SLOT;
+                sl -= PK;
+                if (sl < PV) return reinterpret_cast<float *>(Vt0) + sl * SLOT;
+                sl -= PV;
+                if (sl < PK) return reinterpret_cast<float *>(Ks1) + sl * SLOT;
+                return reinterpret_cast<float *>(Vt1) + (sl - PK) * SLOT;
+            };
+            if (grp > 0) {
+                float *dst = slot_ptr((grp - 1) * QW + wave) + lane;
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
+                for (int n = 0; n < NT; ++n)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<f32x4 *>(op + 32 * n + 8 * g) =
-                    f32x4{o[n][4 * g] * inv, o[n][4 * g + 1] * inv, o[n][4 * g + 2] * inv, o[n][4 * g + 3] * inv};
+                    for (int v = 0; v < 16; ++v) dst[(16 * n + v) * kWave] = o[n][v];
+                dst[16 * NT * kWave] = m_run;
+                dst[(16 * NT + 1) * kWave] = l_run;
+            }
+            __syncthreads();
+            if (grp > 0) return;
+#pragma unroll
+            for (int g = 1; g < KS; ++g) {
+                const float *src = slot_ptr((g - 1) * QW + wave) + lane;
+                const float m_g = src[16 * NT * kWave];
+                const float m_new = fmaxf(m_run, m_g);
+                const float keep = fast_exp2((m_run - m_new) * qsa), take = fast_exp2((m_g - m_new) * qsa);
+                l_run = l_run * keep + src[(16 * NT + 1) * kWave] * take;
+#pragma unroll
+                for (int n = 0; n < NT; ++n)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) o[n][v] = o[n][v] * keep + src[(16 * n + v) * kWave] * take;
+                m_run = m_new;
+            }
+        }
+
+        // ---- normalise and store: lane holds query my_q, dims 32 n + 8 g + 4 lh + (0..3).
+        l_run = sum_xor32(l_run);
+        if (my_q < S) {
+            const float inv = 1.0f / l_run;
+            float *op = a.out + head_base + (size_t)my_q * row_stride + 4 * lh;
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<f32x4 *>(op + 32 * n + 8 * g) =
+                        f32x4{o[n][4 * g] * inv, o[n][4 * g + 1] * inv, o[n][4 * g + 2] * inv, o[n][4 * g + 3] * inv};
+        }
     }
 }
 
@@ -480,6 +512,38 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
 // per query; four waves keep smaller problems spread over the CUs.  One
 // eight-wave workgroup fills a CU, so eight waves are used when that still
 // gives at least two workgroups per CU.
+// Compute units of the current device.
+int32_t cu_count() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 256;
+    return cus;
+}
+
+// Workgroups of `threads` threads of `kernel` that one CU holds at once (at
+// least 1).
+int32_t blocks_per_cu(const void *kernel, int threads) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) return 1;
+    return n;
+}
+
+// Causal prefill over BH (batch, head) rows of T query tiles, each tile with
+// `p` tile-sized blocks of cached keys in front: whether workgroups that take
+// query tiles T-1-j and j (the same 2p + T + 1 key blocks each, in
+// ceil(BH ceil(T/2) / slots) rounds) finish no later than single tiles taken
+// heaviest first (at best the heaviest tile, p + T blocks, or the mean load
+// per slot).  Ties go to the pairs: their workgroups read a row's K/V about
+// once between them.
+bool pair_query_tiles(int64_t BH, int64_t T, int64_t p, int64_t slots) {
+    if (T < 2 || slots < 1) return false;
+    const int64_t paired = (BH * ((T + 1) / 2) + slots - 1) / slots * (2 * p + T + 1);
+    const int64_t total = BH * (p * T + T * (T + 1) / 2);
+    const int64_t single = total / slots + (total % slots != 0);
+    return paired <= (single > p + T ? single : p + T);
+}
+
 template <int D, bool CAUSAL, typename T>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const int32_t BH = a.B * a.H;
@@ -487,11 +551,27 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const int32_t tiles8 = (a.S + 255) / 256;
     if ((int64_t)BH * tiles8 >= 512) {
         // Non-causal: head-major order (a (b, h)'s query tiles share its K/V in
-        // L2: B=4 S=2048 H=32 d=128 412 -> 363 us).  Causal: heaviest tiles
-        // first (head-major makes the heavy tiles of the last heads run last).
-        dim3 grid((unsigned)(BH * tiles8));
-        prefill_lowp_kernel<D, 8, 1, 64, CAUSAL, T, !CAUSAL><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8,
-                                                                                                  xcd_remap);
+        // L2: B=4 S=2048 H=32 d=128 412 -> 363 us).  Causal: pairs of query
+        // tiles when they fill the device as well as single tiles do (B=4
+        // S=2048 H=32 d=128: HBM reads 1.00 -> 0.55 GB, about 2% faster), else
+        // single tiles heaviest first (head-major single tiles would run the
+        // heavy tiles of the last heads last).
+        if constexpr (CAUSAL) {
+            static const int32_t occ =
+                blocks_per_cu((const void *)prefill_lowp_kernel<D, 8, 1, 64, true, T, false, true>, kWave * 8);
+            if (pair_query_tiles(BH, tiles8, 0, (int64_t)cu_count() * occ)) {
+                dim3 grid((unsigned)(BH * ((tiles8 + 1) / 2)));
+                prefill_lowp_kernel<D, 8, 1, 64, true, T, false, true>
+                    <<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
+            } else {
+                dim3 grid((unsigned)(BH * tiles8));
+                prefill_lowp_kernel<D, 8, 1, 64, true, T><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
+            }
+        } else {
+            dim3 grid((unsigned)(BH * tiles8));
+            prefill_lowp_kernel<D, 8, 1, 64, false, T, true><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8,
+                                                                                                 xcd_remap);
+        }
         return hipGetLastError();
     }
     const int32_t tiles4 = (a.S + 127) / 128;
