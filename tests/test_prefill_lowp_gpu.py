@@ -111,6 +111,8 @@ EIGHT_WAVE = [
     (4, 777, 32, 64),
     (16, 300, 32, 32),
     (4, 600, 64, 32),
+    # B*H not a multiple of 8 (no XCD grouping); causal, 64 pairs of 128 query tiles per head
+    (1, 32768, 4, 32),
 ]
 
 
