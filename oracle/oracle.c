@@ -42,6 +42,7 @@
  * Build: gcc -O2 -fopenmp -fPIC -shared oracle.c -o liboracle.so -lm
  * (no -ffast-math: the IEEE semantics of exp and of the sums are relied on).
  */
+#include <complex.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -364,15 +365,15 @@ int oracle_prefill_cached_rows(const float *q, const float *k_new, const float *
     return failed ? -1 : 0;
 }
 
-/* GPT-NeoX half-split partial rotary position embedding (trustformers-core
- * 0.2.0 ..., `rope_neox_gpu_to_gpu` and the test helper `rope_reference`;
- * realizar 0.8.5 ..., `apply_rope_to_buffer`, the rotary_ndims = head_dim case
- * with base = rope theta).  x: n_rows rows of H heads of d floats; row t is at
- * absolute position pos[t].  For each head and i < half = rotary_ndims / 2:
- *   freq_i = base^(-2 i / rotary_ndims),  a = pos * freq_i,
- *   y_i        = x_i cos a - x_{i+half} sin a,
- *   y_{i+half} = x_i sin a + x_{i+half} cos a,
- * and y_l = x_l for l >= rotary_ndims.  out: same shape, f64. */
+/* Rotary position embedding, GPT-NeoX half-split convention (trustformers-core
+ * 0.2.0 ..., `rope_neox_gpu_to_gpu`; realizar 0.8.5 ..., `apply_rope_to_buffer`,
+ * the rotary_ndims = head_dim case with base = rope theta), written from what
+ * the rotation is.  With half = rotary_ndims / 2, dims k and k + half of a head
+ * form one complex number z_k = x_k + i x_{k+half}.  At position p the
+ * embedding turns z_k through the angle p * base^(-2k / rotary_ndims), i.e.
+ * multiplies it by the unit complex number of that angle, and leaves every
+ * dim >= rotary_ndims as it is.  x: n_rows rows of H heads of d floats, row t
+ * at absolute position pos[t].  out: same shape, f64. */
 int oracle_rope(const float *x, const int32_t *pos, double *out, int64_t n_rows, int64_t H,
                 int64_t d, int64_t rotary_ndims, double base)
 {
@@ -381,19 +382,20 @@ int oracle_rope(const float *x, const int32_t *pos, double *out, int64_t n_rows,
     if (!(base > 0.0)) return -1;
 #pragma omp parallel for schedule(static)
     for (t = 0; t < n_rows; ++t) {
-        int64_t h, i, l, half = rotary_ndims / 2;
+        const int64_t half = rotary_ndims / 2;
+        int64_t h, k, l;
         for (h = 0; h < H; ++h) {
-            const float *xr = x + (t * H + h) * d;
-            double *yr = out + (t * H + h) * d;
-            for (l = 0; l < d; ++l) yr[l] = (double)xr[l];
-            for (i = 0; i < half; ++i) {
-                double freq = pow(base, -2.0 * (double)i / (double)rotary_ndims);
-                double a = (double)pos[t] * freq;
-                double c = cos(a), sn = sin(a);
-                double x1 = (double)xr[i], x2 = (double)xr[i + half];
-                yr[i] = x1 * c - x2 * sn;
-                yr[i + half] = x1 * sn + x2 * c;
+            const float *src = x + (t * H + h) * d;
+            double *dst = out + (t * H + h) * d;
+            for (k = 0; k < half; ++k) {
+                double a = (double)pos[t] * pow(base, -2.0 * (double)k / (double)rotary_ndims);
+                double complex turn = cexp(I * a);
+                double complex z = (double)src[k] + I * (double)src[k + half];
+                z = z * turn;
+                dst[k] = creal(z);
+                dst[k + half] = cimag(z);
             }
+            for (l = rotary_ndims; l < d; ++l) dst[l] = (double)src[l];
         }
     }
     return 0;

@@ -66,15 +66,17 @@ MUTANTS = [
     ("round16_no_overflow", "if (fabs(r) > maxv) return copysign(INFINITY, x);", "(void)maxv;"),
     ("lowp_v_not_rounded", "oracle_round16(v, rv, n, fmt) == 0)\n        rc = oracle_prefill(rq, rk, rv,",
      "oracle_round16(v, rv, n, fmt) == 0)\n        rc = oracle_prefill(rq, rk, v,"),
-    ("rope_sign_flip", "yr[i] = x1 * c - x2 * sn;", "yr[i] = x1 * c + x2 * sn;"),
-    ("rope_sin_cos_swapped", "yr[i + half] = x1 * sn + x2 * c;", "yr[i + half] = x1 * c + x2 * sn;"),
-    ("rope_exponent_uses_head_dim", "-2.0 * (double)i / (double)rotary_ndims", "-2.0 * (double)i / (double)d"),
-    ("rope_exponent_off_by_one", "-2.0 * (double)i / (double)rotary_ndims", "-2.0 * (double)(i + 1) / (double)rotary_ndims"),
-    ("rope_adjacent_pairs", "double x1 = (double)xr[i], x2 = (double)xr[i + half];",
-     "double x1 = (double)xr[2 * i], x2 = (double)xr[2 * i + 1];"),
-    ("rope_row_index_as_position", "double a = (double)pos[t] * freq;", "double a = (double)t * freq;"),
-    ("rope_tail_zeroed", "for (l = 0; l < d; ++l) yr[l] = (double)xr[l];",
-     "for (l = 0; l < d; ++l) yr[l] = l < rotary_ndims ? (double)xr[l] : 0.0;"),
+    ("rope_sign_flip", "z = z * turn;", "z = z * conj(turn);"),
+    ("rope_sin_cos_swapped", "double complex turn = cexp(I * a);", "double complex turn = sin(a) + I * cos(a);"),
+    ("rope_exponent_uses_head_dim", "-2.0 * (double)k / (double)rotary_ndims", "-2.0 * (double)k / (double)d"),
+    ("rope_exponent_off_by_one", "-2.0 * (double)k / (double)rotary_ndims", "-2.0 * (double)(k + 1) / (double)rotary_ndims"),
+    ("rope_adjacent_pairs", "double complex z = (double)src[k] + I * (double)src[k + half];",
+     "double complex z = (double)src[2 * k] + I * (double)src[2 * k + 1];"),
+    ("rope_real_imag_swapped", "dst[k] = creal(z);\n                dst[k + half] = cimag(z);",
+     "dst[k] = cimag(z);\n                dst[k + half] = creal(z);"),
+    ("rope_row_index_as_position", "double a = (double)pos[t] * pow(", "double a = (double)t * pow("),
+    ("rope_tail_zeroed", "for (l = rotary_ndims; l < d; ++l) dst[l] = (double)src[l];",
+     "for (l = rotary_ndims; l < d; ++l) dst[l] = 0.0;"),
 ]
 
 
