@@ -174,7 +174,7 @@ int attn_prefill_cached(const float *q, const float *k_new, const float *v_new, 
 /*
  * Bytes of device workspace attn_decode_gqa_batched needs for these sizes
  * (per-split partial maxima, sums and unnormalised outputs).  Returns 0 when
- * the sizes are invalid.  Pure host arithmetic; no HIP call.
+ * the sizes are invalid or max_len > 2^30.  Pure host arithmetic; no HIP call.
  */
 size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                    int32_t max_len);
@@ -202,9 +202,9 @@ size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t 
  * Errors: NULL pointer; M not in [1, 32], num_heads/num_kv_heads/max_len <= 0,
  * num_kv_heads > num_heads, num_heads % num_kv_heads != 0, a seq_lens value
  * outside [0, max_len], scale not finite (INVALID_DIM); head_dim not in
- * {32, 64, 128} or misaligned pointer (UNSUPPORTED); an element count >= 2^40
- * (OVERFLOW); workspace too small (WORKSPACE); out overlapping an input or
- * the workspace (ALIAS).
+ * {32, 64, 128} or misaligned pointer (UNSUPPORTED); max_len > 2^30 or an
+ * element count >= 2^40 (OVERFLOW); workspace too small (WORKSPACE); out
+ * overlapping an input or the workspace (ALIAS).
  */
 int attn_decode_gqa_batched(const float *q, const float *k_cache, const float *v_cache,
                             const int32_t *seq_lens, float *out, int32_t num_seqs,

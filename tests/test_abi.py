@@ -136,6 +136,17 @@ def test_decode_workspace_bytes(lib):
     assert lib.attn_decode_workspace_bytes(0, 8, 128, 16) == 0
     assert lib.attn_decode_workspace_bytes(33, 8, 128, 16) == 0
     assert lib.attn_decode_workspace_bytes(2, 8, 80, 16) == 0
+    # The largest supported cache: 2^30 rows, 64 key blocks of 2^24 keys.
+    assert lib.attn_decode_workspace_bytes(1, 1, 32, 2**30) == 64 * 34 * 4
+    # Beyond it, up to the int32 limit, the size is refused rather than overflowing.
+    assert lib.attn_decode_workspace_bytes(1, 1, 32, 2**30 + 1) == 0
+    assert lib.attn_decode_workspace_bytes(1, 1, 32, 2**31 - 1) == 0
+
+
+def test_decode_refuses_max_len_past_limit(lib):
+    # Validated before any size arithmetic that could overflow; nothing is launched.
+    assert decode(lib, max_len=2**31 - 1, ws_bytes=2**40) == OVF
+    assert decode(lib, max_len=2**30 + 1, ws_bytes=2**40) == OVF
 
 
 def scatter(lib, kn=A, vn=B_, kc=C_, vc=O_, lens=(0, 3), M=2, n_new=2, Hkv=2, d=64, max_len=8):

@@ -20,6 +20,8 @@ using attn::SeqInts;
 
 constexpr int64_t kMaxElems32 = (int64_t(1) << 31) - 1;  // prefill indexes tokens*H*D in int32-safe ranges
 constexpr int64_t kMaxElems = int64_t(1) << 40;          // decode/scatter element-count bound
+// Decode cache rows: key positions plus one chunk step stay inside int32.
+constexpr int32_t kMaxDecodeLen = int32_t(1) << 30;
 
 bool head_dim_ok(int32_t d) { return d == 32 || d == 64 || d == 128; }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -75,6 +77,7 @@ int prepare_decode(const float *q, const float *k_cache, const float *v_cache, c
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
         !aligned16(workspace))
         return ATTN_ERR_UNSUPPORTED;
+    if (max_len > kMaxDecodeLen) return ATTN_ERR_OVERFLOW;
     int64_t q_elems, cache_elems;
     if (!checked_mul({num_seqs, num_heads, head_dim}, kMaxElems, &q_elems) ||
         !checked_mul({num_seqs, num_kv_heads, max_len, head_dim}, kMaxElems, &cache_elems))
@@ -275,7 +278,7 @@ int attn_prefill_cached(const float *q, const float *k_new, const float *v_new, 
 size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                    int32_t max_len) {
     if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS || num_heads <= 0 || max_len <= 0) return 0;
-    if (!head_dim_ok(head_dim)) return 0;
+    if (!head_dim_ok(head_dim) || max_len > kMaxDecodeLen) return 0;
     int64_t slots;
     if (!checked_mul({num_seqs, num_heads, attn::decode_max_splits(max_len), head_dim + 2}, kMaxElems,
                      &slots))

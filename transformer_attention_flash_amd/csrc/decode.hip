@@ -398,11 +398,12 @@ constexpr int32_t kSpanQuantum = kWavesPerBlock * kChunk;  // keys: one chunk pe
 constexpr int32_t kMaxKeyBlocks = 64;                        // per (sequence, head): workspace bound
 
 // Smallest key-block span for a cache of max_len rows: a power-of-two multiple
-// of the quantum that keeps a sequence at <= kMaxKeyBlocks key blocks.
+// of the quantum that keeps a sequence at <= kMaxKeyBlocks key blocks (64-bit
+// arithmetic: max_len may be any positive int32).
 int32_t span_floor(int32_t max_len) {
-    int32_t s = kSpanQuantum;
-    while ((max_len + s - 1) / s > kMaxKeyBlocks) s *= 2;
-    return s;
+    int64_t s = kSpanQuantum;
+    while (((int64_t)max_len + s - 1) / s > kMaxKeyBlocks) s *= 2;
+    return (int32_t)s;
 }
 
 // The decode grid is this many times what the device holds at once (one
@@ -442,8 +443,8 @@ int32_t capacity_for(int32_t D) {
 }  // namespace
 
 int32_t decode_max_splits(int32_t max_len) {
-    const int32_t sf = span_floor(max_len);
-    return (max_len + sf - 1) / sf;
+    const int64_t sf = span_floor(max_len);
+    return (int32_t)(((int64_t)max_len + sf - 1) / sf);
 }
 
 size_t decode_workspace_bytes(int64_t M, int64_t H, int64_t D, int64_t max_len) {
@@ -474,12 +475,12 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
         map.span[i] = sf;
         if (L == 0) continue;
         const double want = (double)L * target / (double)total;  // key blocks per (kh, hb) unit
-        const int32_t nb = want < 1.0 ? 1 : (int32_t)(want + 0.5);
-        int32_t span = (L + nb - 1) / nb;
+        const int64_t nb = want < 1.0 ? 1 : (int64_t)(want + 0.5);
+        int64_t span = ((int64_t)L + nb - 1) / nb;
         span = ((span + kSpanQuantum - 1) / kSpanQuantum) * kSpanQuantum;
         if (span < sf) span = sf;
-        map.span[i] = span;
-        map.nkblk[i] = (L + span - 1) / span;
+        map.span[i] = (int32_t)span;
+        map.nkblk[i] = (int32_t)(((int64_t)L + span - 1) / span);
     }
     for (int i = a.M; i < ATTN_MAX_SEQS; ++i) {
         map.nkblk[i] = 0;
