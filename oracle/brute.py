@@ -1,10 +1,15 @@
-"""Independent numpy fp64 brute force for tiny attention shapes.
+"""Independent numpy fp64 formulation of the attention definitions.
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  A second formulation
 of the same definitions as ``oracle.c``, written differently on purpose so the
-two cannot share a mistake: heads are split with reshapes, scores are formed
-as full matrices, the causal mask is a lower-triangular boolean mask, and the
-softmax is taken over whole rows of the masked matrix.
+two cannot share a mistake: heads are split with reshapes, each head's scores
+are formed as one full matrix by a matrix product, the causal mask is a
+lower-triangular (or position-compared) boolean mask, and the softmax is
+taken over whole rows of the masked matrix.  The pins check it against
+``oracle.c`` on every tiny shape and on medium ones; the GPU tests use it for
+whole-output checks of large results, where its matrix products (BLAS, fp64)
+and one worker thread per independent head make it fast enough.  Heads are
+independent, so the thread count changes no result.
 
 Definitions: trueno-gpu 0.4.11 ``src/memory/resident/attention.rs``,
 ``batched_multihead_attention`` (softmax(Q K^T / sqrt(d_k)) V per head over
@@ -16,43 +21,77 @@ realizar 0.8.5 ``src/cuda/executor/cache_from_cache_from_kv_cache.rs``,
 """
 from __future__ import annotations
 
+import itertools
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
+_WORKERS = max(1, min(16, os.cpu_count() or 1))
 
-def _softmax_rows(s: np.ndarray, visible: np.ndarray) -> np.ndarray:
-    s = np.where(visible, s, -np.inf)
-    s = s - s.max(axis=-1, keepdims=True)
-    e = np.where(visible, np.exp(s), 0.0)
+
+def _softmax_rows(s: np.ndarray, visible: np.ndarray | None) -> np.ndarray:
+    if visible is None:
+        e = np.exp(s - s.max(axis=-1, keepdims=True))
+    else:
+        s = np.where(visible, s, -np.inf)
+        s = s - s.max(axis=-1, keepdims=True)
+        e = np.where(visible, np.exp(s), 0.0)
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def _attend(q: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float,
+            visible: np.ndarray | None) -> np.ndarray:
+    """One head: softmax(scale * q keys^T, masked) vals, with q [n, d], keys and vals [L, d]."""
+    s = scale * (q.astype(np.float64) @ keys.astype(np.float64).T)          # [n, L]
+    return _softmax_rows(s, visible) @ vals.astype(np.float64)              # [n, d]
+
+
+def _each(fn, units) -> None:
+    """fn(u) for every independent unit u, on a pool of threads (BLAS kept to one thread each)."""
+    units = list(units)
+    if len(units) <= 1 or _WORKERS == 1:
+        for u in units:
+            fn(u)
+        return
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(min(_WORKERS, len(units))) as ex:
+        for _ in ex.map(fn, units):
+            pass
+
+
 def prefill(q, k, v, B, S, H, d, scale, causal):
-    qh = np.asarray(q, dtype=np.float64).reshape(B, S, H, d).transpose(0, 2, 1, 3)
-    kh = np.asarray(k, dtype=np.float64).reshape(B, S, H, d).transpose(0, 2, 1, 3)
-    vh = np.asarray(v, dtype=np.float64).reshape(B, S, H, d).transpose(0, 2, 1, 3)
-    s = float(np.float32(scale)) * (qh @ kh.transpose(0, 1, 3, 2))          # [B, H, S, S]
-    visible = np.tril(np.ones((S, S), dtype=bool)) if causal else np.ones((S, S), dtype=bool)
-    p = _softmax_rows(s, visible[None, None])
-    o = p @ vh                                                               # [B, H, S, d]
-    return o.transpose(0, 2, 1, 3).reshape(B, S, H * d)
+    qh = np.asarray(q, dtype=np.float32).reshape(B, S, H, d)
+    kh = np.asarray(k, dtype=np.float32).reshape(B, S, H, d)
+    vh = np.asarray(v, dtype=np.float32).reshape(B, S, H, d)
+    sc = float(np.float32(scale))
+    visible = np.tril(np.ones((S, S), dtype=bool)) if causal else None
+    out = np.empty((B, S, H, d))
+
+    def unit(bh):
+        b, h = bh
+        out[b, :, h, :] = _attend(qh[b, :, h, :], kh[b, :, h, :], vh[b, :, h, :], sc, visible)
+
+    _each(unit, itertools.product(range(B), range(H)))
+    return out.reshape(B, S, H * d)
 
 
 def decode(q, k_cache, v_cache, lens, M, H, Hkv, d, max_len, scale):
     g = H // Hkv
-    qm = np.asarray(q, dtype=np.float64).reshape(M, H, d)
-    kc = np.asarray(k_cache, dtype=np.float64).reshape(M, Hkv, max_len, d)
-    vc = np.asarray(v_cache, dtype=np.float64).reshape(M, Hkv, max_len, d)
+    qm = np.asarray(q, dtype=np.float32).reshape(M, H, d)
+    kc = np.asarray(k_cache, dtype=np.float32).reshape(M, Hkv, max_len, d)
+    vc = np.asarray(v_cache, dtype=np.float32).reshape(M, Hkv, max_len, d)
+    sc = float(np.float32(scale))
     out = np.zeros((M, H, d))
-    for m in range(M):
+
+    def unit(mh):
+        m, h = mh
         L = int(lens[m])
-        if L == 0:
-            continue
-        # Repeat each KV head over its g query heads, then attend per head.
-        kr = np.repeat(kc[m, :, :L, :], g, axis=0)                           # [H, L, d]
-        vr = np.repeat(vc[m, :, :L, :], g, axis=0)
-        s = float(np.float32(scale)) * np.einsum("hd,hld->hl", qm[m], kr)
-        p = _softmax_rows(s, np.ones_like(s, dtype=bool))
-        out[m] = np.einsum("hl,hld->hd", p, vr)
+        if L > 0:  # an empty sequence keeps its zeros
+            out[m, h] = _attend(qm[m, h][None, :], kc[m, h // g, :L], vc[m, h // g, :L], sc, None)[0]
+
+    _each(unit, itertools.product(range(M), range(H)))
     return out.reshape(M, H * d)
 
 
@@ -72,22 +111,23 @@ def scatter(k_new, v_new, k_cache, v_cache, cache_lens, M, n_new, Hkv, d, max_le
 def prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens, M, n_new, H, Hkv, d, max_len, scale):
     """Concatenate cached rows 0..P-1 and the new rows, then a causal mask shifted by P."""
     g = H // Hkv
-    qm = np.asarray(q, dtype=np.float64).reshape(M, n_new, H, d)
-    kn = np.asarray(k_new, dtype=np.float64).reshape(M, n_new, Hkv, d)
-    vn = np.asarray(v_new, dtype=np.float64).reshape(M, n_new, Hkv, d)
-    kc = np.asarray(k_cache, dtype=np.float64).reshape(M, Hkv, max_len, d)
-    vc = np.asarray(v_cache, dtype=np.float64).reshape(M, Hkv, max_len, d)
-    out = np.zeros((M, n_new, H, d))
-    for m in range(M):
-        P = int(cache_lens[m])
-        keys = np.concatenate([kc[m, :, :P, :], kn[m].transpose(1, 0, 2)], axis=1)   # [Hkv, P+n, d]
-        vals = np.concatenate([vc[m, :, :P, :], vn[m].transpose(1, 0, 2)], axis=1)
-        keys = np.repeat(keys, g, axis=0)
-        vals = np.repeat(vals, g, axis=0)                                           # [H, P+n, d]
-        s = float(np.float32(scale)) * np.einsum("rhd,hjd->hrj", qm[m], keys)      # [H, n, P+n]
-        visible = np.arange(P + n_new)[None, :] <= (P + np.arange(n_new))[:, None]
-        p = _softmax_rows(s, visible[None])
-        out[m] = np.einsum("hrj,hjd->rhd", p, vals)
+    qm = np.asarray(q, dtype=np.float32).reshape(M, n_new, H, d)
+    kn = np.asarray(k_new, dtype=np.float32).reshape(M, n_new, Hkv, d)
+    vn = np.asarray(v_new, dtype=np.float32).reshape(M, n_new, Hkv, d)
+    kc = np.asarray(k_cache, dtype=np.float32).reshape(M, Hkv, max_len, d)
+    vc = np.asarray(v_cache, dtype=np.float32).reshape(M, Hkv, max_len, d)
+    sc = float(np.float32(scale))
+    out = np.empty((M, n_new, H, d))
+
+    def unit(mh):
+        m, h = mh
+        P, kh = int(cache_lens[m]), h // g
+        keys = np.concatenate([kc[m, kh, :P], kn[m, :, kh]], axis=0)                # [P+n, d]
+        vals = np.concatenate([vc[m, kh, :P], vn[m, :, kh]], axis=0)
+        visible = np.arange(P + n_new)[None, :] <= (P + np.arange(n_new))[:, None]  # [n, P+n]
+        out[m, :, h, :] = _attend(qm[m, :, h, :], keys, vals, sc, visible)
+
+    _each(unit, itertools.product(range(M), range(H)))
     return out.reshape(M, n_new, H * d)
 
 

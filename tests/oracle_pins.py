@@ -414,6 +414,30 @@ def pin_brute_force_tiny_shapes(orc):
                    f"brute decode H={H} Hkv={Hkv} d={d}")
 
 
+def pin_brute_force_medium_shapes(orc):
+    """C oracle == the numpy formulation where it runs head by head on worker threads: many heads,
+    hundreds of keys, ragged lengths, GQA groups, both masks and a cache behind a chunk."""
+    r = _rng("brute-medium")
+    B, S, H, d = 2, 150, 5, 64
+    q, k, v = (r.standard_normal((B, S, H * d)).astype(np.float32) for _ in range(3))
+    for causal in (False, True):
+        _close(orc.prefill(q, k, v, B, S, H, d, _scale(d), causal),
+               brute.prefill(q, k, v, B, S, H, d, _scale(d), causal), 1e-12, f"brute medium prefill causal={causal}")
+    M, H, Hkv, d, max_len = 4, 12, 3, 32, 400
+    lens = np.array([0, 1, 257, 400], np.int32)
+    qd = r.standard_normal((M, H * d)).astype(np.float32)
+    kc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    vc = r.standard_normal((M, Hkv, max_len, d)).astype(np.float32)
+    _close(orc.decode(qd, kc, vc, lens, M, H, Hkv, d, max_len, _scale(d)),
+           brute.decode(qd, kc, vc, lens, M, H, Hkv, d, max_len, _scale(d)), 1e-12, "brute medium decode")
+    M, n, H, Hkv, d, max_len = 3, 40, 8, 2, 32, 300
+    lens = np.array([0, 133, 260], np.int32)
+    q, kn, vn, kc, vc = _cached_case(r, M, n, H, Hkv, d, max_len, lens)
+    _close(orc.prefill_cached(q, kn, vn, kc, vc, lens, M, n, H, Hkv, d, max_len, _scale(d)),
+           brute.prefill_cached(q, kn, vn, kc, vc, lens, M, n, H, Hkv, d, max_len, _scale(d)), 1e-12,
+           "brute medium chunk behind a cache")
+
+
 def pin_pages_inputs_brute(orc):
     """The pages' deterministic test inputs (sin/cos/linear ramps) agree with the brute force.
 

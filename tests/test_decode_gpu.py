@@ -119,18 +119,8 @@ def test_decode_step_full_size(cid):
     orc = oracle.default()
     k_host, v_host = inp["k_cache"], inp["v_cache"]
     orc.scatter(inp["k_new"], inp["v_new"], k_host, v_host, lens - 1, cfg.M, 1, cfg.Hkv, cfg.d, cfg.max_len)
-    if cid == 4:
-        want = orc.decode(inp["q"], k_host, v_host, lens, cfg.M, cfg.H, cfg.Hkv, cfg.d, cfg.max_len, cfg.scale)
-        assert_attn_close(got, want, f"{cfg.name} (all heads)")
-    else:
-        # Every sequence, 8 heads each spread over the KV groups.
-        g = cfg.H // cfg.Hkv
-        sel = np.array([(m, kh * g + (m + kh) % g) for m in range(cfg.M) for kh in range(cfg.Hkv)], np.int64)
-        want = orc.decode_rows(inp["q"], k_host, v_host, lens, sel, cfg.M, cfg.H, cfg.Hkv, cfg.d,
-                               cfg.max_len, cfg.scale)
-        got_sel = np.stack([got[m, h * cfg.d:(h + 1) * cfg.d] for m, h in sel])
-        assert_attn_close(got_sel, want, f"{cfg.name} (sampled heads)")
-        assert np.all(np.isfinite(got))
+    want = orc.decode(inp["q"], k_host, v_host, lens, cfg.M, cfg.H, cfg.Hkv, cfg.d, cfg.max_len, cfg.scale)
+    assert_attn_close(got, want, f"{cfg.name} (all outputs)")
 
 
 def _decode_on(stream, q, kc, vc, lens, M, H, Hkv, d, max_len, scale):

@@ -5,8 +5,11 @@ Small cases span one to many 128-query and 32-key tiles with ragged tails
 counts on and off the XCD-grouping path (B*H a multiple of 8 or not), causal
 and not, non-default scales and large scores.  Outputs start as NaN so an
 unwritten element fails.  The full-size cases are the three prefill
-workloads: all outputs for the two non-causal ones, sampled rows (first and
-last queries, tile edges, random) for the causal B=4, S=2048, H=32, d=128 one.
+workloads, every output element compared with the C oracle.  The larger
+decomposition cases are compared whole against the numpy formulation of the
+oracle (oracle/brute.py, pinned to the C oracle); only a single-head
+S = 32640 case, whose score matrix alone would take 8.5 GB in fp64, is
+checked on sampled rows.
 Every work decomposition the launcher picks has cases of its own (the small
 and mid-size ones on 16-query waves, causal and not, at every head_dim), and
 each is also captured into a HIP graph whose replays must match eager calls
@@ -19,6 +22,7 @@ import oracle
 import transformer_attention_flash_amd as taf
 from transformer_attention_flash_amd import workloads as wl
 from gpu_common import assert_attn_close, nan_like, note, to_dev, to_host
+from oracle import brute
 
 pytestmark = pytest.mark.gpu
 
@@ -78,12 +82,8 @@ def test_prefill_decompositions(case, causal):
     scale = wl.scale_for(d)
     note(f"prefill decomposition B={B} S={S} H={H} d={d} causal={causal}")
     got = run_prefill(q, k, v, B, S, H, d, scale, causal)
-    assert np.all(np.isfinite(got)), "every output element is written"
-    rows = sorted({0, 1, 31, 32, 63, 64, 127, 128, 255, 256, S // 2, S - 65, S - 64, S - 1} & set(range(S)))
-    sel = np.array([(b, i, h) for b in range(B) for i in rows for h in range(0, H, max(1, H // 8))], np.int64)
-    want = oracle.default().prefill_rows(q, k, v, sel, B, S, H, d, scale, causal)
-    got_sel = np.stack([got[b, i, h * d:(h + 1) * d] for b, i, h in sel])
-    assert_attn_close(got_sel, want, f"prefill decomposition {case} causal={causal}")
+    want = brute.prefill(q, k, v, B, S, H, d, scale, causal)
+    assert_attn_close(got, want, f"prefill decomposition {case} causal={causal}")
 
 
 SMALL_PROBLEMS = [
@@ -127,11 +127,11 @@ SMALL_CAUSAL = [
     (2, 33, 3, 32, None),      # QW 1
     (1, 1500, 8, 32, None),    # QW 1
     (1, 1500, 8, 64, None),    # QW 2
-    (1, 3000, 6, 64, "sampled"),   # QW 3
+    (1, 3000, 6, 64, None),    # QW 3
     (1, 32640, 1, 64, "sampled"),  # QW 4 (255 query tiles of 128 on one head)
     (1, 17, 2, 128, None),     # QW 1
     (1, 512, 32, 128, None),   # QW 2
-    (2, 700, 8, 128, "sampled"),   # QW 2
+    (2, 700, 8, 128, None),    # QW 2
 ]
 
 
@@ -144,20 +144,20 @@ def test_prefill_small_problems_causal(case):
     note(f"prefill small causal problem B={B} S={S} H={H} d={d}")
     got = run_prefill(q, k, v, B, S, H, d, scale, True)
     assert np.all(np.isfinite(got)), "every output element is written"
-    orc = oracle.default()
     if rows is None:
-        assert_attn_close(got, orc.prefill(q, k, v, B, S, H, d, scale, True), f"prefill small causal {case}")
+        assert_attn_close(got, brute.prefill(q, k, v, B, S, H, d, scale, True), f"prefill small causal {case}")
         return
+    # One head of 32640 queries: its fp64 score matrix would not fit a whole-output check.
     picks = sorted({0, 1, 15, 16, 17, 31, 32, 47, 48, 63, 64, S // 3, S // 2, S - 49, S - 48, S - 17, S - 16, S - 1}
                    | set(rng.integers(0, S, 16).tolist()))
     sel = np.array([(b, i, h) for b in range(B) for i in picks for h in range(H)], np.int64)
-    want = orc.prefill_rows(q, k, v, sel, B, S, H, d, scale, True)
+    want = oracle.default().prefill_rows(q, k, v, sel, B, S, H, d, scale, True)
     got_sel = np.stack([got[b, i, h * d:(h + 1) * d] for b, i, h in sel])
     assert_attn_close(got_sel, want, f"prefill small causal {case} (sampled rows)")
 
 
 CAUSAL_MID = [
-    # B, S, H, d: causal problems between the small and the eight-wave ones, sampled rows
+    # B, S, H, d: causal problems between the small and the eight-wave ones
     (1, 4096, 8, 128),    # 256 four-wave workgroups: 16-query waves
     (1, 2000, 12, 64),    # 192 / 96: 16-query waves (eight-wave needs 512)
     (1, 2048, 32, 32),    # 512: 16-query waves
@@ -173,13 +173,7 @@ def test_prefill_causal_mid_size(case):
     scale = wl.scale_for(d)
     note(f"prefill causal mid-size B={B} S={S} H={H} d={d}")
     got = run_prefill(q, k, v, B, S, H, d, scale, True)
-    assert np.all(np.isfinite(got)), "every output element is written"
-    picks = sorted({0, 1, 15, 16, 63, 64, 127, 128, S // 2, S - 65, S - 64, S - 17, S - 16, S - 1}
-                   | set(rng.integers(0, S, 10).tolist()))
-    sel = np.array([(b, i, h) for b in range(B) for i in picks for h in (0, H // 2, H - 1)], np.int64)
-    want = oracle.default().prefill_rows(q, k, v, sel, B, S, H, d, scale, True)
-    got_sel = np.stack([got[b, i, h * d:(h + 1) * d] for b, i, h in sel])
-    assert_attn_close(got_sel, want, f"prefill causal mid-size {case} (sampled rows)")
+    assert_attn_close(got, brute.prefill(q, k, v, B, S, H, d, scale, True), f"prefill causal mid-size {case}")
 
 
 def test_prefill_small_problem_large_scores():
@@ -218,19 +212,14 @@ def test_prefill_full_size_noncausal(cid):
     assert_attn_close(got, want, cfg.name)
 
 
-def test_prefill_full_size_causal_sampled():
+def test_prefill_full_size_causal():
+    """B=4, S=2048, H=32, d=128, causal: all 262,144 output rows against the C oracle."""
     cfg = wl.PREFILL[3]
     q, k, v = wl.prefill_inputs(cfg)
     note(f"prefill full size {cfg.name}")
     got = run_prefill(q, k, v, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, cfg.causal)
-    assert np.all(np.isfinite(got)), "every output element is written"
-    rng = np.random.default_rng(33)
-    rows = [0, 1, 31, 32, 127, 128, 129, 1023, 1024, 2046, 2047] + rng.integers(0, cfg.S, 21).tolist()
-    sel = np.array([(b, i, h) for b in range(cfg.B) for i in rows for h in ((i + b) % cfg.H, (7 * i) % cfg.H)],
-                   np.int64)
-    want = oracle.default().prefill_rows(q, k, v, sel, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, True)
-    got_sel = np.stack([got[b, i, h * cfg.d:(h + 1) * cfg.d] for b, i, h in sel])
-    assert_attn_close(got_sel, want, "causal full-size sampled rows")
+    want = oracle.default().prefill(q, k, v, cfg.B, cfg.S, cfg.H, cfg.d, cfg.scale, True)
+    assert_attn_close(got, want, f"{cfg.name} (all outputs)")
 
 
 GRAPH_CASES = [

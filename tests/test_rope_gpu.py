@@ -210,14 +210,5 @@ def test_decode_rope_step_full_size(cid, rot, theta):
     orc.scatter(k_rot.astype(np.float32).reshape(cfg.M, 1, -1), inp["v_new"], k_host, v_host, lens - 1, cfg.M, 1,
                 cfg.Hkv, cfg.d, cfg.max_len)
     q_rot = rotated_queries(orc, inp["q"], lens, cfg.H, cfg.d, rot, theta)
-    if cid == 4:
-        want = orc.decode(q_rot, k_host, v_host, lens, cfg.M, cfg.H, cfg.Hkv, cfg.d, cfg.max_len, cfg.scale)
-        assert_attn_close(got, want, f"{cfg.name} rotated (all heads)")
-    else:
-        g = cfg.H // cfg.Hkv
-        sel = np.array([(m, kh * g + (m + 3 * kh) % g) for m in range(cfg.M) for kh in range(cfg.Hkv)], np.int64)
-        want = orc.decode_rows(q_rot, k_host, v_host, lens, sel, cfg.M, cfg.H, cfg.Hkv, cfg.d, cfg.max_len,
-                               cfg.scale)
-        got_sel = np.stack([got[m, h * cfg.d:(h + 1) * cfg.d] for m, h in sel])
-        assert_attn_close(got_sel, want, f"{cfg.name} rotated (sampled heads)")
-        assert np.all(np.isfinite(got))
+    want = orc.decode(q_rot, k_host, v_host, lens, cfg.M, cfg.H, cfg.Hkv, cfg.d, cfg.max_len, cfg.scale)
+    assert_attn_close(got, want, f"{cfg.name} rotated (all outputs)")
