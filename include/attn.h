@@ -25,7 +25,8 @@
  * Conventions shared by every entry point
  *   - Tensors are f32, row-major, contiguous, in DEVICE memory owned by the
  *     caller.  The library allocates nothing, keeps no per-call state and is
- *     safe to call from several host threads.  Pointers marked HOST are read
+ *     safe to call from several host threads (attn_decode_gqa_batched_noalloc
+ *     alone uses memory of the library's own: see there).  Pointers marked HOST are read
  *     synchronously during the call and may be reused on return.
  *   - Device pointers must be 16-byte aligned (128-bit accesses).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued and
@@ -211,6 +212,34 @@ int attn_decode_gqa_batched(const float *q, const float *k_cache, const float *v
                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                             int32_t max_len, float scale, void *workspace,
                             size_t workspace_bytes, void *stream);
+
+/* Bytes of device scratch built into the library for
+ * attn_decode_gqa_batched_noalloc (one such array per GPU it runs on). */
+#define ATTN_DECODE_SCRATCH_BYTES (64u << 20)
+
+/*
+ * attn_decode_gqa_batched without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, results and
+ * errors as attn_decode_gqa_batched otherwise, bit for bit (the same kernels).
+ *
+ * The per-split partials go to a scratch array of ATTN_DECODE_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on, from the first call on that
+ * GPU until the process ends.  Sizes whose attn_decode_workspace_bytes()
+ * exceeds it are refused with ATTN_ERR_WORKSPACE (64 MiB covers any
+ * max_len with num_seqs * num_heads <= 2016 at head_dim 128; the long-context
+ * M = 16, 64-head decode needs 34 MB).  Nothing is allocated or freed: the
+ * first call on a GPU looks the array's address up (ATTN_ERR_HIP if that
+ * fails); no call clears it, as every value the decode reads from it is
+ * written earlier in the same call.  All calls on one GPU share the array:
+ * calls that can overlap on one GPU (concurrent streams, several host threads)
+ * race on it and must be ordered by the caller.  The array's GPU is the one
+ * that runs `stream`.
+ */
+int attn_decode_gqa_batched_noalloc(const float *q, const float *k_cache, const float *v_cache,
+                                    const int32_t *seq_lens, float *out, int32_t num_seqs,
+                                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_len, float scale, void *stream);
 
 /*
  * KV-cache append (scatter).

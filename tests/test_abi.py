@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "attn_prefill", "attn_prefill_cached", "attn_decode_workspace_bytes", "attn_decode_gqa_batched",
         "kv_cache_scatter", "attn_status_string", "kv_cache_scatter_rope", "attn_decode_gqa_batched_rope",
-        "kv_cache_copy_to_slot", "kv_lengths_reset", "kv_lengths_rollback", "attn_prefill_lowp"])
+        "kv_cache_copy_to_slot", "kv_lengths_reset", "kv_lengths_rollback", "attn_prefill_lowp",
+        "attn_decode_gqa_batched_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -141,6 +142,39 @@ def test_decode_workspace_bytes(lib):
     # Beyond it, up to the int32 limit, the size is refused rather than overflowing.
     assert lib.attn_decode_workspace_bytes(1, 1, 32, 2**30 + 1) == 0
     assert lib.attn_decode_workspace_bytes(1, 1, 32, 2**31 - 1) == 0
+
+
+def decode_noalloc(lib, q=A, k=B_, v=C_, lens=None, out=O_, M=2, H=8, Hkv=2, d=64, max_len=100, scale=0.125):
+    if lens is None:
+        lens = [5, 100][:M] + [1] * max(0, M - 2)
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens) if lens != "null" else None
+    return lib.attn_decode_gqa_batched_noalloc(q, k, v, arr, out, M, H, Hkv, d, max_len, scale, None)
+
+
+def test_decode_noalloc_validation(lib):
+    """Every refusal happens on the host, before the scratch is looked up."""
+    assert taf.ATTN_DECODE_SCRATCH_BYTES == 64 * 2**20
+    assert decode_noalloc(lib, q=0) == NULL
+    assert decode_noalloc(lib, lens="null") == NULL
+    assert decode_noalloc(lib, M=0, lens=[1]) == DIM
+    assert decode_noalloc(lib, M=33, lens=[1] * 33) == DIM
+    assert decode_noalloc(lib, Hkv=3) == DIM
+    assert decode_noalloc(lib, lens=[101, 3]) == DIM
+    assert decode_noalloc(lib, scale=float("inf")) == DIM
+    assert decode_noalloc(lib, d=96) == UNSUP
+    assert decode_noalloc(lib, out=O_ + 4) == UNSUP
+    assert decode_noalloc(lib, max_len=2**30 + 1) == OVF
+    assert decode_noalloc(lib, out=A) == ALIAS
+    # Sizes whose workspace exceeds the built-in scratch: 32 x 64 heads at d 128 over
+    # 64 key blocks need 68.2 MB; 2016 sequence-heads is the most that fits.
+    need = lib.attn_decode_workspace_bytes(32, 64, 128, 32768)
+    assert need > taf.ATTN_DECODE_SCRATCH_BYTES
+    far = dict(q=A, k=2**36, v=2**37, out=3 * 2**36)  # 4.3 GB caches that overlap nothing
+    assert decode_noalloc(lib, M=32, H=64, Hkv=8, d=128, max_len=32768, lens=[1] * 32, **far) == WS
+    assert decode_noalloc(lib, M=32, H=63, Hkv=7, d=128, max_len=32768, lens=[1] * 32, q=0, k=far["k"],
+                          v=far["v"], out=far["out"]) == NULL
+    assert lib.attn_decode_workspace_bytes(32, 63, 128, 32768) <= taf.ATTN_DECODE_SCRATCH_BYTES
+    assert lib.attn_decode_workspace_bytes(16, 64, 128, 32768) <= taf.ATTN_DECODE_SCRATCH_BYTES
 
 
 def test_decode_refuses_max_len_past_limit(lib):

@@ -27,6 +27,8 @@ __all__ = [
     "ATTN_PREC_BF16",
     "attn_decode_workspace_bytes",
     "attn_decode_gqa_batched",
+    "attn_decode_gqa_batched_noalloc",
+    "ATTN_DECODE_SCRATCH_BYTES",
     "kv_cache_scatter",
     "kv_cache_scatter_rope",
     "attn_decode_gqa_batched_rope",
@@ -41,6 +43,7 @@ __all__ = [
 ATTN_MAX_SEQS = 32
 ATTN_PREC_FP16 = 1
 ATTN_PREC_BF16 = 2
+ATTN_DECODE_SCRATCH_BYTES = 64 << 20
 _STATUS = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_INVALID_DIM", 3: "ATTN_ERR_UNSUPPORTED",
     4: "ATTN_ERR_OVERFLOW", 5: "ATTN_ERR_WORKSPACE", 6: "ATTN_ERR_HIP", 7: "ATTN_ERR_ALIAS",
@@ -82,6 +85,8 @@ def library() -> ctypes.CDLL:
         lib.attn_decode_workspace_bytes.restype = sz
         lib.attn_decode_gqa_batched.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, p, sz, p]
         lib.attn_decode_gqa_batched.restype = ctypes.c_int
+        lib.attn_decode_gqa_batched_noalloc.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, p]
+        lib.attn_decode_gqa_batched_noalloc.restype = ctypes.c_int
         lib.kv_cache_scatter.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, p]
         lib.kv_cache_scatter.restype = ctypes.c_int
         lib.kv_cache_scatter_rope.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p]
@@ -219,6 +224,22 @@ def attn_decode_gqa_batched(q, k_cache, v_cache, seq_lens: Sequence[int], out, n
     _call("attn_decode_gqa_batched",
           library().attn_decode_gqa_batched(*ptrs, lens, po, num_seqs, num_heads, num_kv_heads, head_dim,
                                             max_len, scale, pw, ws_bytes, _stream_ptr(dev, stream)))
+
+
+def attn_decode_gqa_batched_noalloc(q, k_cache, v_cache, seq_lens: Sequence[int], out, num_seqs: int,
+                                    num_heads: int, num_kv_heads: int, head_dim: int, max_len: int,
+                                    scale: float, stream=None) -> None:
+    """attn_decode_gqa_batched on the library's built-in scratch (no workspace, nothing allocated)."""
+    dev = q.device
+    qn = num_seqs * num_heads * head_dim
+    cn = num_seqs * num_kv_heads * max_len * head_dim
+    ptrs = [_check_tensor("q", q, qn, dev), _check_tensor("k_cache", k_cache, cn, dev),
+            _check_tensor("v_cache", v_cache, cn, dev)]
+    po = _check_tensor("out", out, qn, dev)
+    lens = _host_ints("seq_lens", seq_lens, num_seqs)
+    _call("attn_decode_gqa_batched_noalloc",
+          library().attn_decode_gqa_batched_noalloc(*ptrs, lens, po, num_seqs, num_heads, num_kv_heads, head_dim,
+                                                    max_len, scale, _stream_ptr(dev, stream)))
 
 
 def attn_decode_gqa_batched_rope(q, k_cache, v_cache, seq_lens: Sequence[int], out, num_seqs: int,

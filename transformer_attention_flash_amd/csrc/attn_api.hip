@@ -11,8 +11,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "launch.h"
 #include "rope.h"
+
+// Scratch memory of attn_decode_gqa_batched_noalloc, for callers that cannot
+// allocate: one array on every GPU the library runs on, held until the
+// process ends.  In host code this name stands for a host-side placeholder,
+// not for device memory: its device address is looked up once per device
+// (decode_scratch below) and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[ATTN_DECODE_SCRATCH_BYTES];
 
 namespace {
 
@@ -57,13 +66,13 @@ int check_rope(int32_t rotary_ndims, int32_t head_dim, float rope_theta) {
     return ATTN_OK;
 }
 
-// Validation shared by the plain and rotary variants of decode and append;
-// on success *args is filled and nothing has been enqueued.
-int prepare_decode(const float *q, const float *k_cache, const float *v_cache, const int32_t *seq_lens,
-                   float *out, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                   int32_t max_len, float scale, void *workspace, size_t workspace_bytes,
-                   attn::DecodeArgs *args) {
-    if (!q || !k_cache || !v_cache || !seq_lens || !out || !workspace) return ATTN_ERR_NULL;
+// Validation of a decode call's arguments other than its workspace.  On
+// success *args is filled except for the workspace pointers, *need is the
+// workspace size in bytes, and nothing has been enqueued.
+int check_decode(const float *q, const float *k_cache, const float *v_cache, const int32_t *seq_lens, float *out,
+                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_len,
+                 float scale, attn::DecodeArgs *args, size_t *need) {
+    if (!q || !k_cache || !v_cache || !seq_lens || !out) return ATTN_ERR_NULL;
     if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS) return ATTN_ERR_INVALID_DIM;
     if (num_heads <= 0 || num_kv_heads <= 0 || max_len <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_DIM;
     if (num_kv_heads > num_heads || num_heads % num_kv_heads != 0) return ATTN_ERR_INVALID_DIM;
@@ -74,9 +83,7 @@ int prepare_decode(const float *q, const float *k_cache, const float *v_cache, c
         lens.v[m] = seq_lens[m];
     }
     if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
-        !aligned16(workspace))
-        return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return ATTN_ERR_UNSUPPORTED;
     if (max_len > kMaxDecodeLen) return ATTN_ERR_OVERFLOW;
     int64_t q_elems, cache_elems;
     if (!checked_mul({num_seqs, num_heads, head_dim}, kMaxElems, &q_elems) ||
@@ -85,22 +92,66 @@ int prepare_decode(const float *q, const float *k_cache, const float *v_cache, c
     int64_t units;  // upper bound on pass-1 work units and workspace slots
     if (!checked_mul({num_seqs, num_heads, attn::decode_max_splits(max_len)}, kMaxElems32, &units))
         return ATTN_ERR_OVERFLOW;
-    const size_t need = attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_len);
-    if (need == 0) return ATTN_ERR_OVERFLOW;
-    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    *need = attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_len);
+    if (*need == 0) return ATTN_ERR_OVERFLOW;
     const int64_t qb = q_elems * 4, cb = cache_elems * 4;
-    if (overlaps(out, qb, q, qb) || overlaps(out, qb, k_cache, cb) || overlaps(out, qb, v_cache, cb) ||
-        overlaps(out, qb, workspace, (int64_t)need) || overlaps(workspace, (int64_t)need, q, qb) ||
+    if (overlaps(out, qb, q, qb) || overlaps(out, qb, k_cache, cb) || overlaps(out, qb, v_cache, cb))
+        return ATTN_ERR_ALIAS;
+    *args = attn::DecodeArgs{q,    k_cache,  v_cache,   out,          nullptr,  nullptr,
+                             lens, num_seqs, num_heads, num_kv_heads, head_dim, max_len,
+                             attn::decode_max_splits(max_len), scale};
+    return ATTN_OK;
+}
+
+// Point the decode at its workspace: acc[M][H][max_splits][D], then ml.
+void set_decode_workspace(attn::DecodeArgs *a, void *workspace) {
+    float *ws = static_cast<float *>(workspace);
+    a->ws_acc = ws;
+    a->ws_ml = ws + (size_t)a->M * a->H * a->max_splits * a->D;
+}
+
+// Validation shared by the plain and rotary variants of the decode with a
+// caller-owned workspace; on success *args is filled and nothing has been
+// enqueued.
+int prepare_decode(const float *q, const float *k_cache, const float *v_cache, const int32_t *seq_lens,
+                   float *out, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t max_len, float scale, void *workspace, size_t workspace_bytes,
+                   attn::DecodeArgs *args) {
+    if (!workspace) return ATTN_ERR_NULL;
+    size_t need = 0;
+    const int st = check_decode(q, k_cache, v_cache, seq_lens, out, num_seqs, num_heads, num_kv_heads, head_dim,
+                                max_len, scale, args, &need);
+    if (st != ATTN_OK) return st;
+    if (!aligned16(workspace)) return ATTN_ERR_UNSUPPORTED;
+    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    const int64_t qb = (int64_t)num_seqs * num_heads * head_dim * 4;
+    const int64_t cb = (int64_t)num_seqs * num_kv_heads * max_len * head_dim * 4;
+    if (overlaps(out, qb, workspace, (int64_t)need) || overlaps(workspace, (int64_t)need, q, qb) ||
         overlaps(workspace, (int64_t)need, k_cache, cb) || overlaps(workspace, (int64_t)need, v_cache, cb))
         return ATTN_ERR_ALIAS;
+    set_decode_workspace(args, workspace);
+    return ATTN_OK;
+}
 
-    const int32_t max_splits = attn::decode_max_splits(max_len);
-    float *ws = static_cast<float *>(workspace);
-    float *ws_acc = ws;
-    float *ws_ml = ws + (size_t)num_seqs * num_heads * max_splits * head_dim;
-    *args = attn::DecodeArgs{q,   k_cache,      v_cache,   out,        ws_acc,  ws_ml,
-                             lens, num_seqs,    num_heads, num_kv_heads, head_dim, max_len,
-                             max_splits, scale};
+// Device address of `scratch` on the GPU that runs `stream`, looked up once
+// per device with that device current and then reused.
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices];
+
+int decode_scratch(hipStream_t stream, void **ptr) {
+    int dev = -1, cur = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+        return ATTN_ERR_HIP;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return ATTN_ERR_HIP;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) return ATTN_ERR_HIP;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
     return ATTN_OK;
 }
 
@@ -144,7 +195,9 @@ const char *attn_status_string(int status) {
         case ATTN_ERR_INVALID_DIM: return "a size, length or position is out of range";
         case ATTN_ERR_UNSUPPORTED: return "unsupported head_dim (32, 64, 128) or pointer not 16-byte aligned";
         case ATTN_ERR_OVERFLOW: return "a size product overflows the supported range";
-        case ATTN_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case ATTN_ERR_WORKSPACE:
+            return "decode workspace missing or too small (attn_decode_gqa_batched_noalloc: the sizes need more "
+                   "than its ATTN_DECODE_SCRATCH_BYTES of built-in scratch)";
         case ATTN_ERR_HIP: return "the HIP runtime reported an error";
         case ATTN_ERR_ALIAS: return "an output buffer overlaps an input buffer";
         default: return "unknown status";
@@ -295,6 +348,23 @@ int attn_decode_gqa_batched(const float *q, const float *k_cache, const float *v
                                   head_dim, max_len, scale, workspace, workspace_bytes, &a);
     if (st != ATTN_OK) return st;
     return from_hip(attn::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+int attn_decode_gqa_batched_noalloc(const float *q, const float *k_cache, const float *v_cache,
+                                    const int32_t *seq_lens, float *out, int32_t num_seqs, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t max_len, float scale,
+                                    void *stream) {
+    attn::DecodeArgs a;
+    size_t need = 0;
+    int st = check_decode(q, k_cache, v_cache, seq_lens, out, num_seqs, num_heads, num_kv_heads, head_dim, max_len,
+                          scale, &a, &need);
+    if (st != ATTN_OK) return st;
+    if (need > ATTN_DECODE_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    if ((st = decode_scratch(hs, &ws)) != ATTN_OK) return st;
+    set_decode_workspace(&a, ws);
+    return from_hip(attn::launch_decode(a, hs));
 }
 
 int attn_decode_gqa_batched_rope(const float *q, const float *k_cache, const float *v_cache,
