@@ -12,17 +12,24 @@ One step is one pass of the whole path over one batch of synthetic inputs:
 
 Inputs are resident in HBM before the timed region.  Every call is bracketed
 by HIP events on the stream it is launched on (torch's current stream, which
-the binding passes to the library), so each kernel's average duration is
-measured live over the timed steps.  ``value`` is the decode's algorithmic
-HBM throughput (K/V rows 0..L_m-1 of every KV head read once, q read, out
-written) over the decode's measured time; the prefill's algorithmic TFLOP/s
-(visible query/key pairs only) is reported next to it and, being the longest
-kernel of the step, in the ``roofline`` object.
+the binding passes to the library), so each kernel's duration is measured
+live over the timed steps; every rate is computed from the median of those
+durations (mean, min and p90 are printed next to it).  ``value`` is the
+decode's algorithmic HBM throughput (K/V rows 0..L_m-1 of every KV head read
+once, q read, out written) over the decode's median time; the prefill's
+algorithmic TFLOP/s (visible query/key pairs only) is reported next to it
+and, being the longest kernel of the step, in the ``roofline`` object.
+Between two decodes of the step, the prefill and the bulk append move more
+than 1 GB, four times the 256 MB MALL.
 
-Outside the step, each timed on its own: ``next_rows`` (chunked prefill behind
-a cache, rotary append and decode, reduced-precision prefill, slot copy) and
+Outside the step, each timed on its own (median of 10 calls after 5 warm-up
+calls, a 1 GiB write between calls so that no call finds the previous one's
+data in the MALL): ``next_rows`` (chunked prefill behind a cache, rotary
+append and decode, reduced-precision prefill, slot copy) and
 ``other_workloads`` (the 64-token and the 1500-token non-causal prefills and
-the short-context decode, M=32, H=32, Hkv=8, max_len=4096, L_m ~ U{1..4096}).
+the short-context decode, M=32, H=32, Hkv=8, max_len=4096, L_m ~ U{1..4096});
+the last two also as roofline objects of their own
+(``roofline_prefill_encoder``, ``roofline_decode_short``).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -172,12 +179,24 @@ def oracle_timings(wl, gpu_us, prefill3_inputs):
     return out
 
 
-def time_call(torch, run, filler=None, warm=5, reps=10):
-    """Mean milliseconds of `run` over `reps` calls, each bracketed by events on the current stream.
+class Evictor:
+    """A 1 GiB buffer whose fill (a plain write kernel, outside the timed events) leaves
+    nothing of the previous call's data in the 256 MB MALL."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(1 << 28, device=dev)
+
+    def __call__(self):
+        self.buf.fill_(1.0)
+
+
+def time_call(torch, run, filler=None, warm=5, reps=10, evict=None):
+    """Median milliseconds of `run` over `reps` calls, each bracketed by events on the current stream.
 
     `filler` (a long call) is enqueued first, so that the GPU is still busy with it
     while the host enqueues the timed calls: the events then see GPU time only,
-    not the host's launch latency between two short calls.
+    not the host's launch latency between two short calls.  `evict`, if given,
+    runs before every timed call, outside its events.
     """
     for _ in range(warm):
         run()
@@ -186,11 +205,13 @@ def time_call(torch, run, filler=None, warm=5, reps=10):
     if filler is not None:
         filler()
     for e0, e1 in ev:
+        if evict is not None:
+            evict()
         e0.record()
         run()
         e1.record()
     torch.cuda.synchronize()
-    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
 
 
 def main():
@@ -239,6 +260,7 @@ def main():
     dkc, dvc = up(dinp["k_cache"]), up(dinp["v_cache"])
     dout = torch.empty((dcfg.M, dcfg.H * dcfg.d), device=dev)
     ws = torch.empty(taf.attn_decode_workspace_bytes(dcfg.M, dcfg.H, dcfg.d, dcfg.max_len) // 4, device=dev)
+    evict = Evictor(torch, dev)
     torch.cuda.synchronize()
     log("inputs resident on the GPU")
 
@@ -278,14 +300,14 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     samples = {n: np.array([e[n][0].elapsed_time(e[n][1]) for e in evs]) for n in names}
-    per = {n: float(np.mean(samples[n])) for n in names}
+    per = {n: float(np.median(samples[n])) for n in names}  # ms; every rate below uses the median
 
     def spread(n):
-        """median / min / p90 of one call's event times over the timed steps (us)."""
+        """mean / min / p90 of one call's event times over the timed steps (us)."""
         x = samples[n] * 1e3
-        return {"median_us": round(float(np.median(x)), 2), "min_us": round(float(np.min(x)), 2),
+        return {"mean_us": round(float(np.mean(x)), 2), "min_us": round(float(np.min(x)), 2),
                 "p90_us": round(float(np.percentile(x, 90)), 2)}
-    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step; " +
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step; medians: " +
         ", ".join(f"{n} {per[n] * 1e3:.1f} us" for n in names))
 
     if not (torch.isfinite(pout).all() and torch.isfinite(dout).all()):
@@ -319,13 +341,13 @@ def main():
                        "sum_L": int(lens.sum())},
         },
         "decode": {"gbs": round(dec_gbs, 2), "frac_hbm": round(dec_gbs / HBM_PEAK_GBS, 4),
-                   "us": round(per["decode"] * 1e3, 2), **spread("decode"), "algorithmic_bytes": dec_bytes},
+                   "median_us": round(per["decode"] * 1e3, 2), **spread("decode"), "algorithmic_bytes": dec_bytes},
         "prefill": {"tflops": round(pre_tflops, 3), "frac_mfma": round(pre_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
-                    "us": round(per["prefill"] * 1e3, 2), **spread("prefill"), "algorithmic_flops": pre_flops},
+                    "median_us": round(per["prefill"] * 1e3, 2), **spread("prefill"), "algorithmic_flops": pre_flops},
         "bulk_scatter": {"gbs": round(blk_gbs, 2), "frac_hbm": round(blk_gbs / HBM_PEAK_GBS, 4),
-                         "us": round(per["bulk_scatter"] * 1e3, 2), **spread("bulk_scatter"),
+                         "median_us": round(per["bulk_scatter"] * 1e3, 2), **spread("bulk_scatter"),
                          "algorithmic_bytes": scfg.bytes},
-        "append": {"us": round(per["append"] * 1e3, 2), **spread("append"), "algorithmic_bytes": dcfg.append_bytes},
+        "append": {"median_us": round(per["append"] * 1e3, 2), **spread("append"), "algorithmic_bytes": dcfg.append_bytes},
         "roofline": {"kernel": "prefill_kernel<128, 8 waves, causal>", "bound": "mfma", "achieved": round(pre_tflops, 3),
                      "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(pre_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
@@ -352,10 +374,10 @@ def main():
         cached = [scfg.n_new] * ccfg.M
         run = lambda: taf.attn_prefill_cached(cq, ck, cv, bk, bv, cached, cout, ccfg.M, ccfg.n_new, ccfg.H,
                                               ccfg.Hkv, ccfg.d, ccfg.max_len, ccfg.scale)
-        c_ms = time_call(torch, run, calls["prefill"])
+        c_ms = time_call(torch, run, calls["prefill"], evict=evict)
         c_tflops = ccfg.flops(cached) / (c_ms * 1e-3) / 1e12
         result["next_rows"] = {"prefill_cached": {
-            "workload": ccfg.name, "us": round(c_ms * 1e3, 2), "tflops": round(c_tflops, 3),
+            "workload": ccfg.name, "median_us": round(c_ms * 1e3, 2), "tflops": round(c_tflops, 3),
             "frac_mfma": round(c_tflops / FP32_MFMA_PEAK_TFLOPS, 4), "algorithmic_flops": ccfg.flops(cached),
             "note": "append of the chunk's K/V plus attention over 2048 cached + the chunk's own keys; "
                     "timed separately, not part of ms_per_step"}}
@@ -368,24 +390,24 @@ def main():
         rot = pcfg.d
         fill = calls["prefill"]
         r_bulk = time_call(torch, lambda: taf.kv_cache_scatter_rope(pk, pv, bk, bv, [0] * scfg.M, scfg.M, scfg.n_new,
-                                                                    scfg.Hkv, scfg.d, scfg.max_len, rot, 1e4), fill)
+                                                                    scfg.Hkv, scfg.d, scfg.max_len, rot, 1e4), fill, evict=evict)
         r_app = time_call(torch, lambda: taf.kv_cache_scatter_rope(dkn, dvn, dkc, dvc, append_pos, dcfg.M, 1,
-                                                                   dcfg.Hkv, dcfg.d, dcfg.max_len, rot, 1e6), fill)
+                                                                   dcfg.Hkv, dcfg.d, dcfg.max_len, rot, 1e6), fill, evict=evict)
         r_dec = time_call(torch, lambda: taf.attn_decode_gqa_batched_rope(dq, dkc, dvc, lens_list, dout, dcfg.M,
                                                                           dcfg.H, dcfg.Hkv, dcfg.d, dcfg.max_len,
-                                                                          dcfg.scale, rot, 1e6, ws), fill)
+                                                                          dcfg.scale, rot, 1e6, ws), fill, evict=evict)
         r_blk_gbs = scfg.bytes / (r_bulk * 1e-3) / 1e9
         r_dec_gbs = dec_bytes / (r_dec * 1e-3) / 1e9
         result["next_rows"]["rope"] = {
-            "bulk_scatter_rope": {"us": round(r_bulk * 1e3, 2), "gbs": round(r_blk_gbs, 2),
+            "bulk_scatter_rope": {"median_us": round(r_bulk * 1e3, 2), "gbs": round(r_blk_gbs, 2),
                                   "frac_hbm": round(r_blk_gbs / HBM_PEAK_GBS, 4), "rotary_ndims": rot,
                                   "theta": 1e4, "plain_us": round(per["bulk_scatter"] * 1e3, 2)},
-            "append_rope": {"us": round(r_app * 1e3, 2), "plain_us": round(per["append"] * 1e3, 2)},
-            "decode_rope": {"us": round(r_dec * 1e3, 2), "gbs": round(r_dec_gbs, 2),
+            "append_rope": {"median_us": round(r_app * 1e3, 2), "plain_us": round(per["append"] * 1e3, 2)},
+            "decode_rope": {"median_us": round(r_dec * 1e3, 2), "gbs": round(r_dec_gbs, 2),
                             "frac_hbm": round(r_dec_gbs / HBM_PEAK_GBS, 4), "rotary_ndims": rot, "theta": 1e6,
                             "plain_us": round(per["decode"] * 1e3, 2)},
-            "note": "timed separately (10 calls after 5 warm-up calls each, queued behind a prefill), "
-                    "not part of ms_per_step"}
+            "note": "timed separately (median of 10 calls after 5 warm-up calls, queued behind a prefill, "
+                    "a 1 GiB write between calls), not part of ms_per_step"}
         log(f"rope: bulk append {r_bulk * 1e3:.1f} us ({r_blk_gbs:.0f} GB/s), append {r_app * 1e3:.1f} us, "
             f"decode {r_dec * 1e3:.1f} us ({r_dec_gbs:.0f} GB/s)")
 
@@ -393,9 +415,9 @@ def main():
         lowp = {}
         for pname, prec in (("fp16", taf.ATTN_PREC_FP16), ("bf16", taf.ATTN_PREC_BF16)):
             lp_ms = time_call(torch, lambda: taf.attn_prefill_lowp(pq, pk, pv, pout, pcfg.B, pcfg.S, pcfg.H, pcfg.d,
-                                                                   pcfg.scale, True, prec), fill)
+                                                                   pcfg.scale, True, prec), fill, evict=evict)
             lp_tf = pre_flops / (lp_ms * 1e-3) / 1e12
-            lowp[pname] = {"us": round(lp_ms * 1e3, 2), "tflops": round(lp_tf, 3),
+            lowp[pname] = {"median_us": round(lp_ms * 1e3, 2), "tflops": round(lp_tf, 3),
                            "frac_mfma": round(lp_tf / LOWP_MFMA_PEAK_TFLOPS, 4)}
             log(f"prefill {pname}: {lp_ms * 1e3:.1f} us, {lp_tf:.1f} TFLOP/s")
         result["next_rows"]["prefill_lowp"] = {
@@ -407,12 +429,12 @@ def main():
         sk, sv = bk[0], bv[0]
         dk, dv = torch.empty_like(bk), torch.empty_like(bv)
         s_ms = time_call(torch, lambda: taf.kv_cache_copy_to_slot(sk, sv, scfg.max_len, scfg.n_new, dk, dv, 3,
-                                                                  scfg.M, scfg.Hkv, scfg.d, scfg.max_len), fill)
+                                                                  scfg.M, scfg.Hkv, scfg.d, scfg.max_len), fill, evict=evict)
         s_bytes = 2 * 2 * scfg.Hkv * scfg.n_new * scfg.d * 4
         s_gbs = s_bytes / (s_ms * 1e-3) / 1e9
         result["next_rows"]["slot_copy"] = {
             "workload": f"copy of {scfg.n_new} rows x {scfg.Hkv} KV heads x d {scfg.d} (K and V) into slot 3",
-            "us": round(s_ms * 1e3, 2), "gbs": round(s_gbs, 2), "frac_hbm": round(s_gbs / HBM_PEAK_GBS, 4),
+            "median_us": round(s_ms * 1e3, 2), "gbs": round(s_gbs, 2), "frac_hbm": round(s_gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": s_bytes}
         log(f"slot copy: {s_ms * 1e3:.1f} us ({s_gbs:.0f} GB/s)")
         del dk, dv
@@ -425,9 +447,9 @@ def main():
             oq, ok_, ov = (up(x) for x in wl.prefill_inputs(c))
             oo = torch.empty_like(oq)
             o_ms = time_call(torch, lambda: taf.attn_prefill(oq, ok_, ov, oo, c.B, c.S, c.H, c.d, c.scale, c.causal),
-                             fill)
+                             fill, evict=evict)
             o_tf = c.flops / (o_ms * 1e-3) / 1e12
-            others[c.name] = {"us": round(o_ms * 1e3, 2), "tflops": round(o_tf, 3),
+            others[c.name] = {"median_us": round(o_ms * 1e3, 2), "tflops": round(o_tf, 3),
                               "frac_mfma": round(o_tf / FP32_MFMA_PEAK_TFLOPS, 4), "algorithmic_flops": c.flops}
             log(f"prefill {c.name}: {o_ms * 1e3:.1f} us, {o_tf:.1f} TFLOP/s")
             del oq, ok_, ov, oo
@@ -438,17 +460,28 @@ def main():
         out4 = torch.empty((c4.M, c4.H * c4.d), device=dev)
         ws4 = torch.empty(taf.attn_decode_workspace_bytes(c4.M, c4.H, c4.d, c4.max_len) // 4, device=dev)
         a4_ms = time_call(torch, lambda: taf.kv_cache_scatter(kn4, vn4, kc4, vc4, (l4 - 1).tolist(), c4.M, 1, c4.Hkv,
-                                                              c4.d, c4.max_len), fill)
+                                                              c4.d, c4.max_len), fill, evict=evict)
         d4_ms = time_call(torch, lambda: taf.attn_decode_gqa_batched(q4, kc4, vc4, l4.tolist(), out4, c4.M, c4.H,
-                                                                     c4.Hkv, c4.d, c4.max_len, c4.scale, ws4), fill)
+                                                                     c4.Hkv, c4.d, c4.max_len, c4.scale, ws4), fill, evict=evict)
         d4_bytes = c4.decode_bytes(l4)
         d4_gbs = d4_bytes / (d4_ms * 1e-3) / 1e9
-        others[c4.name] = {"decode_us": round(d4_ms * 1e3, 2), "gbs": round(d4_gbs, 2),
+        others[c4.name] = {"decode_median_us": round(d4_ms * 1e3, 2), "gbs": round(d4_gbs, 2),
                            "frac_hbm": round(d4_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": d4_bytes,
-                           "append_us": round(a4_ms * 1e3, 2), "sum_L": int(l4.sum())}
+                           "append_median_us": round(a4_ms * 1e3, 2), "sum_L": int(l4.sum())}
         log(f"decode {c4.name}: {d4_ms * 1e3:.1f} us ({d4_gbs:.0f} GB/s), append {a4_ms * 1e3:.1f} us")
+        c2 = wl.PREFILL[2]
+        tf2 = others[c2.name]["tflops"]
+        result["roofline_prefill_encoder"] = {
+            "workload": c2.name, "kernel": "prefill_small_kernel<64, 3 query waves, non-causal>", "bound": "mfma",
+            "achieved": tf2, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf2 / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+        result["roofline_decode_short"] = {
+            "workload": c4.name, "kernels": "decode_split_kernel<128> + decode_combine_kernel<128>", "bound": "hbm",
+            "achieved": round(d4_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(d4_gbs / HBM_PEAK_GBS, 4), "traffic": None}
         del q4, kn4, vn4, kc4, vc4, out4, ws4
-        others["note"] = "timed separately (10 calls after 5 warm-up calls each, queued behind a prefill)"
+        others["note"] = ("timed separately (median of 10 calls after 5 warm-up calls, queued behind a prefill, "
+                          "a 1 GiB write between calls)")
         result["other_workloads"] = others
 
     if not args.no_next_rows:
@@ -475,9 +508,10 @@ def main():
         result["cpu_baseline"] = cpu_baseline(dinp, dcfg, args.cpu_seconds)
         if result["other_workloads"] is not None:
             ow = result["other_workloads"]
-            gpu_us = {wl.PREFILL[1].name: ow[wl.PREFILL[1].name]["us"], wl.PREFILL[2].name: ow[wl.PREFILL[2].name]["us"],
-                      pcfg.name: result["prefill"]["us"], scfg.name: result["bulk_scatter"]["us"],
-                      wl.DECODE[4].name: ow[wl.DECODE[4].name]["decode_us"]}
+            gpu_us = {wl.PREFILL[1].name: ow[wl.PREFILL[1].name]["median_us"],
+                      wl.PREFILL[2].name: ow[wl.PREFILL[2].name]["median_us"],
+                      pcfg.name: result["prefill"]["median_us"], scfg.name: result["bulk_scatter"]["median_us"],
+                      wl.DECODE[4].name: ow[wl.DECODE[4].name]["decode_median_us"]}
             log("timing the CPU oracle on the other workloads ...")
             result["oracle_timings"] = oracle_timings(wl, gpu_us, (q, k, v))
     print(json.dumps(result), flush=True)
