@@ -396,6 +396,16 @@ def main():
         r_dec = time_call(torch, lambda: taf.attn_decode_gqa_batched_rope(dq, dkc, dvc, lens_list, dout, dcfg.M,
                                                                           dcfg.H, dcfg.Hkv, dcfg.d, dcfg.max_len,
                                                                           dcfg.scale, rot, 1e6, ws), fill, evict=evict)
+        # The chunk behind the cache with its queries and keys rotated (base 10000).
+        rng_r = np.random.default_rng(4098)
+        rshape = (ccfg.M, ccfg.n_new, ccfg.H * ccfg.d)
+        rq, rk, rv = (up(wl.normal(rng_r, rshape, pcfg.std)) for _ in range(3))
+        rout = torch.empty_like(rq)
+        r_chunk = time_call(torch, lambda: taf.attn_prefill_cached_rope(rq, rk, rv, bk, bv, cached, rout, ccfg.M,
+                                                                        ccfg.n_new, ccfg.H, ccfg.Hkv, ccfg.d,
+                                                                        ccfg.max_len, ccfg.scale, rot, 1e4),
+                            fill, evict=evict)
+        del rq, rk, rv, rout
         r_blk_gbs = scfg.bytes / (r_bulk * 1e-3) / 1e9
         r_dec_gbs = dec_bytes / (r_dec * 1e-3) / 1e9
         result["next_rows"]["rope"] = {
@@ -403,13 +413,17 @@ def main():
                                   "frac_hbm": round(r_blk_gbs / HBM_PEAK_GBS, 4), "rotary_ndims": rot,
                                   "theta": 1e4, "plain_us": round(per["bulk_scatter"] * 1e3, 2)},
             "append_rope": {"median_us": round(r_app * 1e3, 2), "plain_us": round(per["append"] * 1e3, 2)},
+            "prefill_cached_rope": {"workload": ccfg.name, "median_us": round(r_chunk * 1e3, 2),
+                                    "tflops": round(ccfg.flops(cached) / (r_chunk * 1e-3) / 1e12, 3),
+                                    "rotary_ndims": rot, "theta": 1e4,
+                                    "plain_us": result["next_rows"]["prefill_cached"]["median_us"]},
             "decode_rope": {"median_us": round(r_dec * 1e3, 2), "gbs": round(r_dec_gbs, 2),
                             "frac_hbm": round(r_dec_gbs / HBM_PEAK_GBS, 4), "rotary_ndims": rot, "theta": 1e6,
                             "plain_us": round(per["decode"] * 1e3, 2)},
             "note": "timed separately (median of 10 calls after 5 warm-up calls, queued behind a prefill, "
                     "a 1 GiB write between calls), not part of ms_per_step"}
         log(f"rope: bulk append {r_bulk * 1e3:.1f} us ({r_blk_gbs:.0f} GB/s), append {r_app * 1e3:.1f} us, "
-            f"decode {r_dec * 1e3:.1f} us ({r_dec_gbs:.0f} GB/s)")
+            f"decode {r_dec * 1e3:.1f} us ({r_dec_gbs:.0f} GB/s), chunk behind cache {r_chunk * 1e3:.1f} us")
 
         # Reduced-precision prefill: the step's causal prefill on 16-bit MFMA operands.
         lowp = {}

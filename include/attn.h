@@ -17,8 +17,9 @@
  *   attn_prefill_cached      a chunk of new tokens behind an existing cache:
  *                            append, then attend with the causal mask offset
  *                            by each sequence's cached length.
- * The append and the decode also come with a rotary position embedding fused
- * in (kv_cache_scatter_rope, attn_decode_gqa_batched_rope); a prefilled
+ * The append, the decode and the chunked prefill also come with a rotary
+ * position embedding fused in (kv_cache_scatter_rope,
+ * attn_decode_gqa_batched_rope, attn_prefill_cached_rope); a prefilled
  * single-sequence cache can be copied into a batch slot
  * (kv_cache_copy_to_slot), and the host length arrays reset or rolled back.
  *
@@ -171,6 +172,37 @@ int attn_prefill_cached(const float *q, const float *k_new, const float *v_new, 
                         float *v_cache, const int32_t *cache_lens, float *out, int32_t num_seqs,
                         int32_t n_new, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t max_len, float scale, void *stream);
+
+/*
+ * attn_prefill_cached with a GPT-NeoX rotary position embedding fused in: the
+ * chunk's keys are appended rotated to their cache rows P + r (exactly as
+ * kv_cache_scatter_rope writes them), and query r is rotated to the same
+ * position P + r before it is scored against the cache, whose rows < P are
+ * taken as already rotated (written by earlier rotary appends).
+ *
+ * Defines: trustformers-core `rope_neox_gpu_to_gpu` (the rotation applied at
+ * an absolute position offset: dim i < rotary_ndims / 2 paired with
+ * i + rotary_ndims / 2, angle pos * rope_theta^(-2i / rotary_ndims), dims at or
+ * past rotary_ndims unchanged) composed with `attention_prefill_gpu_to_gpu`'s
+ * causal attention, for the prefill behind a cache that page leaves to the
+ * decode path.
+ *
+ *   arguments as attn_prefill_cached, plus
+ *   rotary_ndims      0 (no rotation: identical to attn_prefill_cached) or a
+ *                     multiple of 8 up to head_dim
+ *   rope_theta        rotary base, finite and > 0
+ *   With n_new == 1 this equals kv_cache_scatter_rope followed by
+ *   attn_decode_gqa_batched_rope with seq_lens = P + 1.
+ *
+ * Errors: those of attn_prefill_cached; rotary_ndims < 0 or > head_dim,
+ * rope_theta not finite or <= 0 (INVALID_DIM); rotary_ndims not a multiple
+ * of 8 (UNSUPPORTED).
+ */
+int attn_prefill_cached_rope(const float *q, const float *k_new, const float *v_new, float *k_cache,
+                             float *v_cache, const int32_t *cache_lens, float *out, int32_t num_seqs,
+                             int32_t n_new, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t max_len, float scale, int32_t rotary_ndims, float rope_theta,
+                             void *stream);
 
 /*
  * Bytes of device workspace attn_decode_gqa_batched needs for these sizes

@@ -23,10 +23,12 @@ and follows the definitions cited there:
 * copy of a prefilled cache into a batch slot -- realizar
   ``scatter_single_kv_to_batched``;
 * rotary position embedding -- trustformers-core ``rope_neox_gpu_to_gpu`` /
-  ``rope_reference``; realizar ``apply_rope_to_buffer``.
+  ``rope_reference``; realizar ``apply_rope_to_buffer``; also composed with the
+  chunked prefill (rotation at each new token's absolute position).
 
-``brute.py`` is a second, independent numpy fp64 formulation used only to
-cross-check this one on tiny shapes.
+``brute.py`` is a second, independent numpy fp64 formulation, checked
+against this one by the pins and used by the GPU tests for whole-output
+checks of large results.
 """
 from __future__ import annotations
 
@@ -74,6 +76,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_round16.restype = ctypes.c_int
     lib.oracle_prefill_lowp.argtypes = [p, p, p, p, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, ctypes.c_int]
     lib.oracle_prefill_lowp.restype = ctypes.c_int
+    lib.oracle_prefill_cached_rope.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                               i64, ctypes.c_double]
+    lib.oracle_prefill_cached_rope.restype = ctypes.c_int
     lib.oracle_rope.argtypes = [p, p, p, i64, i64, i64, i64, ctypes.c_double]
     lib.oracle_rope.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
@@ -205,6 +210,22 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_prefill_cached_rows rejected its arguments")
         return out
+
+    def prefill_cached_rope(self, q, k_new, v_new, k_cache, v_cache, cache_lens, M, n_new, H, Hkv, d, max_len,
+                            scale, rotary_ndims, base):
+        """prefill_cached with query and new key row r of sequence m rotated to cache_lens[m] + r."""
+        q, k_new, v_new = _f32(q), _f32(k_new), _f32(v_new)
+        k_cache, v_cache = _f32(k_cache), _f32(v_cache)
+        cache_lens = np.ascontiguousarray(cache_lens, dtype=np.int32)
+        assert q.size == M * n_new * H * d and k_new.size == M * n_new * Hkv * d == v_new.size
+        assert k_cache.size == M * Hkv * max_len * d == v_cache.size and cache_lens.size == M
+        out = np.empty(M * n_new * H * d, dtype=np.float64)
+        rc = self.lib.oracle_prefill_cached_rope(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                                 _ptr(cache_lens), _ptr(out), M, n_new, H, Hkv, d, max_len,
+                                                 float(np.float32(scale)), int(rotary_ndims), float(base))
+        if rc != 0:
+            raise ValueError("oracle_prefill_cached_rope rejected its arguments")
+        return out.reshape(M, n_new, H * d)
 
     def copy_to_slot(self, src_k, src_v, src_max_len, seq_len, dst_k, dst_v, slot, M, Hkv, d, max_len):
         """In-place copy of a single cache [Hkv, src_max_len, d] into slot `slot` of [M, Hkv, max_len, d]."""

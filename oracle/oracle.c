@@ -494,3 +494,48 @@ int oracle_num_threads(void)
     }
     return n;
 }
+
+/* A chunk behind a cache with a GPT-NeoX rotary embedding: the rotation of
+ * trustformers-core 0.2.0 ..., `rope_neox_gpu_to_gpu` applied at the absolute
+ * position of each new token, composed with the chunked prefill above.  Query
+ * row r and new key row r of sequence m are rotated (oracle_rope) to position
+ * cache_lens[m] + r and handed over as f32, the precision in which the cache
+ * keeps rotated keys; values are not rotated; cached rows 0 .. cache_lens[m]-1
+ * are taken as they are (already rotated when they were appended).  Then
+ * oracle_prefill_cached.  out as there. */
+int oracle_prefill_cached_rope(const float *q, const float *k_new, const float *v_new,
+                               const float *k_cache, const float *v_cache,
+                               const int32_t *cache_lens, double *out, int64_t M,
+                               int64_t n_new, int64_t H, int64_t Hkv, int64_t d,
+                               int64_t max_len, float scale, int64_t rotary_ndims,
+                               double base)
+{
+    int64_t m, r, i;
+    const int64_t nq = M * n_new * H * d, nk = M * n_new * Hkv * d;
+    int rc = -1;
+    int32_t *pos;
+    double *qr, *kr;
+    float *qf, *kf;
+    if (M <= 0 || n_new <= 0 || H <= 0 || Hkv <= 0 || d <= 0) return -1;
+    pos = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M * n_new));
+    qr = (double *)malloc(sizeof(double) * (size_t)nq);
+    kr = (double *)malloc(sizeof(double) * (size_t)nk);
+    qf = (float *)malloc(sizeof(float) * (size_t)nq);
+    kf = (float *)malloc(sizeof(float) * (size_t)nk);
+    if (!pos || !qr || !kr || !qf || !kf) goto done;
+    for (m = 0; m < M; ++m)
+        for (r = 0; r < n_new; ++r) pos[m * n_new + r] = cache_lens[m] + (int32_t)r;
+    if (oracle_rope(q, pos, qr, M * n_new, H, d, rotary_ndims, base) != 0) goto done;
+    if (oracle_rope(k_new, pos, kr, M * n_new, Hkv, d, rotary_ndims, base) != 0) goto done;
+    for (i = 0; i < nq; ++i) qf[i] = (float)qr[i];
+    for (i = 0; i < nk; ++i) kf[i] = (float)kr[i];
+    rc = oracle_prefill_cached(qf, kf, v_new, k_cache, v_cache, cache_lens, out, M, n_new, H, Hkv, d,
+                               max_len, scale);
+done:
+    free(pos);
+    free(qr);
+    free(kr);
+    free(qf);
+    free(kf);
+    return rc;
+}

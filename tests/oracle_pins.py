@@ -378,6 +378,74 @@ def pin_cached_brute_force(orc):
                                     _scale(d)), 1e-12, f"cached brute {M, n, H, Hkv, d}")
 
 
+def _rotated_rows(orc, x, pos, heads, d, rot, base):
+    """Rows [n, heads*d] turned to positions pos by the oracle's own rotation, handed over as f32."""
+    return orc.rope(np.ascontiguousarray(x, np.float32).reshape(len(pos), heads * d), np.asarray(pos, np.int32),
+                    heads, d, rot, base).astype(np.float32)
+
+
+def pin_cached_rope_zero_width_is_plain(orc):
+    """rotary_ndims = 0 rotates nothing: the plain chunked prefill, exactly."""
+    r = _rng("cached-rope-zero")
+    M, n, H, Hkv, d, max_len = 3, 5, 4, 2, 8, 16
+    lens = np.array([0, 7, 11], np.int32)
+    q, kn, vn, kc, vc = _cached_case(r, M, n, H, Hkv, d, max_len, lens)
+    _close(orc.prefill_cached_rope(q, kn, vn, kc, vc, lens, M, n, H, Hkv, d, max_len, _scale(d), 0, 1e4),
+           orc.prefill_cached(q, kn, vn, kc, vc, lens, M, n, H, Hkv, d, max_len, _scale(d)), 0.0, "rotary width 0")
+
+
+def pin_cached_rope_chunks_compose(orc):
+    """Two rotary chunks equal one: the first chunk's keys appended rotated to rows 0..P-1, the second chunk
+    behind them must turn its queries and keys to P + r (not r) to match the whole sequence from empty."""
+    r = _rng("cached-rope-chunks")
+    for M, S, P, H, Hkv, d, rot, base in [(2, 12, 7, 4, 2, 8, 8, 100.0), (1, 9, 4, 2, 2, 16, 8, 10.0)]:
+        max_len = S + 3
+        q = r.standard_normal((M, S, H * d)).astype(np.float32)
+        kn = r.standard_normal((M, S, Hkv * d)).astype(np.float32)
+        vn = r.standard_normal((M, S, Hkv * d)).astype(np.float32)
+        empty = np.full((M, Hkv, max_len, d), np.nan, np.float32)
+        zero = np.zeros(M, np.int32)
+        whole = orc.prefill_cached_rope(q, kn, vn, empty, empty, zero, M, S, H, Hkv, d, max_len, _scale(d), rot, base)
+        pos = np.tile(np.arange(P), M)
+        k_rot = _rotated_rows(orc, kn[:, :P], pos, Hkv, d, rot, base).reshape(M, P, Hkv * d)
+        kc, vc = empty.copy(), empty.copy()
+        orc.scatter(k_rot, np.ascontiguousarray(vn[:, :P]), kc, vc, zero, M, P, Hkv, d, max_len)
+        second = orc.prefill_cached_rope(np.ascontiguousarray(q[:, P:]), np.ascontiguousarray(kn[:, P:]),
+                                         np.ascontiguousarray(vn[:, P:]), kc, vc, np.full(M, P, np.int32), M, S - P,
+                                         H, Hkv, d, max_len, _scale(d), rot, base)
+        _close(second, whole[:, P:], 1e-13, f"rotary chunk behind {P} vs whole")
+
+
+def pin_cached_rope_single_token_is_rotary_decode(orc):
+    """One new token behind P rotated keys: its query turned to position P, its key appended rotated to row
+    P, then the plain decode over P + 1 keys."""
+    r = _rng("cached-rope-decode")
+    M, H, Hkv, d, max_len, rot, base = 3, 6, 2, 16, 20, 16, 1000.0
+    lens = np.array([0, 5, 19], np.int32)
+    q, kn, vn, kc, vc = _cached_case(r, M, 1, H, Hkv, d, max_len, lens)
+    got = orc.prefill_cached_rope(q, kn, vn, kc, vc, lens, M, 1, H, Hkv, d, max_len, _scale(d), rot, base)
+    kc2, vc2 = kc.copy(), vc.copy()
+    orc.scatter(_rotated_rows(orc, kn, lens, Hkv, d, rot, base).reshape(M, 1, Hkv * d), vn, kc2, vc2, lens, M, 1,
+                Hkv, d, max_len)
+    q_rot = _rotated_rows(orc, q, lens, H, d, rot, base)
+    want = orc.decode(q_rot, kc2, vc2, lens + 1, M, H, Hkv, d, max_len, _scale(d))
+    _close(got.reshape(M, H * d), want, 1e-13, "rotary single token vs rotary decode")
+
+
+def pin_cached_rope_brute_force(orc):
+    """C composition == numpy rotation (complex multiplication) + numpy chunked prefill."""
+    r = _rng("cached-rope-brute")
+    for M, n, H, Hkv, d, max_len, rot, base in [(3, 4, 4, 2, 8, 12, 8, 10000.0), (2, 6, 3, 3, 16, 9, 16, 50.0)]:
+        lens = r.integers(0, max_len - n + 1, size=M).astype(np.int32)
+        q, kn, vn, kc, vc = _cached_case(r, M, n, H, Hkv, d, max_len, lens)
+        pos = (lens[:, None] + np.arange(n)[None, :]).reshape(-1)
+        qb = brute.rope(q.reshape(M * n, H * d), pos, H, d, rot, base).astype(np.float32).reshape(q.shape)
+        kb = brute.rope(kn.reshape(M * n, Hkv * d), pos, Hkv, d, rot, base).astype(np.float32).reshape(kn.shape)
+        _close(orc.prefill_cached_rope(q, kn, vn, kc, vc, lens, M, n, H, Hkv, d, max_len, _scale(d), rot, base),
+               brute.prefill_cached(qb, kb, vn, np.nan_to_num(kc), np.nan_to_num(vc), lens, M, n, H, Hkv, d,
+                                    max_len, _scale(d)), 1e-9, f"rotary chunk brute {M, n, H, Hkv, d}")
+
+
 def pin_cached_rows_match(orc):
     """The sampled-row entry point of the chunked prefill equals the full computation."""
     r = _rng("cached-rows")

@@ -40,7 +40,7 @@ def test_header_declares_the_boundary():
         "attn_prefill", "attn_prefill_cached", "attn_decode_workspace_bytes", "attn_decode_gqa_batched",
         "kv_cache_scatter", "attn_status_string", "kv_cache_scatter_rope", "attn_decode_gqa_batched_rope",
         "kv_cache_copy_to_slot", "kv_lengths_reset", "kv_lengths_rollback", "attn_prefill_lowp",
-        "attn_decode_gqa_batched_noalloc"])
+        "attn_decode_gqa_batched_noalloc", "attn_prefill_cached_rope"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -225,6 +225,31 @@ def test_prefill_cached_validation(lib):
     assert cached(lib, out=A + 64) == ALIAS          # out over q
     assert cached(lib, vc=C_ + 1024) == ALIAS        # the caches overlap
     assert cached(lib, kc=B_) == ALIAS               # cache over k_new
+
+
+def cached_rope(lib, rot=32, theta=1e4, **kw):
+    args = dict(q=A, kn=B_, vn=B_ + 0x1000000, kc=C_, vc=C_ + 0x8000000, lens=(0, 3), out=O_, M=2, n=4, H=8,
+                Hkv=2, d=64, max_len=64, scale=0.125)
+    args.update(kw)
+    lens = args["lens"]
+    arr = (ctypes.c_int32 * max(1, len(lens)))(*lens) if lens is not None else None
+    return lib.attn_prefill_cached_rope(args["q"], args["kn"], args["vn"], args["kc"], args["vc"], arr, args["out"],
+                                        args["M"], args["n"], args["H"], args["Hkv"], args["d"], args["max_len"],
+                                        args["scale"], rot, theta, None)
+
+
+def test_prefill_cached_rope_validation(lib):
+    """The chunked prefill's refusals, then the rotary ones; nothing reaches HIP."""
+    assert cached_rope(lib, q=0) == NULL
+    assert cached_rope(lib, lens=None) == NULL
+    assert cached_rope(lib, lens=(0, 61)) == DIM
+    assert cached_rope(lib, d=48) == UNSUP
+    assert cached_rope(lib, out=A + 64) == ALIAS
+    assert cached_rope(lib, rot=-8) == DIM
+    assert cached_rope(lib, rot=72) == DIM             # wider than head_dim 64
+    assert cached_rope(lib, theta=0.0) == DIM
+    assert cached_rope(lib, theta=float("nan")) == DIM
+    assert cached_rope(lib, rot=12) == UNSUP           # not a multiple of 8
 
 
 def test_scatter_rope_validation(lib):

@@ -77,6 +77,11 @@ MUTANTS = [
     ("rope_row_index_as_position", "double a = (double)pos[t] * pow(", "double a = (double)t * pow("),
     ("rope_tail_zeroed", "for (l = rotary_ndims; l < d; ++l) dst[l] = (double)src[l];",
      "for (l = rotary_ndims; l < d; ++l) dst[l] = 0.0;"),
+    ("cached_rope_drops_cache_offset", "pos[m * n_new + r] = cache_lens[m] + (int32_t)r;",
+     "pos[m * n_new + r] = (int32_t)r;"),
+    ("cached_rope_queries_unrotated", "rc = oracle_prefill_cached(qf, kf, v_new,", "rc = oracle_prefill_cached(q, kf, v_new,"),
+    ("cached_rope_keys_unrotated", "rc = oracle_prefill_cached(qf, kf, v_new,", "rc = oracle_prefill_cached(qf, k_new, v_new,"),
+    ("cached_rope_query_heads_as_kv_heads", "oracle_rope(q, pos, qr, M * n_new, H, d,", "oracle_rope(q, pos, qr, M * n_new * (H / Hkv), Hkv, d,"),
 ]
 
 

@@ -22,6 +22,7 @@ __all__ = [
     "ATTN_MAX_SEQS",
     "attn_prefill",
     "attn_prefill_cached",
+    "attn_prefill_cached_rope",
     "attn_prefill_lowp",
     "ATTN_PREC_FP16",
     "ATTN_PREC_BF16",
@@ -81,6 +82,9 @@ def library() -> ctypes.CDLL:
         lib.attn_prefill_lowp.restype = ctypes.c_int
         lib.attn_prefill_cached.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p]
         lib.attn_prefill_cached.restype = ctypes.c_int
+        lib.attn_prefill_cached_rope.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, i32, f32,
+                                                 p]
+        lib.attn_prefill_cached_rope.restype = ctypes.c_int
         lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         lib.attn_decode_workspace_bytes.restype = sz
         lib.attn_decode_gqa_batched.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, f32, p, sz, p]
@@ -194,6 +198,24 @@ def attn_prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens: Sequence[
     _call("attn_prefill_cached",
           library().attn_prefill_cached(*ptrs, lens, po, num_seqs, n_new, num_heads, num_kv_heads, head_dim,
                                         max_len, scale, _stream_ptr(dev, stream)))
+
+
+def attn_prefill_cached_rope(q, k_new, v_new, k_cache, v_cache, cache_lens: Sequence[int], out, num_seqs: int,
+                             n_new: int, num_heads: int, num_kv_heads: int, head_dim: int, max_len: int,
+                             scale: float, rotary_ndims: int, rope_theta: float, stream=None) -> None:
+    """attn_prefill_cached with keys appended rotated to P + r and query r rotated to P + r."""
+    dev = q.device
+    qn = num_seqs * n_new * num_heads * head_dim
+    nn = num_seqs * n_new * num_kv_heads * head_dim
+    cn = num_seqs * num_kv_heads * max_len * head_dim
+    ptrs = [_check_tensor("q", q, qn, dev), _check_tensor("k_new", k_new, nn, dev),
+            _check_tensor("v_new", v_new, nn, dev), _check_tensor("k_cache", k_cache, cn, dev),
+            _check_tensor("v_cache", v_cache, cn, dev)]
+    lens = _host_ints("cache_lens", cache_lens, num_seqs)
+    po = _check_tensor("out", out, qn, dev)
+    _call("attn_prefill_cached_rope",
+          library().attn_prefill_cached_rope(*ptrs, lens, po, num_seqs, n_new, num_heads, num_kv_heads, head_dim,
+                                             max_len, scale, rotary_ndims, rope_theta, _stream_ptr(dev, stream)))
 
 
 def attn_decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_len: int) -> int:

@@ -184,6 +184,63 @@ int prepare_scatter(const float *k_new, const float *v_new, float *k_cache, floa
     return ATTN_OK;
 }
 
+// Validation of a chunked prefill; on success *sa and *pa are filled (the
+// prefill without a rotary embedding) and nothing has been enqueued.
+int prepare_prefill_cached(const float *q, const float *k_new, const float *v_new, float *k_cache,
+                           float *v_cache, const int32_t *cache_lens, float *out, int32_t num_seqs,
+                           int32_t n_new, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_len, float scale, attn::ScatterArgs *sa, attn::PrefillArgs *pa) {
+    if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_lens || !out) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS) return ATTN_ERR_INVALID_DIM;
+    if (n_new <= 0 || num_heads <= 0 || num_kv_heads <= 0 || max_len <= 0 || head_dim <= 0)
+        return ATTN_ERR_INVALID_DIM;
+    if (num_kv_heads > num_heads || num_heads % num_kv_heads != 0) return ATTN_ERR_INVALID_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_INVALID_DIM;
+    SeqInts pos{};
+    for (int32_t m = 0; m < num_seqs; ++m) {
+        if (cache_lens[m] < 0 || (int64_t)cache_lens[m] + n_new > max_len) return ATTN_ERR_INVALID_DIM;
+        pos.v[m] = cache_lens[m];
+    }
+    if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(out))
+        return ATTN_ERR_UNSUPPORTED;
+    int64_t q_elems, new_elems, cache_elems, per_seq;
+    if (!checked_mul({num_seqs, n_new, num_heads, head_dim}, kMaxElems32, &q_elems) ||
+        !checked_mul({num_seqs, n_new, num_kv_heads, head_dim}, kMaxElems32, &new_elems) ||
+        !checked_mul({num_seqs, num_kv_heads, max_len, head_dim}, kMaxElems, &cache_elems) ||
+        !checked_mul({n_new, num_kv_heads, head_dim}, kMaxElems32, &per_seq))
+        return ATTN_ERR_OVERFLOW;
+    const int64_t qb = q_elems * 4, nb = new_elems * 4, cb = cache_elems * 4;
+    const void *ins[] = {q, k_new, v_new};
+    const int64_t in_bytes[] = {qb, nb, nb};
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(out, qb, ins[i], in_bytes[i]) || overlaps(k_cache, cb, ins[i], in_bytes[i]) ||
+            overlaps(v_cache, cb, ins[i], in_bytes[i]))
+            return ATTN_ERR_ALIAS;
+    if (overlaps(out, qb, k_cache, cb) || overlaps(out, qb, v_cache, cb) || overlaps(k_cache, cb, v_cache, cb))
+        return ATTN_ERR_ALIAS;
+
+    *sa = attn::ScatterArgs{k_new, v_new, k_cache, v_cache, pos, num_seqs, n_new, num_kv_heads, head_dim, max_len};
+    attn::PrefillArgs &a = *pa;
+    a = attn::PrefillArgs{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.B = num_seqs;
+    a.S = n_new;
+    a.H = num_heads;
+    a.D = head_dim;
+    a.scale = scale;
+    a.causal = 1;
+    a.cached = 1;
+    a.Hkv = num_kv_heads;
+    a.max_len = max_len;
+    a.pos = pos;
+    return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -269,63 +326,41 @@ int attn_prefill_lowp(const float *q, const float *k, const float *v, float *out
     return from_hip(attn::launch_prefill_lowp(a, precision, static_cast<hipStream_t>(stream)));
 }
 
+
 int attn_prefill_cached(const float *q, const float *k_new, const float *v_new, float *k_cache,
                         float *v_cache, const int32_t *cache_lens, float *out, int32_t num_seqs,
                         int32_t n_new, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t max_len, float scale, void *stream) {
-    if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_lens || !out) return ATTN_ERR_NULL;
-    if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS) return ATTN_ERR_INVALID_DIM;
-    if (n_new <= 0 || num_heads <= 0 || num_kv_heads <= 0 || max_len <= 0 || head_dim <= 0)
-        return ATTN_ERR_INVALID_DIM;
-    if (num_kv_heads > num_heads || num_heads % num_kv_heads != 0) return ATTN_ERR_INVALID_DIM;
-    if (!isfinite(scale)) return ATTN_ERR_INVALID_DIM;
-    SeqInts pos{};
-    for (int32_t m = 0; m < num_seqs; ++m) {
-        if (cache_lens[m] < 0 || (int64_t)cache_lens[m] + n_new > max_len) return ATTN_ERR_INVALID_DIM;
-        pos.v[m] = cache_lens[m];
-    }
-    if (!head_dim_ok(head_dim)) return ATTN_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
-        !aligned16(v_cache) || !aligned16(out))
-        return ATTN_ERR_UNSUPPORTED;
-    int64_t q_elems, new_elems, cache_elems, per_seq;
-    if (!checked_mul({num_seqs, n_new, num_heads, head_dim}, kMaxElems32, &q_elems) ||
-        !checked_mul({num_seqs, n_new, num_kv_heads, head_dim}, kMaxElems32, &new_elems) ||
-        !checked_mul({num_seqs, num_kv_heads, max_len, head_dim}, kMaxElems, &cache_elems) ||
-        !checked_mul({n_new, num_kv_heads, head_dim}, kMaxElems32, &per_seq))
-        return ATTN_ERR_OVERFLOW;
-    const int64_t qb = q_elems * 4, nb = new_elems * 4, cb = cache_elems * 4;
-    const void *ins[] = {q, k_new, v_new};
-    const int64_t in_bytes[] = {qb, nb, nb};
-    for (int i = 0; i < 3; ++i)
-        if (overlaps(out, qb, ins[i], in_bytes[i]) || overlaps(k_cache, cb, ins[i], in_bytes[i]) ||
-            overlaps(v_cache, cb, ins[i], in_bytes[i]))
-            return ATTN_ERR_ALIAS;
-    if (overlaps(out, qb, k_cache, cb) || overlaps(out, qb, v_cache, cb) || overlaps(k_cache, cb, v_cache, cb))
-        return ATTN_ERR_ALIAS;
-
+    attn::ScatterArgs sa;
+    attn::PrefillArgs a;
+    const int st = prepare_prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens, out, num_seqs, n_new,
+                                          num_heads, num_kv_heads, head_dim, max_len, scale, &sa, &a);
+    if (st != ATTN_OK) return st;
     // Append the chunk's K/V rows at each sequence's length, then attend over
     // the cache; both launches go on the same stream, in that order.
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    attn::ScatterArgs sa{k_new, v_new, k_cache, v_cache, pos, num_seqs, n_new, num_kv_heads, head_dim, max_len};
-    hipError_t e = attn::launch_kv_scatter(sa, st);
-    if (e != hipSuccess) return ATTN_ERR_HIP;
-    attn::PrefillArgs a{};
-    a.q = q;
-    a.k = k_cache;
-    a.v = v_cache;
-    a.out = out;
-    a.B = num_seqs;
-    a.S = n_new;
-    a.H = num_heads;
-    a.D = head_dim;
-    a.scale = scale;
-    a.causal = 1;
-    a.cached = 1;
-    a.Hkv = num_kv_heads;
-    a.max_len = max_len;
-    a.pos = pos;
-    return from_hip(attn::launch_prefill(a, st));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (attn::launch_kv_scatter(sa, hs) != hipSuccess) return ATTN_ERR_HIP;
+    return from_hip(attn::launch_prefill(a, hs));
+}
+
+int attn_prefill_cached_rope(const float *q, const float *k_new, const float *v_new, float *k_cache,
+                             float *v_cache, const int32_t *cache_lens, float *out, int32_t num_seqs,
+                             int32_t n_new, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t max_len, float scale, int32_t rotary_ndims, float rope_theta,
+                             void *stream) {
+    attn::ScatterArgs sa;
+    attn::PrefillArgs a;
+    int st = prepare_prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens, out, num_seqs, n_new, num_heads,
+                                    num_kv_heads, head_dim, max_len, scale, &sa, &a);
+    if (st != ATTN_OK) return st;
+    if ((st = check_rope(rotary_ndims, head_dim, rope_theta)) != ATTN_OK) return st;
+    // The chunk's keys go into the cache rotated to their rows P_m + r, and
+    // query r is rotated to the same position inside the attention.
+    const attn::RopeParams rp = attn::make_rope(rotary_ndims, rope_theta);
+    a.rope = rp;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (attn::launch_kv_scatter(sa, hs, &rp) != hipSuccess) return ATTN_ERR_HIP;
+    return from_hip(attn::launch_prefill(a, hs));
 }
 
 size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,

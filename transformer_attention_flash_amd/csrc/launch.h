@@ -8,10 +8,9 @@
 #include <stdint.h>
 
 #include "../../include/attn.h"
+#include "rope.h"
 
 namespace attn {
-
-struct RopeParams;  // rope.h
 
 // Per-sequence host values travel in the kernel arguments (at most 32).
 struct SeqInts {
@@ -44,7 +43,9 @@ hipError_t launch_slot_copy(const SlotCopyArgs &a, hipStream_t stream);
 // element).  With cached == 0, k and v are [B, S, H * D] too (prefill from an
 // empty cache).  With cached == 1, k and v are the caches [B, Hkv, max_len, D]:
 // element b's queries sit at absolute positions pos[b] .. pos[b] + S - 1 and
-// query i attends to cache rows 0 .. pos[b] + i (causal must be 1).
+// query i attends to cache rows 0 .. pos[b] + i (causal must be 1); with
+// rope.rot > 0 (cached mode only) query i is first rotated to its position
+// pos[b] + i.
 struct PrefillArgs {
     const float *q;
     const float *k;
@@ -56,6 +57,7 @@ struct PrefillArgs {
     int32_t cached;
     int32_t Hkv, max_len;
     SeqInts pos;
+    RopeParams rope;  // rot == 0: queries not rotated
 };
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // The prefill of a small problem (head_dim 32, 64 or 128) on 16-query waves

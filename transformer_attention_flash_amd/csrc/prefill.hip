@@ -143,15 +143,25 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
     const int qw0 = q0 + 32 * qwave;  // first query of this wave
     const int my_q = qw0 + li;
 
-    // ---- Q^T operand, pre-scaled so scores are in log2 units.
+    // ---- Q^T operand, pre-scaled so scores are in log2 units (behind a cache
+    // with a rotary embedding, first turned to the query's position P + my_q;
+    // the partner dims half a rotary width away come from the same row).
     const float qs = a.scale * kLog2e;
     float qreg[QV][4];
     {
         const bool ok = my_q < S;
-        const float *qp = qg + (size_t)(ok ? my_q : 0) * row_stride + 4 * lk;
+        const float *qrow = qg + (size_t)(ok ? my_q : 0) * row_stride;
+        const float *qp = qrow + 4 * lk;
 #pragma unroll
         for (int j = 0; j < QV; ++j) {
             f32x4 v4 = ok ? *reinterpret_cast<const f32x4 *>(qp + 8 * j) : f32x4{0, 0, 0, 0};
+            if (a.rope.rot > 0) {
+                const int l0 = 8 * j + 4 * lk;
+                const int pl = l0 < a.rope.half ? l0 + a.rope.half : l0 - a.rope.half;
+                const f32x4 part =
+                    (ok && l0 < a.rope.rot) ? *reinterpret_cast<const f32x4 *>(qrow + pl) : f32x4{0, 0, 0, 0};
+                v4 = rope_rotate4(v4, part, l0, P + my_q, a.rope);
+            }
 #pragma unroll
             for (int c = 0; c < 4; ++c) qreg[j][c] = v4[c] * qs;
         }

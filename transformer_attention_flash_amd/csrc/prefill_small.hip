@@ -166,15 +166,25 @@ __global__ __launch_bounds__(kWave * QW * SKS, 1) void prefill_small_kernel(Pref
     const int my_q = qw0 + li;
 
     // ---- Q operand, pre-scaled so scores are in log2 units: lane supplies
-    // Q[my_q][(D / 4) lk + j] at step j.
+    // Q[my_q][(D / 4) lk + j] at step j (behind a cache with a rotary
+    // embedding, first turned to the query's position P + my_q; the partner
+    // dims half a rotary width away come from the same row).
     const float qs = a.scale * kLog2e;
     float qreg[QJ];
     {
         const bool ok = my_q < S;
-        const float *qp = qg + (size_t)(ok ? my_q : 0) * row_stride + QJ * lk;
+        const float *qrow = qg + (size_t)(ok ? my_q : 0) * row_stride;
+        const float *qp = qrow + QJ * lk;
 #pragma unroll
         for (int jj = 0; jj < QJ / 4; ++jj) {
-            const f32x4 v4 = ok ? *reinterpret_cast<const f32x4 *>(qp + 4 * jj) : f32x4{0, 0, 0, 0};
+            f32x4 v4 = ok ? *reinterpret_cast<const f32x4 *>(qp + 4 * jj) : f32x4{0, 0, 0, 0};
+            if (a.rope.rot > 0) {
+                const int l0 = QJ * lk + 4 * jj;
+                const int pl = l0 < a.rope.half ? l0 + a.rope.half : l0 - a.rope.half;
+                const f32x4 part =
+                    (ok && l0 < a.rope.rot) ? *reinterpret_cast<const f32x4 *>(qrow + pl) : f32x4{0, 0, 0, 0};
+                v4 = rope_rotate4(v4, part, l0, P + my_q, a.rope);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) qreg[4 * jj + e] = v4[e] * qs;
         }
