@@ -45,9 +45,10 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
-def build(src: str = _SRC, out: str = _LIB_PATH) -> str:
-    """Compile oracle.c into a shared library (gcc, -O2, OpenMP, no fast-math)."""
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", src, "-o", out, "-lm"]
+def build(src: str = _SRC, out: str = _LIB_PATH, extra_flags: list[str] | None = None) -> str:
+    """Compile oracle.c into a shared library (gcc, -O2, OpenMP, no fast-math); ``extra_flags``
+    (e.g. sanitizers, for the CPU checks) are added to the command."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", *(extra_flags or []), src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 

@@ -33,6 +33,7 @@
 // transposed to [D][BN] with its 4-key groups paired and XOR-swizzled by
 // dimension (one conflict-free 16-byte read per operand, see vswz).  One
 // workgroup barrier per tile.  The softmax rescales lazily (see kLazy).
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -512,20 +513,22 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_lowp_kernel(Prefil
 // per query; four waves keep smaller problems spread over the CUs.  One
 // eight-wave workgroup fills a CU, so eight waves are used when that still
 // gives at least two workgroups per CU.
-// Compute units of the current device.
-int32_t cu_count() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 256;
-    return cus;
-}
+// Workgroups of `threads` threads of `kernel` that the current device holds
+// at once (CUs x resident workgroups per CU, at least 1 per CU), queried once
+// per device and kernel: `cache` is that kernel's per-device slot.
+constexpr int kMaxDevices = 64;
 
-// Workgroups of `threads` threads of `kernel` that one CU holds at once (at
-// least 1).
-int32_t blocks_per_cu(const void *kernel, int threads) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) return 1;
+int64_t device_slots(const void *kernel, int threads, std::atomic<int64_t> (&cache)[kMaxDevices]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int64_t n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    n = (int64_t)cus * per_cu;
+    cache[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
@@ -557,9 +560,10 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
         // single tiles heaviest first (head-major single tiles would run the
         // heavy tiles of the last heads last).
         if constexpr (CAUSAL) {
-            static const int32_t occ =
-                blocks_per_cu((const void *)prefill_lowp_kernel<D, 8, 1, 64, true, T, false, true>, kWave * 8);
-            if (pair_query_tiles(BH, tiles8, 0, (int64_t)cu_count() * occ)) {
+            static std::atomic<int64_t> pair_slots[kMaxDevices];
+            const int64_t slots = device_slots(
+                (const void *)prefill_lowp_kernel<D, 8, 1, 64, true, T, false, true>, kWave * 8, pair_slots);
+            if (pair_query_tiles(BH, tiles8, 0, slots)) {
                 dim3 grid((unsigned)(BH * ((tiles8 + 1) / 2)));
                 prefill_lowp_kernel<D, 8, 1, 64, true, T, false, true>
                     <<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
