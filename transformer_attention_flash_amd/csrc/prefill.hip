@@ -19,10 +19,14 @@
 // Work decomposition: a workgroup owns BM = 32 NW queries of one (b, h) (NW =
 // 8 waves, or 4 for smaller problems); each wavefront owns 32 of them and
 // keeps its Q slice in VGPRs and its 32 x D output accumulator in registers.
-// K and V tiles of BN = 32 keys go from HBM straight into a double-buffered
-// LDS tile (global_load_lds, no register staging); the next tile's transfer is
-// in flight while the current one is consumed, with one workgroup barrier per
-// tile.  Both products run on v_mfma_f32_32x32x2_f32.  (Problems too small to
+// K and V tiles of BN keys (64 for the eight-wave kernels at head_dim 128,
+// else 32) go from HBM straight into a double-buffered LDS tile
+// (global_load_lds, no register staging); the next tile's transfer is in
+// flight while the current one is consumed, with one workgroup barrier per
+// tile.  Both products run on v_mfma_f32_32x32x2_f32.  A 64-key tile is two
+// 32-key sub-tiles whose score products are two independent accumulation
+// chains (B=4 S=2048 H=32 d=128: causal 1106 -> 1095 us, non-causal 2023 ->
+// 2004 us against 32-key tiles with three chains).  (Problems too small to
 // fill the CUs with these workgroups, and mid-size causal ones, run
 // prefill_small.hip; see launch_typed.)
 //
@@ -42,7 +46,6 @@
 namespace attn {
 namespace {
 
-constexpr int BN = 32;  // keys per LDS tile (one 32-key MFMA sub-tile)
 constexpr float kLazy = 8.0f;  // log2 headroom of the lazily rescaled softmax
 
 __device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16 &c) {
@@ -67,10 +70,12 @@ __device__ __forceinline__ void wait_vmem_all() {
 }
 
 // NW waves of 32 queries each (BM = 32 NW queries per workgroup) walk all of
-// their key tiles together.
-template <int D, int NW, bool CAUSAL>
+// their key tiles (BN keys: one or two 32-key MFMA sub-tiles) together.
+template <int D, int NW, bool CAUSAL, int BN = 32>
 __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs a, int32_t n_qtiles,
                                                                      int32_t xcd_remap) {
+    constexpr int NSUB = BN / 32;  // 32-key sub-tiles per tile
+    static_assert(NSUB == 1 || NSUB == 2, "tiles of 32 or 64 keys");
     constexpr int QW = NW;  // query waves per workgroup
     constexpr int BM = 32 * QW;
     constexpr int NT = D / 32;          // 32-row tiles of O^T; also floats per lane per V row
@@ -205,6 +210,7 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
         // S^T = K Q^T over D (k-slot lk of step (j, c) is column 8j + 4lk + c).
         f32x16 s = f32x16{};
         const float *kbase = Kt + li * D;
+        f32x16 sb = f32x16{};  // second sub-tile (keys 32 .. 63) of a 64-key tile
         // Raised wave priority while this wave issues matrix instructions:
         // the SIMD's other wave (in its softmax or waiting) does not delay
         // them.
@@ -217,7 +223,22 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
         // it by 3-4%.  The non-causal d = 128 kernels keep two (three gave
         // nothing there, four spill).
         f32x16 s2 = f32x16{}, s3 = f32x16{}, s4 = f32x16{};
-        if constexpr (CAUSAL && D == 128) {
+        if constexpr (NSUB == 2) {
+            // Two sub-tiles: two independent chains, interleaved, no sums.
+            const float *kbase2 = Kt + (32 + li) * D;
+#pragma unroll
+            for (int j = 0; j < QV; ++j) {
+                const int cpos = 4 * ((2 * j + lk) ^ (li & SWZ));  // rows li and 32 + li share the swizzle
+                const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + cpos);
+                const f32x4 kv2 = *reinterpret_cast<const f32x4 *>(kbase2 + cpos);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s = mfma32(kv[e], qreg[j][e], s);
+                    sb = mfma32(kv2[e], qreg[j][e], sb);
+                }
+            }
+            __builtin_amdgcn_s_setprio(0);
+        } else if constexpr (CAUSAL && D == 128) {
 #pragma unroll
             for (int j = 0; j < QV; ++j) {
                 const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + 4 * ((2 * j + lk) ^ (li & SWZ)));
@@ -259,19 +280,27 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
         }
 
         // Mask: keys past Sk, and (causal) keys after the query's position.
-        const bool need_mask = (ks0 + 32 > Sk) || (CAUSAL && ks0 + 31 > P + qw0);
+        const bool need_mask = (ks0 + BN > Sk) || (CAUSAL && ks0 + BN - 1 > P + qw0);
         if (need_mask) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int key = ks0 + mrow(v, lk);
                 const bool dead = key >= Sk || (CAUSAL && key > P + my_q);
                 s[v] = dead ? -INFINITY : s[v];
+                if constexpr (NSUB == 2) {
+                    const bool dead2 = key + 32 >= Sk || (CAUSAL && key + 32 > P + my_q);
+                    sb[v] = dead2 ? -INFINITY : sb[v];
+                }
             }
         }
 
         float mx = s[0];
 #pragma unroll
         for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+        if constexpr (NSUB == 2) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sb[v]);
+        }
         mx = max_xor32(mx);
         // Lazy rescaling: the reference maximum m_run moves (and O and l are
         // rescaled) only when a lane's scores would exceed it by more than
@@ -286,13 +315,17 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
 #pragma unroll
             for (int n = 0; n < NT; ++n) o[n] *= alpha;
         }
-        float psum = 0.f;
+        float psum = 0.f, psum2 = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             s[v] = fast_exp2(s[v] - m_run);
             psum += s[v];
+            if constexpr (NSUB == 2) {
+                sb[v] = fast_exp2(sb[v] - m_run);
+                psum2 += sb[v];
+            }
         }
-        l_run += psum;
+        l_run += psum + psum2;
 
         // O^T += V^T P^T: at key step v this lane supplies V[key][NT*li + n]
         // for n-tile n and P^T[key][my_q] = s[v].
@@ -302,6 +335,14 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
             const vrow_t vv = *reinterpret_cast<const vrow_t *>(Vt + mrow(v, lk) * D + NT * li);
 #pragma unroll
             for (int n = 0; n < NT; ++n) o[n] = mfma32(vget<NT>(vv, n), s[v], o[n]);
+        }
+        if constexpr (NSUB == 2) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const vrow_t vv = *reinterpret_cast<const vrow_t *>(Vt + (32 + mrow(v, lk)) * D + NT * li);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) o[n] = mfma32(vget<NT>(vv, n), sb[v], o[n]);
+            }
         }
         __builtin_amdgcn_s_setprio(0);
     };
@@ -364,7 +405,10 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     if constexpr (D >= 64) {
         if ((int64_t)BH * tiles8 >= 512) {
             dim3 grid((unsigned)(BH * tiles8));
-            prefill_kernel<D, 8, CAUSAL><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
+            if constexpr (D == 128)
+                prefill_kernel<D, 8, CAUSAL, 64><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
+            else
+                prefill_kernel<D, 8, CAUSAL><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
             return hipGetLastError();
         }
     }
