@@ -57,8 +57,10 @@ METRIC = "decode attn HBM GB/s (% peak) + prefill TFLOP/s (% fp32 MFMA peak), 1 
 # (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  A figure is reported only while the
 # kernel source still has the hash it was measured on.
 MEASURED_TRAFFIC = {
-    "prefill": {"source": "prefill.hip", "sha256_16": "d191ba0c6d56d940", "bytes": 1_141_601_952},
-    "decode": {"source": "decode.hip", "sha256_16": "ae91dfba08ac07f7", "bytes": 3_346_034_720},
+    "prefill": {"source": "prefill.hip", "sha256_16": "562580af8e54ce45", "bytes": 1_148_545_312},
+    "decode": {"source": "decode.hip", "sha256_16": "46204f31b440b2f0", "bytes": 3_346_042_448},
+    "decode_short": {"source": "decode.hip", "sha256_16": "46204f31b440b2f0", "bytes": 485_570_509},
+    "prefill_encoder": {"source": "prefill_small.hip", "sha256_16": "e6ad1eee23282454", "bytes": 12_489_865},
 }
 
 def measured_traffic(kernel):
@@ -488,11 +490,11 @@ def main():
         result["roofline_prefill_encoder"] = {
             "workload": c2.name, "kernel": "prefill_small_kernel<64, 3 query waves, non-causal>", "bound": "mfma",
             "achieved": tf2, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tf2 / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+            "frac": round(tf2 / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": measured_traffic("prefill_encoder")}
         result["roofline_decode_short"] = {
             "workload": c4.name, "kernels": "decode_split_kernel<128> + decode_combine_kernel<128>", "bound": "hbm",
             "achieved": round(d4_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(d4_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+            "frac": round(d4_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode_short")}
         del q4, kn4, vn4, kc4, vc4, out4, ws4
         others["note"] = ("timed separately (median of 10 calls after 5 warm-up calls, queued behind a prefill, "
                           "a 1 GiB write between calls)")
