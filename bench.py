@@ -350,7 +350,7 @@ def main():
                          "median_us": round(per["bulk_scatter"] * 1e3, 2), **spread("bulk_scatter"),
                          "algorithmic_bytes": scfg.bytes},
         "append": {"median_us": round(per["append"] * 1e3, 2), **spread("append"), "algorithmic_bytes": dcfg.append_bytes},
-        "roofline": {"kernel": "prefill_kernel<128, 8 waves, causal>", "bound": "mfma", "achieved": round(pre_tflops, 3),
+        "roofline": {"kernel": "prefill_kernel<128, 8 waves, causal, 64-key tiles>", "bound": "mfma", "achieved": round(pre_tflops, 3),
                      "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(pre_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic("prefill")},
