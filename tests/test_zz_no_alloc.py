@@ -87,3 +87,35 @@ def test_noalloc_decode_graph_replays_match_eager():
         eager = nan_like((M, H * d))
         taf.attn_decode_gqa_batched(q_new, kc, vc, lens, eager, M, H, Hkv, d, max_len, scale, ws)
         assert np.array_equal(bits(got), bits(to_host(eager))), f"replay {rep} differs from the eager decode"
+
+
+def test_noalloc_decode_at_the_scratch_limit():
+    """The largest decode the built-in scratch takes: 32 sequences x 63 heads (7 KV heads) at
+    d 128 and max_len 8192 need 2016 x 64 split slots of 130 floats = 67 092 480 bytes of the
+    67 108 864, every sequence at a different length up to the full cache.  Equal bit for bit
+    to the workspace decode of the same inputs (whose parity with the oracle at full size is
+    covered by the decode tests), on a call after a smaller one."""
+    import torch
+    M, H, Hkv, d, max_len = 32, 63, 7, 128, 8192
+    assert taf.attn_decode_workspace_bytes(M, H, d, max_len) <= taf.ATTN_DECODE_SCRATCH_BYTES
+    assert taf.attn_decode_workspace_bytes(M, H + 1, d, max_len) > taf.ATTN_DECODE_SCRATCH_BYTES
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(4420)
+    kc = torch.randn((M, Hkv, max_len, d), generator=g, device="cuda:0")
+    vc = torch.randn((M, Hkv, max_len, d), generator=g, device="cuda:0")
+    q = torch.randn((M, H * d), generator=g, device="cuda:0")
+    lens = np.random.default_rng(4421).integers(1, max_len + 1, size=M).astype(np.int32)
+    lens[0], lens[1] = max_len, 1
+    scale = wl.scale_for(d)
+    note("decode_noalloc at the scratch limit: M=32 H=63 Hkv=7 d=128 max_len=8192")
+    small = nan_like((2, 8 * 64))
+    taf.attn_decode_gqa_batched_noalloc(q[:2, :8 * 64].contiguous(), kc[:2, :1, :64, :64].contiguous(),
+                                        vc[:2, :1, :64, :64].contiguous(), [64, 3], small, 2, 8, 1, 64, 64, scale)
+    out = nan_like((M, H * d))
+    taf.attn_decode_gqa_batched_noalloc(q, kc, vc, lens.tolist(), out, M, H, Hkv, d, max_len, scale)
+    ws = torch.empty(taf.attn_decode_workspace_bytes(M, H, d, max_len) // 4, device="cuda:0")
+    ref = nan_like((M, H * d))
+    taf.attn_decode_gqa_batched(q, kc, vc, lens.tolist(), ref, M, H, Hkv, d, max_len, scale, ws)
+    got = to_host(out)
+    assert np.all(np.isfinite(got))
+    assert np.array_equal(bits(got), bits(to_host(ref))), "differs from the workspace decode"
