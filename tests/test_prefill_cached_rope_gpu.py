@@ -40,6 +40,8 @@ CASES = [
     (2, 1100, 16, 4, 64, 1600, [100, 480], 64, 1e4),
     (2, 300, 64, 8, 128, 1300, [600, 950], 128, 1e6),
     (1, 2100, 48, 16, 32, 2200, [64], 24, 1e4),
+    # eight waves (512 workgroups, 64-key tiles), ragged cached lengths, half rotary width
+    (2, 1000, 64, 8, 128, 2100, [600, 1030], 64, 1e4),
 ]
 
 

@@ -69,7 +69,8 @@ DECOMPOSITIONS = [
     (1, 700, 4, 128),     # 16-query waves on 16-key tiles, ragged tail
     (3, 70, 5, 32),       # 16-query waves with fewer key tiles than groups
     (2, 1100, 16, 64),    # 288 workgroups: four waves, causal 16-query waves
-    (2, 1000, 64, 128),   # eight waves
+    (2, 1000, 64, 128),   # eight waves, 64-key tiles; the last tile's second sub-tile partly past S
+    (2, 1050, 64, 128),   # eight waves; the last tile's second 32-key sub-tile wholly past S
 ]
 
 
