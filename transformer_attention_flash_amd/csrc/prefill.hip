@@ -26,7 +26,10 @@
 // tile.  Both products run on v_mfma_f32_32x32x2_f32.  A 64-key tile is two
 // 32-key sub-tiles whose score products are two independent accumulation
 // chains (B=4 S=2048 H=32 d=128: causal 1106 -> 1095 us, non-causal 2023 ->
-// 2004 us against 32-key tiles with three chains).  (Problems too small to
+// 2004 us against 32-key tiles with three chains).  In a causal wave's
+// diagonal 64-key tile whose second sub-tile lies wholly above the wave's
+// queries, only the first is computed (1096 -> 1090 us; the 2048-behind-2048
+// chunk 3129 -> 3100 us).  (Problems too small to
 // fill the CUs with these workgroups, and mid-size causal ones, run
 // prefill_small.hip; see launch_typed.)
 //
@@ -39,6 +42,7 @@
 // holds one query column in both, which makes the row max/sum a reduction
 // over 16 registers plus one exchange with the partner half-wave.
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -207,144 +211,158 @@ __global__ __launch_bounds__(kWave * NW, 8 / NW) void prefill_kernel(PrefillArgs
         const int ks0 = kt * BN;  // first key of the tile
         if (CAUSAL && ks0 > P + qw0 + 31) return;  // whole tile above this wave's diagonal
 
-        // S^T = K Q^T over D (k-slot lk of step (j, c) is column 8j + 4lk + c).
-        f32x16 s = f32x16{};
-        const float *kbase = Kt + li * D;
-        f32x16 sb = f32x16{};  // second sub-tile (keys 32 .. 63) of a 64-key tile
-        // Raised wave priority while this wave issues matrix instructions:
-        // the SIMD's other wave (in its softmax or waiting) does not delay
-        // them.
-        __builtin_amdgcn_s_setprio(1);
-        // Independent accumulation chains, summed afterwards: back-to-back
-        // dependent MFMAs issue more slowly (two chains gave +7%, four another
-        // +5% on the causal d = 128 prefill, before the lazy softmax update
-        // below).  The causal d = 128 kernels now use three: four leave no
-        // registers for the lazy update, and three with it beat four without
-        // it by 3-4%.  The non-causal d = 128 kernels keep two (three gave
-        // nothing there, four spill).
-        f32x16 s2 = f32x16{}, s3 = f32x16{}, s4 = f32x16{};
-        if constexpr (NSUB == 2) {
-            // Two sub-tiles: two independent chains, interleaved, no sums.
-            const float *kbase2 = Kt + (32 + li) * D;
-#pragma unroll
-            for (int j = 0; j < QV; ++j) {
-                const int cpos = 4 * ((2 * j + lk) ^ (li & SWZ));  // rows li and 32 + li share the swizzle
-                const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + cpos);
-                const f32x4 kv2 = *reinterpret_cast<const f32x4 *>(kbase2 + cpos);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    s = mfma32(kv[e], qreg[j][e], s);
-                    sb = mfma32(kv2[e], qreg[j][e], sb);
-                }
-            }
-            __builtin_amdgcn_s_setprio(0);
-        } else if constexpr (CAUSAL && D == 128) {
-#pragma unroll
-            for (int j = 0; j < QV; ++j) {
-                const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + 4 * ((2 * j + lk) ^ (li & SWZ)));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = (4 * j + e) % 3;  // compile-time after unrolling
-                    if (c == 0)
+        // The tile's work for NS computed 32-key sub-tiles: NS = 1 (causal)
+        // when the second sub-tile of a 64-key tile lies wholly above this
+        // wave's diagonal (its scores would all be masked).
+        auto body = [&](auto ns_tag) {
+            constexpr int NS = decltype(ns_tag)::value;
+            // S^T = K Q^T over D (k-slot lk of step (j, c) is column 8j + 4lk + c).
+            f32x16 s = f32x16{};
+            const float *kbase = Kt + li * D;
+            f32x16 sb = f32x16{};  // second sub-tile (keys 32 .. 63) of a 64-key tile
+            // Raised wave priority while this wave issues matrix instructions:
+            // the SIMD's other wave (in its softmax or waiting) does not delay
+            // them.
+            __builtin_amdgcn_s_setprio(1);
+            // Independent accumulation chains, summed afterwards: back-to-back
+            // dependent MFMAs issue more slowly (two chains gave +7%, four another
+            // +5% on the causal d = 128 prefill, before the lazy softmax update
+            // below).  The causal d = 128 kernels now use three: four leave no
+            // registers for the lazy update, and three with it beat four without
+            // it by 3-4%.  The non-causal d = 128 kernels keep two (three gave
+            // nothing there, four spill).
+            f32x16 s2 = f32x16{}, s3 = f32x16{}, s4 = f32x16{};
+            if constexpr (NS == 2) {
+                // Two sub-tiles: two independent chains, interleaved, no sums.
+                const float *kbase2 = Kt + (32 + li) * D;
+    #pragma unroll
+                for (int j = 0; j < QV; ++j) {
+                    const int cpos = 4 * ((2 * j + lk) ^ (li & SWZ));  // rows li and 32 + li share the swizzle
+                    const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + cpos);
+                    const f32x4 kv2 = *reinterpret_cast<const f32x4 *>(kbase2 + cpos);
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
                         s = mfma32(kv[e], qreg[j][e], s);
-                    else if (c == 1)
-                        s2 = mfma32(kv[e], qreg[j][e], s2);
-                    else
-                        s3 = mfma32(kv[e], qreg[j][e], s3);
+                        sb = mfma32(kv2[e], qreg[j][e], sb);
+                    }
                 }
-            }
-            __builtin_amdgcn_s_setprio(0);
-            s += s2;
-            s += s3;
-        } else {
-            constexpr bool kFourChains = CAUSAL || D < 128;
-#pragma unroll
-            for (int j = 0; j < QV; ++j) {
-                const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + 4 * ((2 * j + lk) ^ (li & SWZ)));
-                s = mfma32(kv[0], qreg[j][0], s);
-                s2 = mfma32(kv[1], qreg[j][1], s2);
-                if constexpr (kFourChains) {
-                    s3 = mfma32(kv[2], qreg[j][2], s3);
-                    s4 = mfma32(kv[3], qreg[j][3], s4);
-                } else {
-                    s = mfma32(kv[2], qreg[j][2], s);
-                    s2 = mfma32(kv[3], qreg[j][3], s2);
+                __builtin_amdgcn_s_setprio(0);
+            } else if constexpr (CAUSAL && D == 128) {
+    #pragma unroll
+                for (int j = 0; j < QV; ++j) {
+                    const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + 4 * ((2 * j + lk) ^ (li & SWZ)));
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int c = (4 * j + e) % 3;  // compile-time after unrolling
+                        if (c == 0)
+                            s = mfma32(kv[e], qreg[j][e], s);
+                        else if (c == 1)
+                            s2 = mfma32(kv[e], qreg[j][e], s2);
+                        else
+                            s3 = mfma32(kv[e], qreg[j][e], s3);
+                    }
                 }
-            }
-            __builtin_amdgcn_s_setprio(0);
-            s += s2;
-            if constexpr (kFourChains) {
-                s3 += s4;
+                __builtin_amdgcn_s_setprio(0);
+                s += s2;
                 s += s3;
-            }
-        }
-
-        // Mask: keys past Sk, and (causal) keys after the query's position.
-        const bool need_mask = (ks0 + BN > Sk) || (CAUSAL && ks0 + BN - 1 > P + qw0);
-        if (need_mask) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = ks0 + mrow(v, lk);
-                const bool dead = key >= Sk || (CAUSAL && key > P + my_q);
-                s[v] = dead ? -INFINITY : s[v];
-                if constexpr (NSUB == 2) {
-                    const bool dead2 = key + 32 >= Sk || (CAUSAL && key + 32 > P + my_q);
-                    sb[v] = dead2 ? -INFINITY : sb[v];
+            } else {
+                constexpr bool kFourChains = CAUSAL || D < 128;
+    #pragma unroll
+                for (int j = 0; j < QV; ++j) {
+                    const f32x4 kv = *reinterpret_cast<const f32x4 *>(kbase + 4 * ((2 * j + lk) ^ (li & SWZ)));
+                    s = mfma32(kv[0], qreg[j][0], s);
+                    s2 = mfma32(kv[1], qreg[j][1], s2);
+                    if constexpr (kFourChains) {
+                        s3 = mfma32(kv[2], qreg[j][2], s3);
+                        s4 = mfma32(kv[3], qreg[j][3], s4);
+                    } else {
+                        s = mfma32(kv[2], qreg[j][2], s);
+                        s2 = mfma32(kv[3], qreg[j][3], s2);
+                    }
+                }
+                __builtin_amdgcn_s_setprio(0);
+                s += s2;
+                if constexpr (kFourChains) {
+                    s3 += s4;
+                    s += s3;
                 }
             }
-        }
 
-        float mx = s[0];
-#pragma unroll
-        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
-        if constexpr (NSUB == 2) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sb[v]);
-        }
-        mx = max_xor32(mx);
-        // Lazy rescaling: the reference maximum m_run moves (and O and l are
-        // rescaled) only when a lane's scores would exceed it by more than
-        // 2^kLazy; otherwise the probabilities are taken against the stale
-        // reference (below 2^kLazy, exact enough in f32).  The decision is
-        // wave-uniform, so most tiles skip the 16 * NT multiplies.
-        if (__any(mx - m_run > kLazy)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int n = 0; n < NT; ++n) o[n] *= alpha;
-        }
-        float psum = 0.f, psum2 = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            s[v] = fast_exp2(s[v] - m_run);
-            psum += s[v];
-            if constexpr (NSUB == 2) {
-                sb[v] = fast_exp2(sb[v] - m_run);
-                psum2 += sb[v];
+            // Mask: keys past Sk, and (causal) keys after the query's position.
+            const bool need_mask = (ks0 + 32 * NS > Sk) || (CAUSAL && ks0 + 32 * NS - 1 > P + qw0);
+            if (need_mask) {
+    #pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = ks0 + mrow(v, lk);
+                    const bool dead = key >= Sk || (CAUSAL && key > P + my_q);
+                    s[v] = dead ? -INFINITY : s[v];
+                    if constexpr (NS == 2) {
+                        const bool dead2 = key + 32 >= Sk || (CAUSAL && key + 32 > P + my_q);
+                        sb[v] = dead2 ? -INFINITY : sb[v];
+                    }
+                }
             }
-        }
-        l_run += psum + psum2;
 
-        // O^T += V^T P^T: at key step v this lane supplies V[key][NT*li + n]
-        // for n-tile n and P^T[key][my_q] = s[v].
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const vrow_t vv = *reinterpret_cast<const vrow_t *>(Vt + mrow(v, lk) * D + NT * li);
-#pragma unroll
-            for (int n = 0; n < NT; ++n) o[n] = mfma32(vget<NT>(vv, n), s[v], o[n]);
-        }
-        if constexpr (NSUB == 2) {
-#pragma unroll
+            float mx = s[0];
+    #pragma unroll
+            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+            if constexpr (NS == 2) {
+    #pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sb[v]);
+            }
+            mx = max_xor32(mx);
+            // Lazy rescaling: the reference maximum m_run moves (and O and l are
+            // rescaled) only when a lane's scores would exceed it by more than
+            // 2^kLazy; otherwise the probabilities are taken against the stale
+            // reference (below 2^kLazy, exact enough in f32).  The decision is
+            // wave-uniform, so most tiles skip the 16 * NT multiplies.
+            if (__any(mx - m_run > kLazy)) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+    #pragma unroll
+                for (int n = 0; n < NT; ++n) o[n] *= alpha;
+            }
+            float psum = 0.f, psum2 = 0.f;
+    #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const vrow_t vv = *reinterpret_cast<const vrow_t *>(Vt + (32 + mrow(v, lk)) * D + NT * li);
-#pragma unroll
-                for (int n = 0; n < NT; ++n) o[n] = mfma32(vget<NT>(vv, n), sb[v], o[n]);
+                s[v] = fast_exp2(s[v] - m_run);
+                psum += s[v];
+                if constexpr (NS == 2) {
+                    sb[v] = fast_exp2(sb[v] - m_run);
+                    psum2 += sb[v];
+                }
             }
+            l_run += psum + psum2;
+
+            // O^T += V^T P^T: at key step v this lane supplies V[key][NT*li + n]
+            // for n-tile n and P^T[key][my_q] = s[v].
+            __builtin_amdgcn_s_setprio(1);
+    #pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const vrow_t vv = *reinterpret_cast<const vrow_t *>(Vt + mrow(v, lk) * D + NT * li);
+    #pragma unroll
+                for (int n = 0; n < NT; ++n) o[n] = mfma32(vget<NT>(vv, n), s[v], o[n]);
+            }
+            if constexpr (NS == 2) {
+    #pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const vrow_t vv = *reinterpret_cast<const vrow_t *>(Vt + (32 + mrow(v, lk)) * D + NT * li);
+    #pragma unroll
+                    for (int n = 0; n < NT; ++n) o[n] = mfma32(vget<NT>(vv, n), sb[v], o[n]);
+                }
+            }
+            __builtin_amdgcn_s_setprio(0);
+        };
+        if constexpr (NSUB == 2 && CAUSAL) {
+            if (ks0 + 32 > P + qw0 + 31)
+                body(std::integral_constant<int, 1>{});
+            else
+                body(std::integral_constant<int, 2>{});
+        } else {
+            body(std::integral_constant<int, NSUB>{});
         }
-        __builtin_amdgcn_s_setprio(0);
     };
 
     // Two-stage pipeline with one barrier per tile: after a tile's barrier every
