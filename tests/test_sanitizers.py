@@ -6,7 +6,8 @@
   report both count.
 * The library's host code (the C ABI's validation in csrc/attn_api.hip and the
   launchers) built with host-only sanitizers (hipcc, -Xarch_host before each
-  -fsanitize=; device code as usual) runs tests/test_abi.py.
+  -fsanitize=; device code as usual) runs tests/test_abi.py and the
+  property-based fuzz of the same validation, tests/test_abi_fuzz.py.
 
 Python itself is not instrumented, so each run is a child process with the
 sanitizer runtime of its compiler preloaded (gcc's libasan for the oracle,
@@ -125,8 +126,9 @@ def test_abi_clean_under_host_sanitizers(tmp_path):
             "import transformer_attention_flash_amd as taf\n"
             "taf._LIB_PATH = {lib!r}\n"
             "import pytest\n"
-            "sys.exit(pytest.main(['-q', '-p', 'no:cacheprovider', {abi!r}]))\n").format(
-                root=ROOT, tests=TESTS, lib=lib, abi=os.path.join(TESTS, "test_abi.py"))
+            "sys.exit(pytest.main(['-q', '-p', 'no:cacheprovider', {abi!r}, {fuzz!r}]))\n").format(
+                root=ROOT, tests=TESTS, lib=lib, abi=os.path.join(TESTS, "test_abi.py"),
+                fuzz=os.path.join(TESTS, "test_abi_fuzz.py"))
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=600,
                          env=_env(runtime))
     assert res.returncode == 0 and not _sanitizer_report(res), (res.stdout[-3000:], res.stderr[-3000:])
