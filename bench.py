@@ -220,7 +220,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path).", file=sys.stderr)
+              "(the library and this benchmark have no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 
     import torch
