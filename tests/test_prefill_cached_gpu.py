@@ -118,6 +118,7 @@ CACHED_DECOMPOSITIONS = [
     (1, 2100, 48, 16, 32, 2200, [64]),        # 816 workgroups at d = 32, P < n: 16-query waves
     (2, 1000, 64, 8, 128, 2100, [600, 1030]), # 512 eight-wave workgroups, 64-key tiles, ragged P + n
     (2, 1000, 64, 8, 128, 2100, [40, 1080]),  # the same; each diagonal starts 40 and 56 keys into a 64-key tile
+    (2, 1000, 64, 8, 64, 2100, [600, 1030]),  # eight waves, 64-key tiles at d = 64
 ]
 
 

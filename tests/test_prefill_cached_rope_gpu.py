@@ -42,6 +42,7 @@ CASES = [
     (1, 2100, 48, 16, 32, 2200, [64], 24, 1e4),
     # eight waves (512 workgroups, 64-key tiles), ragged cached lengths, half rotary width
     (2, 1000, 64, 8, 128, 2100, [600, 1030], 64, 1e4),
+    (2, 1000, 64, 8, 64, 2100, [40, 1080], 32, 1e4),   # the same at d = 64 (64-key tiles)
 ]
 
 

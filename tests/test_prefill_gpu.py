@@ -71,6 +71,8 @@ DECOMPOSITIONS = [
     (2, 1100, 16, 64),    # 288 workgroups: four waves, causal 16-query waves
     (2, 1000, 64, 128),   # eight waves, 64-key tiles; the last tile's second sub-tile partly past S
     (2, 1050, 64, 128),   # eight waves; the last tile's second 32-key sub-tile wholly past S
+    (2, 1000, 64, 64),    # eight waves, 64-key tiles at d = 64; second sub-tile partly past S
+    (2, 1050, 64, 64),    # the same with the last tile's second sub-tile wholly past S
 ]
 
 

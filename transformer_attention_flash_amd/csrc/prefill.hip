@@ -19,14 +19,15 @@
 // Work decomposition: a workgroup owns BM = 32 NW queries of one (b, h) (NW =
 // 8 waves, or 4 for smaller problems); each wavefront owns 32 of them and
 // keeps its Q slice in VGPRs and its 32 x D output accumulator in registers.
-// K and V tiles of BN keys (64 for the eight-wave kernels at head_dim 128,
-// else 32) go from HBM straight into a double-buffered LDS tile
+// K and V tiles of BN keys (64 for the eight-wave kernels at head_dim 64 and
+// 128, else 32) go from HBM straight into a double-buffered LDS tile
 // (global_load_lds, no register staging); the next tile's transfer is in
 // flight while the current one is consumed, with one workgroup barrier per
 // tile.  Both products run on v_mfma_f32_32x32x2_f32.  A 64-key tile is two
 // 32-key sub-tiles whose score products are two independent accumulation
 // chains (B=4 S=2048 H=32 d=128: causal 1106 -> 1095 us, non-causal 2023 ->
-// 2004 us against 32-key tiles with three chains).  In a causal wave's
+// 2004 us against 32-key tiles with three chains; at d=64 1.5-3% on five
+// shapes, B=2 S=4096 H=32 causal 1122 -> 1085 us).  In a causal wave's
 // diagonal 64-key tile whose second sub-tile lies wholly above the wave's
 // queries, only the first is computed (1096 -> 1090 us; the 2048-behind-2048
 // chunk 3129 -> 3100 us).  (Problems too small to
@@ -423,7 +424,7 @@ hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     if constexpr (D >= 64) {
         if ((int64_t)BH * tiles8 >= 512) {
             dim3 grid((unsigned)(BH * tiles8));
-            if constexpr (D == 128)
+            if constexpr (D >= 64)
                 prefill_kernel<D, 8, CAUSAL, 64><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
             else
                 prefill_kernel<D, 8, CAUSAL><<<grid, dim3(kWave * 8), 0, stream>>>(a, tiles8, xcd_remap);
