@@ -41,7 +41,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;
-constexpr int kChunk = 32;  // keys per softmax step: two 16-key MFMA tiles
 
 // Column of the head dimension that n-tile n, row i (0..15) of O^T stands for.
 // Chosen so each lane's share of a V row is one or two contiguous 16-byte
@@ -56,14 +55,24 @@ __host__ __device__ constexpr int ocol(int n, int i) {
 }
 
 // Work decomposition of one call, computed on the host from the lengths.
-// Every (kh, head block) of sequence m is cut into nkblk[m] key blocks of
-// span[m] keys (a multiple of 4 waves x 32 keys; the last block may be
-// shorter); workgroup start[m] + (kh * n_hblk + hb) * nkblk[m] + kblk runs one.
-struct UnitMap {
-    int32_t start[ATTN_MAX_SEQS + 1];  // first workgroup of the i-th sequence in grid order; start[M] = grid size
-    int32_t seq[ATTN_MAX_SEQS];        // the i-th sequence in grid order (longest key blocks first)
-    int32_t nkblk[ATTN_MAX_SEQS];      // per sequence
-    int32_t span[ATTN_MAX_SEQS];       // per sequence
+// The keys of every unit (kh, head block) of sequence m are cut, in key
+// order, into nsplit[m] key blocks: first the bulk blocks, of one span shared
+// by all sequences, then tail blocks of a smaller span (the last one may be
+// shorter).  The grid lists every bulk block first and every tail block
+// after them, as segments: segment s holds the blocks of sequence seq[s] of
+// one kind, npiece[s] per unit, and workgroup start[s] + u * npiece[s] + p
+// runs block piece0[s] + p (its split slot) of unit u.  The bulk blocks fill
+// at most one round of the device; the small tail blocks then keep every
+// slot busy while the bulk blocks, which run at unequal speeds, finish.
+constexpr int kMaxSegs = 2 * ATTN_MAX_SEQS;
+struct SegMap {
+    int32_t start[kMaxSegs + 1];    // first workgroup of segment s; start[nseg] = grid size
+    int32_t seq[kMaxSegs];          // its sequence
+    int32_t piece0[kMaxSegs];       // split slot of its first block in each unit
+    int32_t npiece[kMaxSegs];       // its blocks per unit
+    int32_t nsplit[ATTN_MAX_SEQS];  // key blocks per unit of each sequence
+    int32_t nseg, nbulk;            // segments, of which the first nbulk are bulk
+    int32_t bulk_span, tail_span;   // keys per block
 };
 
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
@@ -76,34 +85,41 @@ __device__ __forceinline__ T load_stream(const T *p) {
     return __builtin_nontemporal_load(p);
 }
 
-template <int D, bool ROPE>
-__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a, UnitMap map,
+template <int D, int CH, bool ROPE>
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a, SegMap map,
                                                                 int32_t n_hblk, RopeParams rp) {
     constexpr int NT = D / 16;     // 16-column tiles of O^T
     constexpr int KV4 = D / 16;    // 16-byte K vectors per lane per 16-key tile
     constexpr int VW = D >= 64 ? 4 : 2;  // floats per V vector
     constexpr int NVV = NT / VW;   // V vectors per lane per key
+    constexpr int NTL = CH / 16;   // 16-key MFMA tiles per chunk
     typedef typename VecN<VW>::type vvec;
+    static_assert(CH == 16 || CH == 32, "chunks of 16 or 32 keys");
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x >> 6;
-    const int unit = blockIdx.x;  // the grid has exactly map.start[M] blocks
+    const int wg = blockIdx.x;  // the grid has exactly map.start[map.nseg] blocks
 
-    // unit -> (m, kh, head block hb, key block kblk).  Wave w of the
-    // workgroup takes chunks w, w + 4, w + 8, ... of the key block, so the
-    // four waves stream adjacent 32-key chunks of K (and of V) side by side;
-    // the workgroup writes split slot kblk.
-    int pos = 0;
-    while (unit >= map.start[pos + 1]) ++pos;
-    const int m = map.seq[pos];
+    // workgroup -> (segment s, unit, block p of the segment) -> (m, kh, head
+    // block hb, split slot kblk, keys [k0, k1)).  Wave w of the workgroup
+    // takes chunks w, w + 4, w + 8, ... of the key block, so the four waves
+    // stream adjacent 32-key chunks of K (and of V) side by side.
+    int s = 0;
+    for (int hi_s = map.nseg; hi_s - s > 1;) {  // last segment with start <= wg
+        const int mid = (s + hi_s) >> 1;
+        if (wg >= map.start[mid]) s = mid; else hi_s = mid;
+    }
+    const int m = map.seq[s];
     const int L = a.lens.v[m];
-    const int span = map.span[m];
-    const int nkblk = map.nkblk[m];
-    int rem = unit - map.start[pos];
-    const int kblk = rem % nkblk;
-    rem /= nkblk;
-    const int hb = rem % n_hblk;
-    const int kh = rem / n_hblk;
+    const int npiece = map.npiece[s];
+    const int rem = wg - map.start[s];
+    const int p = rem % npiece;
+    const int hb = (rem / npiece) % n_hblk;
+    const int kh = (rem / npiece) / n_hblk;
+    const int kblk = map.piece0[s] + p;
+    const int k0 = s < map.nbulk ? p * map.bulk_span
+                                 : map.piece0[s] * map.bulk_span + p * map.tail_span;  // the workgroup's keys are [k0, k1)
+    const int k1 = min(k0 + (s < map.nbulk ? map.bulk_span : map.tail_span), L);
 
     const int g = a.H / a.Hkv;
     const int hi = lane & 15;  // head column / key row within a tile
@@ -112,10 +128,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     const bool head_ok = head_in_group < g;
     const int h = kh * g + head_in_group;
 
-    const int k0 = kblk * span;        // the workgroup's keys are [k0, k1)
-    const int k1 = min(k0 + span, L);
-    const int kfirst = k0 + kChunk * wave;
-    constexpr int kStep = kChunk * kWavesPerBlock;
+    const int kfirst = k0 + CH * wave;
+    constexpr int kStep = CH * kWavesPerBlock;
 
     // q^T operand, pre-scaled so scores come out in log2 units.  With a
     // rotary embedding the query is first turned to the position of the
@@ -176,11 +190,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     // past the key block's end are clamped to its last row (in bounds) and
     // masked below.
     constexpr int KROW = D + 4;                      // LDS pitch of a K row (floats)
-    constexpr int KST = kChunk * D / 4 / kWave;      // 16-byte K vectors per lane per chunk
-    __shared__ __attribute__((aligned(16))) float k_lds[kWavesPerBlock][kChunk * KROW];
+    constexpr int KST = CH * D / 4 / kWave;          // 16-byte K vectors per lane per chunk
+    __shared__ __attribute__((aligned(16))) float k_lds[kWavesPerBlock][CH * KROW];
     float *kl = k_lds[wave];
     f32x4 kst[KST];
-    vvec vf[2][4][NVV];
+    vvec vf[NTL][4][NVV];
     auto load_k = [&](int kb) {
 #pragma unroll
         for (int u = 0; u < KST; ++u) {
@@ -198,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     };
     auto load_v = [&](int kb) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NTL; ++t) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int vrow = min(kb + 16 * t + 4 * kq + r, k1 - 1);
@@ -241,9 +255,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
         __builtin_amdgcn_sched_barrier(0);
 
         // S^T tiles: rows = keys kb + 16t + 4kq + r, columns = heads.
-        f32x4 sc[2];
+        f32x4 sc[NTL];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NTL; ++t) {
             f32x4 acc = {0, 0, 0, 0};
             const float *krow = kl + (16 * t + hi) * KROW + 4 * kq;
 #pragma unroll
@@ -258,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
         // Online softmax over the chunk; keys >= k1 are masked.
         float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NTL; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const bool live = kb + 16 * t + 4 * kq + r < k1;
@@ -271,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
         m_run = m_new;
         float psum = 0.f;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NTL; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 sc[t][r] = fast_exp2(sc[t][r] - m_new);
@@ -283,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
 
         // O^T += V^T P^T; rows of V past the split end contribute zero.
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NTL; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const bool live = kb + 16 * t + 4 * kq + r < k1;
@@ -308,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     // A wave that had no chunk of the key block parks max kNegBig, sum 0,
     // output 0, which the merge weighs by 2^(kNegBig - M*) = 0 (wave 0 always
     // has a chunk, so M* is a real maximum).
-    static_assert(16 * D + 32 <= kChunk * KROW, "parked state fits the K tile");
+    static_assert(16 * D + 32 <= CH * KROW, "parked state fits the K tile");
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -352,11 +366,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     }
 }
 
-// One wave per (m, h): folds the nkblk[m] splits in split order with a
+// One wave per (m, h): folds the nsplit[m] splits in split order with a
 // running max (loads of 8 splits in flight together) and writes
 // out[m][h] = acc / l, or zeros for an empty sequence.
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a, UnitMap map) {
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a, SegMap map) {
     constexpr int PER = D >= 64 ? D / 64 : 1;  // floats per lane
     constexpr int LANES = D / PER;             // lanes holding output columns
     constexpr int BATCH = 8;
@@ -365,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a, 
     const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     if (w >= a.M * a.H) return;  // no barrier below
     const int m = w / a.H;
-    const int nsplit = map.nkblk[m];
+    const int nsplit = map.nsplit[m];
     const size_t slot0 = (size_t)w * a.max_splits;
     const float *ml = a.ws_ml + 2 * slot0;
     const float *accp = a.ws_acc + slot0 * D + PER * lane;
@@ -394,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a, 
         *reinterpret_cast<pvec *>(a.out + (size_t)w * D + PER * lane) = nsplit > 0 ? acc * (1.0f / l_run) : pvec{};
 }
 
-constexpr int32_t kSpanQuantum = kWavesPerBlock * kChunk;  // keys: one chunk per wave
+constexpr int32_t kSpanQuantum = 128;  // keys: one 32-key chunk per wave
 constexpr int32_t kMaxKeyBlocks = 64;                        // per (sequence, head): workspace bound
 
 // Smallest key-block span for a cache of max_len rows: a power-of-two multiple
@@ -406,38 +420,61 @@ int32_t span_floor(int32_t max_len) {
     return (int32_t)s;
 }
 
-// The decode grid is this many times what the device holds at once (one
-// round, or three or more, measured slower).
-constexpr int kDecodeRounds = 2;
+// Share of the keys that go to the bulk blocks (the rest to the tail), and
+// the tail span in units of span_floor.
+constexpr int64_t kBulkNum = 9, kBulkDen = 10;
+constexpr int32_t kTailFloors = 2;
 
-// Workgroups of decode_split_kernel<D> that fit on the device at once (CUs x
-// resident blocks per CU), queried once per device and head_dim.
+// Below this many keys per workgroup slot (at 32-key chunks) a call streams
+// 16-key chunks: half the loads in flight per wave and a third resident
+// workgroup per CU, which shortens each key block's start and the queueing
+// of a short call (M 32, up to 4096 keys: 92 -> 88 us); long contexts keep
+// 32-key chunks (M 16, 16K-32K keys: 1-3% faster than 16).
+constexpr int64_t kShortKeysPerSlot = 4096;
+
+// Workgroups of decode_split_kernel<D, CH, ROPE> that fit on the device at
+// once (CUs x resident blocks per CU), queried once per device and kernel.
 constexpr int kMaxDevices = 64;
-std::atomic<int32_t> g_capacity[kMaxDevices][3];
+std::atomic<int32_t> g_capacity[kMaxDevices][3][2][2];
 
-template <int D>
+template <int D, int CH, bool ROPE>
 int32_t query_capacity() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 512;
     const int slot = D == 32 ? 0 : D == 64 ? 1 : 2;
-    int32_t cap = g_capacity[dev][slot].load(std::memory_order_relaxed);
+    int32_t cap = g_capacity[dev][slot][CH == 16][ROPE].load(std::memory_order_relaxed);
     if (cap > 0) return cap;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0 ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, false>, kThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_split_kernel<D, CH, ROPE>, kThreads, 0) != hipSuccess ||
         per_cu <= 0)
         return 512;
     cap = cus * per_cu;
-    g_capacity[dev][slot].store(cap, std::memory_order_relaxed);
+    g_capacity[dev][slot][CH == 16][ROPE].store(cap, std::memory_order_relaxed);
     return cap;
 }
 
-int32_t capacity_for(int32_t D) {
+template <int D>
+int32_t capacity_d(int32_t CH, bool rot) {
+    if (CH == 16) return rot ? query_capacity<D, 16, true>() : query_capacity<D, 16, false>();
+    return rot ? query_capacity<D, 32, true>() : query_capacity<D, 32, false>();
+}
+
+int32_t capacity_for(int32_t D, int32_t CH, bool rot) {
     switch (D) {
-        case 32: return query_capacity<32>();
-        case 64: return query_capacity<64>();
-        default: return query_capacity<128>();
+        case 32: return capacity_d<32>(CH, rot);
+        case 64: return capacity_d<64>(CH, rot);
+        default: return capacity_d<128>(CH, rot);
     }
+}
+
+template <int D, int CH>
+void launch_split(bool rot, dim3 grid, hipStream_t stream, const DecodeArgs &a, const SegMap &map, int32_t n_hblk,
+                  const RopeParams &rp) {
+    if (rot)
+        decode_split_kernel<D, CH, true><<<grid, dim3(kThreads), 0, stream>>>(a, map, n_hblk, rp);
+    else
+        decode_split_kernel<D, CH, false><<<grid, dim3(kThreads), 0, stream>>>(a, map, n_hblk, rp);
 }
 
 }  // namespace
@@ -457,73 +494,83 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
     const int32_t n_hblk = (g + 15) / 16;
     const int64_t units_per_seq = (int64_t)a.Hkv * n_hblk;
 
-    // Balance: cut every sequence's keys into key blocks of (nearly) equal
-    // size, sized so the whole grid is kDecodeRounds times what the device
-    // holds at once.  Equal blocks finish together, so no lone partial round
-    // runs at the end.  Spans are multiples of 4 x 32 keys and at least
-    // span_floor(max_len), which bounds the workspace.
+    // Bulk blocks carry about kBulkNum / kBulkDen of the keys in at most one
+    // round of the device (CU count x resident workgroups per CU), all of one
+    // span; each sequence's remaining keys go to tail blocks of kTailFloors x
+    // span_floor keys, which run last and fill the slots that the bulk blocks,
+    // running at unequal speeds, leave free one after another.  The bulk span
+    // is a multiple of the tail span, so a sequence of L keys has at most
+    // ceil(L / span_floor) <= max_splits blocks.
     int64_t total = 0;
     for (int i = 0; i < a.M; ++i) total += a.lens.v[i];
     total *= units_per_seq;
-    const double target = (double)capacity_for(a.D) * kDecodeRounds;
-    const int32_t sf = span_floor(a.max_len);
+    const bool rot = rope && rope->rot > 0;
+    const int32_t ch = total < kShortKeysPerSlot * capacity_for(a.D, 32, rot) ? 16 : 32;
+    const int64_t slots = capacity_for(a.D, ch, rot);
+    const int32_t tspan = span_floor(a.max_len) * kTailFloors;
+    int64_t bspan = (kBulkNum * total + kBulkDen * slots - 1) / (kBulkDen * slots);
+    bspan = ((bspan + tspan - 1) / tspan) * tspan;
+    if (bspan < tspan) bspan = tspan;
+    if (bspan > a.max_len) bspan = ((int64_t)a.max_len + tspan - 1) / tspan * tspan;
 
-    UnitMap map;
-    for (int i = 0; i < a.M; ++i) {
-        const int32_t L = a.lens.v[i];
-        map.nkblk[i] = 0;
-        map.span[i] = sf;
-        if (L == 0) continue;
-        const double want = (double)L * target / (double)total;  // key blocks per (kh, hb) unit
-        const int64_t nb = want < 1.0 ? 1 : (int64_t)(want + 0.5);
-        int64_t span = ((int64_t)L + nb - 1) / nb;
-        span = ((span + kSpanQuantum - 1) / kSpanQuantum) * kSpanQuantum;
-        if (span < sf) span = sf;
-        map.span[i] = (int32_t)span;
-        map.nkblk[i] = (int32_t)(((int64_t)L + span - 1) / span);
+    SegMap map;
+    map.bulk_span = (int32_t)bspan;
+    map.tail_span = tspan;
+    int32_t nb[ATTN_MAX_SEQS], nt[ATTN_MAX_SEQS];
+    for (int i = 0; i < ATTN_MAX_SEQS; ++i) {
+        nb[i] = nt[i] = 0;
+        if (i >= a.M || a.lens.v[i] <= 0) continue;
+        const int64_t L = a.lens.v[i];
+        nb[i] = (int32_t)(kBulkNum * L / (kBulkDen * bspan));
+        nt[i] = (int32_t)((L - nb[i] * bspan + tspan - 1) / tspan);
     }
-    for (int i = a.M; i < ATTN_MAX_SEQS; ++i) {
-        map.nkblk[i] = 0;
-        map.span[i] = sf;
-    }
-    // Grid order: sequences with the longest key blocks first, so the blocks
-    // dispatched last are the short ones and the device drains evenly.
-    for (int i = 0; i < a.M; ++i) map.seq[i] = i;
-    for (int i = 1; i < a.M; ++i) {  // insertion sort, stable, by span descending
-        const int32_t x = map.seq[i];
-        int j = i - 1;
-        while (j >= 0 && map.span[map.seq[j]] < map.span[x]) {
-            map.seq[j + 1] = map.seq[j];
-            --j;
-        }
-        map.seq[j + 1] = x;
-    }
-    for (int i = a.M; i < ATTN_MAX_SEQS; ++i) map.seq[i] = i;
+    // Segments in grid order: the bulk blocks of every sequence (most first),
+    // then the tail blocks (most first).
+    int32_t order[ATTN_MAX_SEQS];
+    int nseg = 0;
     int32_t acc = 0;
-    for (int i = 0; i < a.M; ++i) {
-        map.start[i] = acc;
-        acc += map.nkblk[map.seq[i]] * (int32_t)units_per_seq;
+    for (int kind = 0; kind < 2; ++kind) {
+        const int32_t *cnt = kind == 0 ? nb : nt;
+        for (int i = 0; i < a.M; ++i) order[i] = i;
+        for (int i = 1; i < a.M; ++i) {  // insertion sort, stable, by block count descending
+            const int32_t x = order[i];
+            int j = i - 1;
+            while (j >= 0 && cnt[order[j]] < cnt[x]) {
+                order[j + 1] = order[j];
+                --j;
+            }
+            order[j + 1] = x;
+        }
+        for (int i = 0; i < a.M; ++i) {
+            const int32_t sq = order[i];
+            if (cnt[sq] == 0) continue;
+            map.start[nseg] = acc;
+            map.seq[nseg] = sq;
+            map.piece0[nseg] = kind == 0 ? 0 : nb[sq];
+            map.npiece[nseg] = cnt[sq];
+            acc += cnt[sq] * (int32_t)units_per_seq;
+            ++nseg;
+        }
+        if (kind == 0) map.nbulk = nseg;
     }
-    for (int i = a.M; i <= ATTN_MAX_SEQS; ++i) map.start[i] = acc;
+    map.nseg = nseg;
+    for (int i = nseg; i <= kMaxSegs; ++i) map.start[i] = acc;
+    for (int i = nseg; i < kMaxSegs; ++i) map.seq[i] = map.piece0[i] = map.npiece[i] = 0;
+    for (int i = 0; i < ATTN_MAX_SEQS; ++i) map.nsplit[i] = nb[i] + nt[i];
 
     dim3 block(kThreads);
     if (acc > 0) {
         dim3 grid(acc);
-        if (rope && rope->rot > 0) {
-            switch (a.D) {
-                case 32: decode_split_kernel<32, true><<<grid, block, 0, stream>>>(a, map, n_hblk, *rope); break;
-                case 64: decode_split_kernel<64, true><<<grid, block, 0, stream>>>(a, map, n_hblk, *rope); break;
-                case 128: decode_split_kernel<128, true><<<grid, block, 0, stream>>>(a, map, n_hblk, *rope); break;
-                default: return hipErrorInvalidValue;
-            }
-        } else {
-            const RopeParams none{};
-            switch (a.D) {
-                case 32: decode_split_kernel<32, false><<<grid, block, 0, stream>>>(a, map, n_hblk, none); break;
-                case 64: decode_split_kernel<64, false><<<grid, block, 0, stream>>>(a, map, n_hblk, none); break;
-                case 128: decode_split_kernel<128, false><<<grid, block, 0, stream>>>(a, map, n_hblk, none); break;
-                default: return hipErrorInvalidValue;
-            }
+        const RopeParams none{};
+        const RopeParams &rp = rot ? *rope : none;
+        switch (a.D * 2 + (ch == 16)) {
+            case 64: launch_split<32, 32>(rot, grid, stream, a, map, n_hblk, rp); break;
+            case 65: launch_split<32, 16>(rot, grid, stream, a, map, n_hblk, rp); break;
+            case 128: launch_split<64, 32>(rot, grid, stream, a, map, n_hblk, rp); break;
+            case 129: launch_split<64, 16>(rot, grid, stream, a, map, n_hblk, rp); break;
+            case 256: launch_split<128, 32>(rot, grid, stream, a, map, n_hblk, rp); break;
+            case 257: launch_split<128, 16>(rot, grid, stream, a, map, n_hblk, rp); break;
+            default: return hipErrorInvalidValue;
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
