@@ -31,6 +31,18 @@ SMALL = [
     (5, 12, 4, 64, 2000, [0, 511, 512, 513, 1999]),
     (2, 6, 3, 128, 5000, [4097, 1024]),
     (3, 16, 8, 128, 9000, [8999, 256, 257]),
+    # 32 sequences x 64 KV heads of at most 256 keys: the bulk key-block span
+    # would pass max_len, so every key block is a tail block.
+    (32, 64, 64, 64, 256, None),
+]
+
+# Long contexts with enough keys per workgroup slot that the decode streams
+# 32-key chunks at d = 32 and d = 64 (d = 128 is the long-context full-size
+# step below; short calls stream 16-key chunks): every output is compared.
+LONG = [
+    # M, H, Hkv, d, max_len, lowest length
+    (16, 32, 16, 32, 32768, 24000),
+    (8, 32, 16, 64, 32768, 28000),
 ]
 
 
@@ -62,6 +74,22 @@ def test_decode_small(case):
     assert_attn_close(got, want, f"decode {case}")
     for m in np.nonzero(lens == 0)[0]:
         assert np.all(got[m] == 0.0), "an empty sequence must give zeros"
+
+
+@pytest.mark.parametrize("case", LONG, ids=[f"M{c[0]}_H{c[1]}_Hkv{c[2]}_d{c[3]}_max{c[4]}" for c in LONG])
+def test_decode_long_contexts(case):
+    M, H, Hkv, d, max_len, lo = case
+    rng = np.random.default_rng(500 + d)
+    lens = rng.integers(lo, max_len + 1, size=M).astype(np.int32)
+    lens[0] = max_len
+    q = rng.standard_normal((M, H * d), dtype=np.float32)
+    kc = rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32)
+    vc = rng.standard_normal((M, Hkv, max_len, d), dtype=np.float32)
+    scale = wl.scale_for(d)
+    note(f"decode long M={M} H={H} Hkv={Hkv} d={d} max_len={max_len} sum(L)={int(lens.sum())}")
+    got = run_decode(to_dev(q), to_dev(kc), to_dev(vc), lens.tolist(), M, H, Hkv, d, max_len, scale)
+    want = oracle.default().decode(q, kc, vc, lens, M, H, Hkv, d, max_len, scale)
+    assert_attn_close(got, want, f"decode long {case}")
 
 
 def test_decode_large_scores():

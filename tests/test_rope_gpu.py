@@ -141,6 +141,8 @@ DECODE = [
     (5, 12, 4, 64, 2000, [0, 511, 512, 513, 1999], 16, 500.0),
     (32, 8, 8, 32, 50, None, 8, 10000.0),
     (2, 64, 2, 128, 130, [130, 7], 64, 1e6),
+    # long enough per workgroup slot for 32-key chunks at d = 64
+    (8, 32, 16, 64, 32768, [32768, 31000, 30500, 29000, 32000, 28000, 30000, 31500], 64, 1e4),
 ]
 
 
