@@ -58,8 +58,8 @@ METRIC = "decode attn HBM GB/s (% peak) + prefill TFLOP/s (% fp32 MFMA peak), 1 
 # kernel source still has the hash it was measured on.
 MEASURED_TRAFFIC = {
     "prefill": {"source": "prefill.hip", "sha256_16": "2e250bd89cb5273c", "bytes": 1_151_588_064},
-    "decode": {"source": "decode.hip", "sha256_16": "46204f31b440b2f0", "bytes": 3_346_042_448},
-    "decode_short": {"source": "decode.hip", "sha256_16": "46204f31b440b2f0", "bytes": 485_570_509},
+    "decode": {"source": "decode.hip", "sha256_16": "93151181ff8bf225", "bytes": 3_347_757_056},
+    "decode_short": {"source": "decode.hip", "sha256_16": "93151181ff8bf225", "bytes": 485_696_410},
     "prefill_encoder": {"source": "prefill_small.hip", "sha256_16": "e6ad1eee23282454", "bytes": 12_489_865},
 }
 
@@ -354,7 +354,7 @@ def main():
                      "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(pre_tflops / FP32_MFMA_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic("prefill")},
-        "roofline_decode": {"kernels": "decode_split_kernel<128> + decode_combine_kernel<128>", "bound": "hbm",
+        "roofline_decode": {"kernels": "decode_split_kernel<128, 32-key chunks> + decode_combine_kernel<128>", "bound": "hbm",
                             "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                             "traffic": measured_traffic("decode")},
@@ -492,7 +492,7 @@ def main():
             "achieved": tf2, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf2 / FP32_MFMA_PEAK_TFLOPS, 4), "traffic": measured_traffic("prefill_encoder")}
         result["roofline_decode_short"] = {
-            "workload": c4.name, "kernels": "decode_split_kernel<128> + decode_combine_kernel<128>", "bound": "hbm",
+            "workload": c4.name, "kernels": "decode_split_kernel<128, 16-key chunks> + decode_combine_kernel<128>", "bound": "hbm",
             "achieved": round(d4_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(d4_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode_short")}
         del q4, kn4, vn4, kc4, vc4, out4, ws4
