@@ -56,23 +56,24 @@ __host__ __device__ constexpr int ocol(int n, int i) {
 
 // Work decomposition of one call, computed on the host from the lengths.
 // The keys of every unit (kh, head block) of sequence m are cut, in key
-// order, into nsplit[m] key blocks: first the bulk blocks, of one span shared
-// by all sequences, then tail blocks of a smaller span (the last one may be
-// shorter).  The grid lists every bulk block first and every tail block
-// after them, as segments: segment s holds the blocks of sequence seq[s] of
-// one kind, npiece[s] per unit, and workgroup start[s] + u * npiece[s] + p
-// runs block piece0[s] + p (its split slot) of unit u.  The bulk blocks fill
-// at most one round of the device; the small tail blocks then keep every
-// slot busy while the bulk blocks, which run at unequal speeds, finish.
-constexpr int kMaxSegs = 2 * ATTN_MAX_SEQS;
+// order, into nsplit[m] key blocks.  A segment is a run of blocks of one
+// sequence and one span: segment s holds npiece[s] blocks per unit, of
+// span[s] keys each from key kbase[s] on (a block is clipped to the sequence
+// length), and workgroup start[s] + u * npiece[s] + p runs block p of unit u,
+// whose split slot is piece0[s] + p.  launch_decode orders the segments so
+// that the blocks of the device's first round come first, sized for the slot
+// each will occupy, and small tail blocks after them.
+constexpr int kMaxSlotsPerCu = 3;  // first-round block kinds (workgroups per CU)
+constexpr int kMaxSegs = (kMaxSlotsPerCu + 1) * ATTN_MAX_SEQS;
 struct SegMap {
     int32_t start[kMaxSegs + 1];    // first workgroup of segment s; start[nseg] = grid size
-    int32_t seq[kMaxSegs];          // its sequence
-    int32_t piece0[kMaxSegs];       // split slot of its first block in each unit
-    int32_t npiece[kMaxSegs];       // its blocks per unit
+    int32_t kbase[kMaxSegs];        // first key of its first block
+    int32_t span[kMaxSegs];         // keys per block
+    int16_t npiece[kMaxSegs];       // its blocks per unit
+    int8_t seq[kMaxSegs];           // its sequence
+    int8_t piece0[kMaxSegs];        // split slot of its first block
     int32_t nsplit[ATTN_MAX_SEQS];  // key blocks per unit of each sequence
-    int32_t nseg, nbulk;            // segments, of which the first nbulk are bulk
-    int32_t bulk_span, tail_span;   // keys per block
+    int32_t nseg;
 };
 
 __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
@@ -117,9 +118,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     const int hb = (rem / npiece) % n_hblk;
     const int kh = (rem / npiece) / n_hblk;
     const int kblk = map.piece0[s] + p;
-    const int k0 = s < map.nbulk ? p * map.bulk_span
-                                 : map.piece0[s] * map.bulk_span + p * map.tail_span;  // the workgroup's keys are [k0, k1)
-    const int k1 = min(k0 + (s < map.nbulk ? map.bulk_span : map.tail_span), L);
+    const int k0 = map.kbase[s] + p * map.span[s];  // the workgroup's keys are [k0, k1)
+    const int k1 = min(k0 + map.span[s], L);
 
     const int g = a.H / a.Hkv;
     const int hi = lane & 15;  // head column / key row within a tile
@@ -420,10 +420,17 @@ int32_t span_floor(int32_t max_len) {
     return (int32_t)s;
 }
 
-// Share of the keys that go to the bulk blocks (the rest to the tail), and
-// the tail span in units of span_floor.
-constexpr int64_t kBulkNum = 9, kBulkDen = 10;
-constexpr int32_t kTailFloors = 2;
+// The first round of the grid carries about kFirstRoundPct percent of the
+// keys, the rest goes to tail blocks of kTailFloors x span_floor keys.
+// Workgroups co-resident on one CU stream at unequal speeds: the one placed
+// first wins issue arbitration on every SIMD.  Timed per workgroup on the
+// device, the second-placed streams at 0.69-0.74 of the first's rate and a
+// third at about a quarter, so the first round's block for the k-th
+// workgroup of a CU is sized by kSlotWeight[k] (percent), and all of them
+// finish at about the same time.
+constexpr int64_t kFirstRoundPct = 90;
+constexpr int32_t kTailFloors = 1;
+constexpr int64_t kSlotWeight[kMaxSlotsPerCu] = {100, 72, 28};
 
 // Below this many keys per workgroup slot (at 32-key chunks) a call streams
 // 16-key chunks: half the loads in flight per wave and a third resident
@@ -436,6 +443,19 @@ constexpr int64_t kShortKeysPerSlot = 4096;
 // once (CUs x resident blocks per CU), queried once per device and kernel.
 constexpr int kMaxDevices = 64;
 std::atomic<int32_t> g_capacity[kMaxDevices][3][2][2];
+std::atomic<int32_t> g_cus[kMaxDevices];
+
+// Compute units of the current device, queried once per device.
+int32_t decode_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int32_t n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
 
 template <int D, int CH, bool ROPE>
 int32_t query_capacity() {
@@ -494,69 +514,101 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
     const int32_t n_hblk = (g + 15) / 16;
     const int64_t units_per_seq = (int64_t)a.Hkv * n_hblk;
 
-    // Bulk blocks carry about kBulkNum / kBulkDen of the keys in at most one
-    // round of the device (CU count x resident workgroups per CU), all of one
-    // span; each sequence's remaining keys go to tail blocks of kTailFloors x
-    // span_floor keys, which run last and fill the slots that the bulk blocks,
-    // running at unequal speeds, leave free one after another.  The bulk span
-    // is a multiple of the tail span, so a sequence of L keys has at most
-    // ceil(L / span_floor) <= max_splits blocks.
-    int64_t total = 0;
-    for (int i = 0; i < a.M; ++i) total += a.lens.v[i];
-    total *= units_per_seq;
+    // First round: the k-th workgroup placed on a CU (k < the kernel's
+    // workgroups per CU) gets a block of span[k] keys, span[k] proportional
+    // to kSlotWeight[k], kFirstRoundPct percent of the keys over all of them.
+    // Each kind holds one block per CU, counted in units of whole sequences
+    // (all units of a sequence have the same blocks), and goes to the
+    // sequences with the most keys left, in key order: a sequence's kind-0
+    // blocks come first, then its kind-1 blocks, ...  The keys left after the
+    // first round go to tail blocks of kTailFloors x span_floor keys, which
+    // run last.  Every span is a multiple of span_floor, so a sequence of L
+    // keys has at most ceil(L / span_floor) <= max_splits blocks.
+    int64_t lsum = 0;
+    for (int i = 0; i < a.M; ++i) lsum += a.lens.v[i];
+    const int64_t total = lsum * units_per_seq;
     const bool rot = rope && rope->rot > 0;
     const int32_t ch = total < kShortKeysPerSlot * capacity_for(a.D, 32, rot) ? 16 : 32;
-    const int64_t slots = capacity_for(a.D, ch, rot);
-    const int32_t tspan = span_floor(a.max_len) * kTailFloors;
-    int64_t bspan = (kBulkNum * total + kBulkDen * slots - 1) / (kBulkDen * slots);
-    bspan = ((bspan + tspan - 1) / tspan) * tspan;
-    if (bspan < tspan) bspan = tspan;
-    if (bspan > a.max_len) bspan = ((int64_t)a.max_len + tspan - 1) / tspan * tspan;
+    const int64_t cus = decode_cus();
+    int64_t per_cu = capacity_for(a.D, ch, rot) / cus;
+    per_cu = per_cu < 1 ? 1 : per_cu > kMaxSlotsPerCu ? kMaxSlotsPerCu : per_cu;
+    const int64_t nkind = cus / units_per_seq;  // blocks of each kind, in sequences
+    const int64_t sf = span_floor(a.max_len);
+    const int32_t tspan = (int32_t)sf * kTailFloors;
+
+    int64_t rem[ATTN_MAX_SEQS];
+    int32_t nk[kMaxSlotsPerCu][ATTN_MAX_SEQS] = {};
+    int64_t kspan[kMaxSlotsPerCu] = {};
+    for (int i = 0; i < ATTN_MAX_SEQS; ++i) rem[i] = i < a.M ? a.lens.v[i] : 0;
+    int64_t wsum = 0;
+    for (int k = 0; k < per_cu; ++k) wsum += kSlotWeight[k];
+    for (int k = 0; k < per_cu && nkind > 0; ++k) {
+        int64_t span = kFirstRoundPct * lsum * kSlotWeight[k] / (100 * nkind * wsum);
+        span = span / sf * sf;
+        if (span > a.max_len) span = (int64_t)a.max_len / sf * sf;
+        if (span < sf) continue;
+        kspan[k] = span;
+        // Blocks in proportion to the keys left (largest remainders next),
+        // never more than a sequence can hold.
+        int64_t left = 0;
+        for (int i = 0; i < a.M; ++i) left += rem[i];
+        if (left == 0) break;
+        int64_t given = 0;
+        for (int i = 0; i < a.M; ++i) {
+            const int64_t cap = rem[i] / span;
+            const int64_t want = nkind * rem[i] / left;
+            nk[k][i] = (int32_t)(want < cap ? want : cap);
+            given += nk[k][i];
+        }
+        while (given < nkind) {
+            int best = -1;
+            int64_t best_left = 0;
+            for (int i = 0; i < a.M; ++i) {
+                const int64_t after = rem[i] - (int64_t)nk[k][i] * span;
+                if (after >= span && after > best_left) {
+                    best = i;
+                    best_left = after;
+                }
+            }
+            if (best < 0) break;
+            ++nk[k][best];
+            ++given;
+        }
+        for (int i = 0; i < a.M; ++i) rem[i] -= (int64_t)nk[k][i] * span;
+    }
 
     SegMap map;
-    map.bulk_span = (int32_t)bspan;
-    map.tail_span = tspan;
-    int32_t nb[ATTN_MAX_SEQS], nt[ATTN_MAX_SEQS];
-    for (int i = 0; i < ATTN_MAX_SEQS; ++i) {
-        nb[i] = nt[i] = 0;
-        if (i >= a.M || a.lens.v[i] <= 0) continue;
-        const int64_t L = a.lens.v[i];
-        nb[i] = (int32_t)(kBulkNum * L / (kBulkDen * bspan));
-        nt[i] = (int32_t)((L - nb[i] * bspan + tspan - 1) / tspan);
-    }
-    // Segments in grid order: the bulk blocks of every sequence (most first),
-    // then the tail blocks (most first).
-    int32_t order[ATTN_MAX_SEQS];
     int nseg = 0;
     int32_t acc = 0;
-    for (int kind = 0; kind < 2; ++kind) {
-        const int32_t *cnt = kind == 0 ? nb : nt;
-        for (int i = 0; i < a.M; ++i) order[i] = i;
-        for (int i = 1; i < a.M; ++i) {  // insertion sort, stable, by block count descending
-            const int32_t x = order[i];
-            int j = i - 1;
-            while (j >= 0 && cnt[order[j]] < cnt[x]) {
-                order[j + 1] = order[j];
-                --j;
+    int32_t done[ATTN_MAX_SEQS] = {};    // blocks laid so far per sequence
+    int64_t kdone[ATTN_MAX_SEQS] = {};   // keys covered so far per sequence
+    auto add_segment = [&](int i, int32_t n, int64_t span) {
+        map.start[nseg] = acc;
+        map.kbase[nseg] = (int32_t)kdone[i];
+        map.span[nseg] = (int32_t)span;
+        map.npiece[nseg] = (int16_t)n;
+        map.seq[nseg] = (int8_t)i;
+        map.piece0[nseg] = (int8_t)done[i];
+        acc += n * (int32_t)units_per_seq;
+        done[i] += n;
+        ++nseg;
+    };
+    for (int k = 0; k < per_cu; ++k)
+        for (int i = 0; i < a.M; ++i)
+            if (nk[k][i] > 0) {
+                add_segment(i, nk[k][i], kspan[k]);
+                kdone[i] += (int64_t)nk[k][i] * kspan[k];
             }
-            order[j + 1] = x;
-        }
-        for (int i = 0; i < a.M; ++i) {
-            const int32_t sq = order[i];
-            if (cnt[sq] == 0) continue;
-            map.start[nseg] = acc;
-            map.seq[nseg] = sq;
-            map.piece0[nseg] = kind == 0 ? 0 : nb[sq];
-            map.npiece[nseg] = cnt[sq];
-            acc += cnt[sq] * (int32_t)units_per_seq;
-            ++nseg;
-        }
-        if (kind == 0) map.nbulk = nseg;
-    }
+    for (int i = 0; i < a.M; ++i)
+        if (rem[i] > 0) add_segment(i, (int32_t)((rem[i] + tspan - 1) / tspan), tspan);
     map.nseg = nseg;
     for (int i = nseg; i <= kMaxSegs; ++i) map.start[i] = acc;
-    for (int i = nseg; i < kMaxSegs; ++i) map.seq[i] = map.piece0[i] = map.npiece[i] = 0;
-    for (int i = 0; i < ATTN_MAX_SEQS; ++i) map.nsplit[i] = nb[i] + nt[i];
+    for (int i = nseg; i < kMaxSegs; ++i) {
+        map.kbase[i] = map.span[i] = 0;
+        map.npiece[i] = 0;
+        map.seq[i] = map.piece0[i] = 0;
+    }
+    for (int i = 0; i < ATTN_MAX_SEQS; ++i) map.nsplit[i] = done[i];
 
     dim3 block(kThreads);
     if (acc > 0) {
