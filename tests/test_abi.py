@@ -128,17 +128,24 @@ def test_decode_validation(lib):
 
 def test_decode_workspace_bytes(lib):
     # acc [M, H, splits, d] + (max, sum) [M, H, splits, 2] floats.  A split is
-    # one key block; a sequence has at most 64 key blocks of at least 128 keys
-    # (a power-of-two multiple of 128).
+    # one key block of at least a floor of keys, a power-of-two multiple of 128
+    # that keeps a sequence at <= 64 blocks; calls with M * ceil(H / 16) < 16
+    # may take 128, 256 or 512 blocks (doubled while M * ceil(H / 16) * n < 1024).
     assert lib.attn_decode_workspace_bytes(32, 32, 128, 4096) == 32 * 32 * 32 * 130 * 4
     assert lib.attn_decode_workspace_bytes(16, 64, 128, 32768) == 16 * 64 * 64 * 130 * 4
     assert lib.attn_decode_workspace_bytes(1, 1, 32, 1) == 1 * 1 * 1 * 34 * 4
     assert lib.attn_decode_workspace_bytes(2, 4, 64, 300) == 2 * 4 * 3 * 66 * 4
+    assert lib.attn_decode_workspace_bytes(8, 32, 128, 32768) == 8 * 32 * 64 * 130 * 4    # 16 units: 64
+    assert lib.attn_decode_workspace_bytes(4, 32, 128, 32768) == 4 * 32 * 128 * 130 * 4   # 8 units: 128
+    assert lib.attn_decode_workspace_bytes(1, 32, 128, 32768) == 1 * 32 * 256 * 130 * 4   # 512 at most; 128-key floor
+    assert lib.attn_decode_workspace_bytes(2, 8, 128, 60000) == 2 * 8 * 469 * 130 * 4     # 512 at most; 128-key floor
     assert lib.attn_decode_workspace_bytes(0, 8, 128, 16) == 0
     assert lib.attn_decode_workspace_bytes(33, 8, 128, 16) == 0
     assert lib.attn_decode_workspace_bytes(2, 8, 80, 16) == 0
-    # The largest supported cache: 2^30 rows, 64 key blocks of 2^24 keys.
-    assert lib.attn_decode_workspace_bytes(1, 1, 32, 2**30) == 64 * 34 * 4
+    # The largest supported cache: 2^30 rows, 64 key blocks of 2^24 keys, or for
+    # a single head 512 blocks of 2^21 keys.
+    assert lib.attn_decode_workspace_bytes(16, 1, 32, 2**30) == 16 * 64 * 34 * 4
+    assert lib.attn_decode_workspace_bytes(1, 1, 32, 2**30) == 512 * 34 * 4
     # Beyond it, up to the int32 limit, the size is refused rather than overflowing.
     assert lib.attn_decode_workspace_bytes(1, 1, 32, 2**30 + 1) == 0
     assert lib.attn_decode_workspace_bytes(1, 1, 32, 2**31 - 1) == 0

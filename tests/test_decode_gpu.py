@@ -43,6 +43,14 @@ LONG = [
     # M, H, Hkv, d, max_len, lowest length
     (16, 32, 16, 32, 32768, 24000),
     (8, 32, 16, 64, 32768, 28000),
+    # Calls of fewer than 16 (sequence, KV head, head block) units: equal key
+    # blocks, up to 512 splits per (m, h) and the 16-wave merge of the splits.
+    (1, 8, 1, 128, 65536, 65536),   # 512 splits, the most a sequence can have
+    (2, 8, 1, 128, 65536, 60000),
+    (1, 32, 8, 128, 32768, 32768),
+    (3, 20, 4, 64, 20000, 1),       # ragged: lengths from 1 up
+    (1, 15, 15, 32, 9000, 9000),    # 15 units: the last count that takes equal blocks
+    (1, 16, 16, 32, 9000, 9000),    # 16 units: the first-round decomposition again
 ]
 
 

@@ -90,7 +90,7 @@ int check_decode(const float *q, const float *k_cache, const float *v_cache, con
         !checked_mul({num_seqs, num_kv_heads, max_len, head_dim}, kMaxElems, &cache_elems))
         return ATTN_ERR_OVERFLOW;
     int64_t units;  // upper bound on pass-1 work units and workspace slots
-    if (!checked_mul({num_seqs, num_heads, attn::decode_max_splits(max_len)}, kMaxElems32, &units))
+    if (!checked_mul({num_seqs, num_heads, attn::decode_max_splits(num_seqs, num_heads, max_len)}, kMaxElems32, &units))
         return ATTN_ERR_OVERFLOW;
     *need = attn_decode_workspace_bytes(num_seqs, num_heads, head_dim, max_len);
     if (*need == 0) return ATTN_ERR_OVERFLOW;
@@ -99,7 +99,7 @@ int check_decode(const float *q, const float *k_cache, const float *v_cache, con
         return ATTN_ERR_ALIAS;
     *args = attn::DecodeArgs{q,    k_cache,  v_cache,   out,          nullptr,  nullptr,
                              lens, num_seqs, num_heads, num_kv_heads, head_dim, max_len,
-                             attn::decode_max_splits(max_len), scale};
+                             attn::decode_max_splits(num_seqs, num_heads, max_len), scale};
     return ATTN_OK;
 }
 
@@ -368,7 +368,7 @@ size_t attn_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t 
     if (num_seqs < 1 || num_seqs > ATTN_MAX_SEQS || num_heads <= 0 || max_len <= 0) return 0;
     if (!head_dim_ok(head_dim) || max_len > kMaxDecodeLen) return 0;
     int64_t slots;
-    if (!checked_mul({num_seqs, num_heads, attn::decode_max_splits(max_len), head_dim + 2}, kMaxElems,
+    if (!checked_mul({num_seqs, num_heads, attn::decode_max_splits(num_seqs, num_heads, max_len), head_dim + 2}, kMaxElems,
                      &slots))
         return 0;
     return attn::decode_workspace_bytes(num_seqs, num_heads, head_dim, max_len);

@@ -22,7 +22,10 @@
 // with M* = max_s m_s and w_s = 2^(m_s - M*), out = sum_s w_s acc_s /
 // sum_s w_s l_s, or zeros when the sequence is empty, folded split by split in
 // split order with a running max (the same identity applied incrementally),
-// so the result is the same on every run.
+// so the result is the same on every run.  When a sequence has more than 16
+// splits (calls of one or a few sequences, up to 512 splits),
+// decode_combine_wide_kernel gives each (m, h) sixteen waves, each folding a
+// contiguous range of the splits, and folds their states in range order.
 //
 // Register layouts of v_mfma_f32_16x16x4_f32 (lane l, i = l % 16, k = l / 16):
 // operand A supplies A[i][k], operand B supplies B[k][i], and output register
@@ -71,7 +74,7 @@ struct SegMap {
     int32_t span[kMaxSegs];         // keys per block
     int16_t npiece[kMaxSegs];       // its blocks per unit
     int8_t seq[kMaxSegs];           // its sequence
-    int8_t piece0[kMaxSegs];        // split slot of its first block
+    int16_t piece0[kMaxSegs];       // split slot of its first block
     int32_t nsplit[ATTN_MAX_SEQS];  // key blocks per unit of each sequence
     int32_t nseg;
 };
@@ -366,58 +369,136 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     }
 }
 
+// Folds splits [s_lo, s_hi) of one (m, h) into the running (m_run, l_run,
+// acc) in split order, loads of BATCH splits in flight together (the merge
+// waits on one memory latency per batch, about a microsecond).  Lane l holds
+// output columns PER*l .. PER*l + PER - 1 (lanes >= LANES hold none).
+template <int D>
+struct Fold {
+    static constexpr int PER = D >= 64 ? D / 64 : 1;  // floats per lane
+    static constexpr int LANES = D / PER;             // lanes holding output columns
+    static constexpr int BATCH = 16;
+    typedef typename VecN<PER>::type pvec;
+
+    __device__ static void run(const float *ml, const float *accp, int s_lo, int s_hi, int lane, float &m_run,
+                               float &l_run, pvec &acc) {
+        for (int s0 = s_lo; s0 < s_hi; s0 += BATCH) {
+            f32x2 mlv[BATCH];
+            pvec av[BATCH];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) {
+                const int s = s0 + b;
+                const bool ok = s < s_hi;
+                mlv[b] = ok ? *reinterpret_cast<const f32x2 *>(ml + 2 * s) : f32x2{kNegBig, 0.f};
+                av[b] = (ok && lane < LANES) ? *reinterpret_cast<const pvec *>(accp + (size_t)s * D) : pvec{};
+            }
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) merge(m_run, l_run, acc, mlv[b][0], mlv[b][1], av[b]);
+        }
+    }
+
+    // (m_run, l_run, acc) <- the fold of itself and one more state (m, l, a).
+    __device__ static void merge(float &m_run, float &l_run, pvec &acc, float m, float l, const pvec &a) {
+        const float m_new = fmaxf(m_run, m);
+        const float keep = fast_exp2(m_run - m_new), take = fast_exp2(m - m_new);
+        l_run = l_run * keep + l * take;
+        acc = acc * keep + a * take;
+        m_run = m_new;
+    }
+};
+
 // One wave per (m, h): folds the nsplit[m] splits in split order with a
-// running max (loads of 8 splits in flight together) and writes
-// out[m][h] = acc / l, or zeros for an empty sequence.
+// running max and writes out[m][h] = acc / l, or zeros for an empty sequence.
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeArgs a, SegMap map) {
-    constexpr int PER = D >= 64 ? D / 64 : 1;  // floats per lane
-    constexpr int LANES = D / PER;             // lanes holding output columns
-    constexpr int BATCH = 8;
-    typedef typename VecN<PER>::type pvec;
+    typedef Fold<D> F;
     const int lane = threadIdx.x & (kWave - 1);
     const int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     if (w >= a.M * a.H) return;  // no barrier below
-    const int m = w / a.H;
-    const int nsplit = map.nsplit[m];
+    const int nsplit = map.nsplit[w / a.H];
     const size_t slot0 = (size_t)w * a.max_splits;
-    const float *ml = a.ws_ml + 2 * slot0;
-    const float *accp = a.ws_acc + slot0 * D + PER * lane;
     float m_run = kNegBig, l_run = 0.f;
-    pvec acc{};
-    for (int s0 = 0; s0 < nsplit; s0 += BATCH) {
-        f32x2 mlv[BATCH];
-        pvec av[BATCH];
-#pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-            const int s = s0 + b;
-            const bool ok = s < nsplit;
-            mlv[b] = ok ? *reinterpret_cast<const f32x2 *>(ml + 2 * s) : f32x2{kNegBig, 0.f};
-            av[b] = (ok && lane < LANES) ? *reinterpret_cast<const pvec *>(accp + (size_t)s * D) : pvec{};
-        }
-#pragma unroll
-        for (int b = 0; b < BATCH; ++b) {
-            const float m_new = fmaxf(m_run, mlv[b][0]);
-            const float keep = fast_exp2(m_run - m_new), take = fast_exp2(mlv[b][0] - m_new);
-            l_run = l_run * keep + mlv[b][1] * take;
-            acc = acc * keep + av[b] * take;
-            m_run = m_new;
-        }
+    typename F::pvec acc{};
+    F::run(a.ws_ml + 2 * slot0, a.ws_acc + slot0 * D + F::PER * lane, 0, nsplit, lane, m_run, l_run, acc);
+    if (lane < F::LANES)
+        *reinterpret_cast<typename F::pvec *>(a.out + (size_t)w * D + F::PER * lane) =
+            nsplit > 0 ? acc * (1.0f / l_run) : typename F::pvec{};
+}
+
+// For calls whose sequences have many splits: one workgroup of kWideWaves
+// waves per (m, h).  Wave v folds the v-th of kWideWaves contiguous ranges of
+// the splits, then wave 0 folds the waves' states in wave order, so the
+// splits are still combined in one fixed order on every run.
+constexpr int kWideWaves = 16;
+constexpr int kWideSplits = Fold<32>::BATCH;  // the wide merge runs when a sequence has more splits
+
+template <int D>
+__global__ __launch_bounds__(kWideWaves * kWave) void decode_combine_wide_kernel(DecodeArgs a, SegMap map) {
+    typedef Fold<D> F;
+    __shared__ float st_acc[kWideWaves][D];
+    __shared__ float st_ml[kWideWaves][2];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int v = threadIdx.x >> 6;
+    const int w = blockIdx.x;  // (m, h); the grid is exactly M * H
+    const int nsplit = map.nsplit[w / a.H];
+    const int per = (nsplit + kWideWaves - 1) / kWideWaves;
+    const int s_lo = min(v * per, nsplit), s_hi = min(s_lo + per, nsplit);
+    const size_t slot0 = (size_t)w * a.max_splits;
+    float m_run = kNegBig, l_run = 0.f;
+    typename F::pvec acc{};
+    F::run(a.ws_ml + 2 * slot0, a.ws_acc + slot0 * D + F::PER * lane, s_lo, s_hi, lane, m_run, l_run, acc);
+    if (lane < F::LANES) *reinterpret_cast<typename F::pvec *>(&st_acc[v][F::PER * lane]) = acc;
+    if (lane == 0) {
+        st_ml[v][0] = m_run;
+        st_ml[v][1] = l_run;
     }
-    if (lane < LANES)
-        *reinterpret_cast<pvec *>(a.out + (size_t)w * D + PER * lane) = nsplit > 0 ? acc * (1.0f / l_run) : pvec{};
+    __syncthreads();
+    if (v != 0) return;
+    m_run = kNegBig;
+    l_run = 0.f;
+    acc = typename F::pvec{};
+    for (int u = 0; u < kWideWaves; ++u) {
+        const typename F::pvec au =
+            lane < F::LANES ? *reinterpret_cast<const typename F::pvec *>(&st_acc[u][F::PER * lane])
+                            : typename F::pvec{};
+        F::merge(m_run, l_run, acc, st_ml[u][0], st_ml[u][1], au);
+    }
+    if (lane < F::LANES)
+        *reinterpret_cast<typename F::pvec *>(a.out + (size_t)w * D + F::PER * lane) =
+            nsplit > 0 ? acc * (1.0f / l_run) : typename F::pvec{};
 }
 
 constexpr int32_t kSpanQuantum = 128;  // keys: one 32-key chunk per wave
-constexpr int32_t kMaxKeyBlocks = 64;                        // per (sequence, head): workspace bound
+constexpr int32_t kMaxKeyBlocks = 64;       // per (sequence, head), calls with many units
+constexpr int32_t kMaxKeyBlocksFew = 512;   // per (sequence, head), calls with few units
+constexpr int64_t kKeyBlocksWanted = 1024;  // key blocks per call: about four per CU
+
+// Key blocks a sequence may be cut into when a call has `units` work units
+// (sequence, KV head, head block) over all its sequences: 64, doubled up to
+// 512 while the call would have fewer than kKeyBlocksWanted blocks in all, so
+// that a call of one or two sequences still fills the device.
+int32_t key_block_limit(int64_t units) {
+    int32_t n = kMaxKeyBlocks;
+    while (n < kMaxKeyBlocksFew && units * n < kKeyBlocksWanted) n *= 2;
+    return n;
+}
 
 // Smallest key-block span for a cache of max_len rows: a power-of-two multiple
-// of the quantum that keeps a sequence at <= kMaxKeyBlocks key blocks (64-bit
+// of the quantum that keeps a sequence at <= `limit` key blocks (64-bit
 // arithmetic: max_len may be any positive int32).
-int32_t span_floor(int32_t max_len) {
+int32_t span_floor(int32_t max_len, int32_t limit) {
     int64_t s = kSpanQuantum;
-    while (((int64_t)max_len + s - 1) / s > kMaxKeyBlocks) s *= 2;
+    while (((int64_t)max_len + s - 1) / s > limit) s *= 2;
     return (int32_t)s;
+}
+
+// Splits a call of M sequences and H query heads may write per (m, h).  A
+// sequence's units number num_kv_heads * ceil(group / 16) >= ceil(H / 16),
+// so the launch, which sizes its floor from its actual units, never uses a
+// smaller floor (more blocks) than this bound allows.
+int32_t max_splits_for(int64_t M, int64_t H, int32_t max_len) {
+    const int64_t sf = span_floor(max_len, key_block_limit(M * ((H + 15) / 16)));
+    return (int32_t)(((int64_t)max_len + sf - 1) / sf);
 }
 
 // The first round of the grid carries about kFirstRoundPct percent of the
@@ -438,6 +519,11 @@ constexpr int64_t kSlotWeight[kMaxSlotsPerCu] = {100, 72, 28};
 // of a short call (M 32, up to 4096 keys: 92 -> 88 us); long contexts keep
 // 32-key chunks (M 16, 16K-32K keys: 1-3% faster than 16).
 constexpr int64_t kShortKeysPerSlot = 4096;
+
+// Blocks per CU for a call of few units, all of one span: on such calls equal
+// blocks, two per CU, ran faster than the slot-sized first round (M 1, 8 KV
+// heads, 131072 keys: split pass 164 against 178 us).
+constexpr int64_t kFewBlocksPerCu = 2;
 
 // Workgroups of decode_split_kernel<D, CH, ROPE> that fit on the device at
 // once (CUs x resident blocks per CU), queried once per device and kernel.
@@ -499,13 +585,10 @@ void launch_split(bool rot, dim3 grid, hipStream_t stream, const DecodeArgs &a, 
 
 }  // namespace
 
-int32_t decode_max_splits(int32_t max_len) {
-    const int64_t sf = span_floor(max_len);
-    return (int32_t)(((int64_t)max_len + sf - 1) / sf);
-}
+int32_t decode_max_splits(int32_t M, int32_t H, int32_t max_len) { return max_splits_for(M, H, max_len); }
 
 size_t decode_workspace_bytes(int64_t M, int64_t H, int64_t D, int64_t max_len) {
-    const int64_t slots = M * H * (int64_t)decode_max_splits((int32_t)max_len);
+    const int64_t slots = M * H * (int64_t)max_splits_for(M, H, (int32_t)max_len);
     return (size_t)(slots * (D + 2) * (int64_t)sizeof(float));
 }
 
@@ -522,8 +605,13 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
     // sequences with the most keys left, in key order: a sequence's kind-0
     // blocks come first, then its kind-1 blocks, ...  The keys left after the
     // first round go to tail blocks of kTailFloors x span_floor keys, which
-    // run last.  Every span is a multiple of span_floor, so a sequence of L
-    // keys has at most ceil(L / span_floor) <= max_splits blocks.
+    // run last.  A call of few units (fewer than kKeyBlocksWanted /
+    // kMaxKeyBlocks over all its sequences) has no first round: its
+    // sequences are cut into equal blocks, about kFewBlocksPerCu per CU over
+    // the call.  Every span is at least span_floor (the floor for the call's
+    // own units, no smaller than the one the workspace was sized with), so a
+    // sequence of L keys has at most ceil(L / span_floor) <= max_splits
+    // blocks: all but its last block hold span_floor keys or more.
     int64_t lsum = 0;
     for (int i = 0; i < a.M; ++i) lsum += a.lens.v[i];
     const int64_t total = lsum * units_per_seq;
@@ -532,9 +620,16 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
     const int64_t cus = decode_cus();
     int64_t per_cu = capacity_for(a.D, ch, rot) / cus;
     per_cu = per_cu < 1 ? 1 : per_cu > kMaxSlotsPerCu ? kMaxSlotsPerCu : per_cu;
-    const int64_t nkind = cus / units_per_seq;  // blocks of each kind, in sequences
-    const int64_t sf = span_floor(a.max_len);
-    const int32_t tspan = (int32_t)sf * kTailFloors;
+    const int64_t call_units = (int64_t)a.M * units_per_seq;
+    const int64_t sf = span_floor(a.max_len, key_block_limit(call_units));
+    const bool few = call_units * kMaxKeyBlocks < kKeyBlocksWanted;
+    int64_t tspan = sf * kTailFloors;
+    if (few) {
+        const int64_t blocks = kFewBlocksPerCu * cus;
+        const int64_t even = ((total + blocks - 1) / blocks + kSpanQuantum - 1) / kSpanQuantum * kSpanQuantum;
+        tspan = even > sf ? even : sf;  // below max_len + kSpanQuantum: total < 16 * max_len
+    }
+    const int64_t nkind = few ? 0 : cus / units_per_seq;  // blocks of each kind, in sequences
 
     int64_t rem[ATTN_MAX_SEQS];
     int32_t nk[kMaxSlotsPerCu][ATTN_MAX_SEQS] = {};
@@ -588,7 +683,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
         map.span[nseg] = (int32_t)span;
         map.npiece[nseg] = (int16_t)n;
         map.seq[nseg] = (int8_t)i;
-        map.piece0[nseg] = (int8_t)done[i];
+        map.piece0[nseg] = (int16_t)done[i];
         acc += n * (int32_t)units_per_seq;
         done[i] += n;
         ++nseg;
@@ -600,7 +695,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
                 kdone[i] += (int64_t)nk[k][i] * kspan[k];
             }
     for (int i = 0; i < a.M; ++i)
-        if (rem[i] > 0) add_segment(i, (int32_t)((rem[i] + tspan - 1) / tspan), tspan);
+        if (rem[i] > 0) add_segment(i, (int32_t)((rem[i] + tspan - 1) / tspan), (int32_t)tspan);
     map.nseg = nseg;
     for (int i = nseg; i <= kMaxSegs; ++i) map.start[i] = acc;
     for (int i = nseg; i < kMaxSegs; ++i) {
@@ -626,6 +721,18 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+    }
+    int32_t most = 0;
+    for (int i = 0; i < a.M; ++i) most = done[i] > most ? done[i] : most;
+    if (most > kWideSplits) {
+        dim3 grid2(a.M * a.H), block2(kWideWaves * kWave);
+        switch (a.D) {
+            case 32: decode_combine_wide_kernel<32><<<grid2, block2, 0, stream>>>(a, map); break;
+            case 64: decode_combine_wide_kernel<64><<<grid2, block2, 0, stream>>>(a, map); break;
+            case 128: decode_combine_wide_kernel<128><<<grid2, block2, 0, stream>>>(a, map); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
     }
     dim3 grid2((a.M * a.H + kWavesPerBlock - 1) / kWavesPerBlock);
     switch (a.D) {

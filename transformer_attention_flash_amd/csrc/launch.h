@@ -86,7 +86,7 @@ struct DecodeArgs {
     float scale;
 };
 // Number of split slots per (sequence, head) the workspace must hold.
-int32_t decode_max_splits(int32_t max_len);
+int32_t decode_max_splits(int32_t M, int32_t H, int32_t max_len);
 // Bytes of workspace for (M, H, D, max_len); 0 if it overflows.
 size_t decode_workspace_bytes(int64_t M, int64_t H, int64_t D, int64_t max_len);
 // With rope (rotary_ndims > 0) each sequence's query is rotated to position
