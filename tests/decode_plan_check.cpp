@@ -59,8 +59,8 @@ bool check_call(const int32_t *lens, int32_t M, int32_t H, int32_t Hkv, int32_t 
         const int s = (int)(next_u64() % (uint64_t)m.nseg);
         switch (next_u64() % 3) {
             case 0: m.kbase[s] += 1; break;   // a gap of one key
-            case 1: m.piece0[s] += 1; break;  // a split slot out of order
-            default: m.npiece[s] += 1; break; // one block too many
+            case 1: m.info[s] += 1u << 20; break;  // a split slot out of order
+            default: m.info[s] += 1u << 8; break;  // one block too many
         }
         ++*altered;
     }
@@ -74,9 +74,11 @@ bool check_call(const int32_t *lens, int32_t M, int32_t H, int32_t Hkv, int32_t 
     int64_t grid = 0;
     for (int s = 0; s < m.nseg; ++s) {
         CHECK(m.start[s] == grid, "segment %d starts at %d, expected %lld", s, m.start[s], (long long)grid);
-        CHECK(m.npiece[s] >= 1 && m.span[s] >= 1, "segment %d: %d blocks of %d keys", s, m.npiece[s], m.span[s]);
-        CHECK(m.seq[s] >= 0 && m.seq[s] < M, "segment %d: sequence %d", s, m.seq[s]);
-        grid += (int64_t)m.npiece[s] * units;
+        const int32_t np = seg_npiece(m.info[s]), sq = seg_seq(m.info[s]);
+        CHECK(np >= 1 && m.span[s] >= 1, "segment %d: %d blocks of %d keys", s, np, m.span[s]);
+        CHECK(sq < M, "segment %d: sequence %d", s, sq);
+        CHECK(seg_info(sq, np, seg_piece0(m.info[s])) == m.info[s], "segment %d: fields overflow", s);
+        grid += (int64_t)np * units;
     }
     CHECK(grid == plan.grid && grid < (1ll << 31), "grid %d, segments give %lld", plan.grid, (long long)grid);
     for (int s = m.nseg; s <= kMaxSegs; ++s) CHECK(m.start[s] == plan.grid, "start[%d] past the last segment", s);
@@ -84,13 +86,13 @@ bool check_call(const int32_t *lens, int32_t M, int32_t H, int32_t Hkv, int32_t 
     for (int i = 0; i < M; ++i) {
         std::vector<Block> blocks;
         for (int s = 0; s < m.nseg; ++s) {
-            if (m.seq[s] != i) continue;
-            for (int p = 0; p < m.npiece[s]; ++p) {
+            if (seg_seq(m.info[s]) != i) continue;
+            for (int p = 0; p < seg_npiece(m.info[s]); ++p) {
                 const int64_t k0 = (int64_t)m.kbase[s] + (int64_t)p * m.span[s];
                 const int64_t k1 = std::min<int64_t>(k0 + m.span[s], lens[i]);
                 CHECK(k0 < k1, "sequence %d: empty block [%lld, %lld)", i, (long long)k0, (long long)k1);
                 CHECK(k0 + m.span[s] < (1ll << 31), "sequence %d: key index overflows int32", i);
-                blocks.push_back({m.piece0[s] + p, k0, k1});
+                blocks.push_back({seg_piece0(m.info[s]) + p, k0, k1});
             }
         }
         std::sort(blocks.begin(), blocks.end(), [](const Block &x, const Block &y) { return x.slot < y.slot; });

@@ -34,6 +34,7 @@
 // operand-B value that lane supplies at key step r of the P.V contraction
 // O^T = V^T P^T: no data moves between the two products.
 #include <atomic>
+#include <climits>
 
 #include "decode_plan.h"
 #include "device_common.h"
@@ -86,20 +87,38 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a,
     // workgroup -> (segment s, unit, block p of the segment) -> (m, kh, head
     // block hb, split slot kblk, keys [k0, k1)).  Wave w of the workgroup
     // takes chunks w, w + 4, w + 8, ... of the key block, so the four waves
-    // stream adjacent 32-key chunks of K (and of V) side by side.
-    int s = 0;
-    for (int hi_s = map.nseg; hi_s - s > 1;) {  // last segment with start <= wg
-        const int mid = (s + hi_s) >> 1;
-        if (wg >= map.start[mid]) s = mid; else hi_s = mid;
+    // stream adjacent 32-key chunks of K (and of V) side by side.  The
+    // segment is the number of segment starts <= wg, less one (starts
+    // increase, and the entries past the last segment hold the grid size).
+    // The lanes load every start and every sequence length at once and the
+    // values needed are read from their lanes, so that the lookup waits on
+    // two loads (the starts, then the segment's fields), not on a search
+    // whose every step waits on one.
+    constexpr int kStartLoads = (kMaxSegs + kWave) / kWave;  // kMaxSegs + 1 starts
+    static_assert(ATTN_MAX_SEQS <= kWave, "one sequence length per lane");
+    int st[kStartLoads];
+#pragma unroll
+    for (int c = 0; c < kStartLoads; ++c) {
+        const int i = c * kWave + lane;
+        st[c] = i <= kMaxSegs ? map.start[i] : INT_MAX;
     }
-    const int m = map.seq[s];
-    const int L = a.lens.v[m];
-    const int npiece = map.npiece[s];
-    const int rem = wg - map.start[s];
+    const int len_lane = lane < ATTN_MAX_SEQS ? a.lens.v[lane] : 0;
+    int s = -1;
+#pragma unroll
+    for (int c = 0; c < kStartLoads; ++c) s += __popcll(__ballot(st[c] <= wg));
+    // s < nseg <= kMaxSegs, so its start is held by lane s % 64 of load s / 64
+    int st_s = st[0];
+#pragma unroll
+    for (int c = 1; c < kStartLoads; ++c) st_s = s >= c * kWave ? st[c] : st_s;
+    const uint32_t info = map.info[s];
+    const int m = seg_seq(info);
+    const int L = __builtin_amdgcn_readlane(len_lane, m);
+    const int npiece = seg_npiece(info);
+    const int rem = wg - __builtin_amdgcn_readlane(st_s, s & (kWave - 1));
     const int p = rem % npiece;
     const int hb = (rem / npiece) % n_hblk;
     const int kh = (rem / npiece) / n_hblk;
-    const int kblk = map.piece0[s] + p;
+    const int kblk = seg_piece0(info) + p;
     const int k0 = map.kbase[s] + p * map.span[s];  // the workgroup's keys are [k0, k1)
     const int k1 = min(k0 + map.span[s], L);
 

@@ -17,26 +17,36 @@ namespace attn {
 // sequence and one span: segment s holds npiece[s] blocks per unit, of
 // span[s] keys each from key kbase[s] on (a block is clipped to the sequence
 // length), and workgroup start[s] + u * npiece[s] + p runs block p of unit u,
-// whose split slot is piece0[s] + p.  plan_decode orders the segments so
+// whose split slot is piece0[s] + p; sequence, npiece and piece0 share one
+// word (seg_info), so that a workgroup reads its segment in one round trip.
+// plan_decode orders the segments so
 // that the blocks of the device's first round come first, sized for the slot
 // each will occupy, and small tail blocks after them.
 constexpr int kMaxSlotsPerCu = 3;  // first-round block kinds (workgroups per CU)
 constexpr int kMaxSegs = (kMaxSlotsPerCu + 1) * ATTN_MAX_SEQS;
 struct SegMap {
-    int32_t start[kMaxSegs + 1];    // first workgroup of segment s; start[nseg] = grid size
+    int32_t start[kMaxSegs + 1];    // first workgroup of segment s; from nseg on, the grid size
     int32_t kbase[kMaxSegs];        // first key of its first block
     int32_t span[kMaxSegs];         // keys per block
-    int16_t npiece[kMaxSegs];       // its blocks per unit
-    int8_t seq[kMaxSegs];           // its sequence
-    int16_t piece0[kMaxSegs];       // split slot of its first block
+    uint32_t info[kMaxSegs];        // seg_info(sequence, npiece, piece0)
     int32_t nsplit[ATTN_MAX_SEQS];  // key blocks per unit of each sequence
     int32_t nseg;
 };
+
+// Sequence (8 bits), blocks per unit and first split slot (12 bits each) of a
+// segment; a sequence has at most kMaxKeyBlocksFew <= 4095 blocks.
+constexpr uint32_t seg_info(int32_t seq, int32_t npiece, int32_t piece0) {
+    return (uint32_t)seq | (uint32_t)npiece << 8 | (uint32_t)piece0 << 20;
+}
+constexpr int32_t seg_seq(uint32_t info) { return (int32_t)(info & 0xffu); }
+constexpr int32_t seg_npiece(uint32_t info) { return (int32_t)((info >> 8) & 0xfffu); }
+constexpr int32_t seg_piece0(uint32_t info) { return (int32_t)(info >> 20); }
 
 constexpr int32_t kSpanQuantum = 128;  // keys: one 32-key chunk per wave
 constexpr int32_t kMaxKeyBlocks = 64;       // per (sequence, head), calls with many units
 constexpr int32_t kMaxKeyBlocksFew = 512;   // per (sequence, head), calls with few units
 constexpr int64_t kKeyBlocksWanted = 1024;  // key blocks per call: about four per CU
+static_assert(kMaxKeyBlocksFew < 4096 && ATTN_MAX_SEQS <= 256, "seg_info field widths");
 
 // Key blocks a sequence may be cut into when a call has `units` work units
 // (sequence, KV head, head block) over all its sequences: 64, doubled up to
@@ -189,9 +199,7 @@ inline void plan_decode(const int32_t *lens, int32_t M, int32_t H, int32_t Hkv, 
         map.start[nseg] = acc;
         map.kbase[nseg] = (int32_t)kdone[i];
         map.span[nseg] = (int32_t)span;
-        map.npiece[nseg] = (int16_t)n;
-        map.seq[nseg] = (int8_t)i;
-        map.piece0[nseg] = (int16_t)done[i];
+        map.info[nseg] = seg_info(i, n, done[i]);
         acc += n * (int32_t)units_per_seq;
         done[i] += n;
         ++nseg;
@@ -208,8 +216,7 @@ inline void plan_decode(const int32_t *lens, int32_t M, int32_t H, int32_t Hkv, 
     for (int i = nseg; i <= kMaxSegs; ++i) map.start[i] = acc;
     for (int i = nseg; i < kMaxSegs; ++i) {
         map.kbase[i] = map.span[i] = 0;
-        map.npiece[i] = 0;
-        map.seq[i] = map.piece0[i] = 0;
+        map.info[i] = 0;
     }
     for (int i = 0; i < ATTN_MAX_SEQS; ++i) map.nsplit[i] = done[i];
 
