@@ -51,6 +51,9 @@ LONG = [
     (3, 20, 4, 64, 20000, 1),       # ragged: lengths from 1 up
     (1, 15, 15, 32, 9000, 9000),    # 15 units: the last count that takes equal blocks
     (1, 16, 16, 32, 9000, 9000),    # 16 units: the first-round decomposition again
+    # 512 units (twice the CUs): the first round's largest block would exceed every
+    # sequence and is clamped to the longest one left
+    (16, 32, 32, 64, 2048, 1900),
 ]
 
 

@@ -559,7 +559,10 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream, const RopePara
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (plan.most > kWideSplits) {
+    // The 16-wave merge when a sequence has more splits than one batch and
+    // there are no more (m, h) than CUs (one workgroup each); with more, one
+    // wave per (m, h) folding batch after batch keeps the device fuller.
+    if (plan.most > kWideSplits && (int64_t)a.M * a.H <= decode_cus()) {
         dim3 grid2(a.M * a.H), block2(kWideWaves * kWave);
         switch (a.D) {
             case 32: decode_combine_wide_kernel<32><<<grid2, block2, 0, stream>>>(a, map); break;

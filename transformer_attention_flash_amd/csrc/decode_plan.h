@@ -84,7 +84,7 @@ inline int32_t max_splits_for(int64_t M, int64_t H, int32_t max_len) {
 // third at about a quarter, so the first round's block for the k-th
 // workgroup of a CU is sized by kSlotWeight[k] (percent), and all of them
 // finish at about the same time.
-constexpr int64_t kFirstRoundPct = 90;
+constexpr int64_t kFirstRoundPct = 95;
 constexpr int32_t kTailFloors = 1;
 constexpr int64_t kSlotWeight[kMaxSlotsPerCu] = {100, 72, 28};
 
@@ -157,8 +157,11 @@ inline void plan_decode(const int32_t *lens, int32_t M, int32_t H, int32_t Hkv, 
     for (int k = 0; k < per_cu; ++k) wsum += kSlotWeight[k];
     for (int k = 0; k < per_cu && nkind > 0; ++k) {
         int64_t span = kFirstRoundPct * lsum * kSlotWeight[k] / (100 * nkind * wsum);
+        // no longer than the longest sequence left, or no sequence could take one
+        int64_t longest = 0;
+        for (int i = 0; i < M; ++i) longest = rem[i] > longest ? rem[i] : longest;
+        if (span > longest) span = longest;
         span = span / sf * sf;
-        if (span > max_len) span = (int64_t)max_len / sf * sf;
         if (span < sf) continue;
         kspan[k] = span;
         // Blocks in proportion to the keys left (largest remainders next),
