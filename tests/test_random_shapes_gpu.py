@@ -5,7 +5,8 @@ fixed seed instead, so that work decompositions nobody picked by hand are
 compared too.  Decode draws batches up to 32 sequences, group sizes 1 to 20,
 every head_dim and cache lengths up to 4000, with an empty, a one-key and a
 full sequence in every batch of three or more: the launcher's split into bulk
-and tail key blocks then sees sequence mixes of every kind.  Prefill draws
+and tail key blocks then sees sequence mixes of every kind; a second set draws
+caches of up to 70000 rows and mostly one to four sequences.  Prefill draws
 batch, length, heads, head_dim and causality (every small-problem and 4-wave
 decomposition), the chunked prefill draws cached lengths behind a GQA cache,
 and the append draws positions and row counts.  Attention outputs are compared
@@ -38,6 +39,27 @@ def _decode_cases(n=48, seed=7777):
         if M >= 3:
             lens[:3] = [0, 1, max_len]
             rng.shuffle(lens)
+        cases.append((M, Hkv * g, Hkv, d, max_len, [int(x) for x in lens]))
+    return cases
+
+
+def _decode_cases_wide(n=48, seed=4242):
+    """Caches of 1 to 70000 rows (log-uniform), batches weighted to one or a few
+    sequences, group sizes up to 32: calls of few units (equal key blocks, up to
+    512 splits per head and the 16-wave merge) as often as calls of many, full,
+    ragged and top-half lengths."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        d = int(rng.choice([32, 64, 128]))
+        Hkv = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        g = int(rng.choice([1, 2, 4, 5, 8, 16, 17, 32]))
+        M = int(rng.choice([1, 1, 2, 3, 4, 8, 16, 32]))
+        max_len = int(np.exp(rng.uniform(0, np.log(70000))))
+        max_len = max(1, min(max_len, 2 * CACHE_CAP // (M * Hkv * d * 4)))
+        mode = rng.integers(3)
+        lens = (rng.integers(0, max_len + 1, size=M) if mode == 0 else np.full(M, max_len) if mode == 1
+                else rng.integers(max_len // 2, max_len + 1, size=M))
         cases.append((M, Hkv * g, Hkv, d, max_len, [int(x) for x in lens]))
     return cases
 
@@ -83,7 +105,7 @@ def _scatter_cases(n=16, seed=6666):
     return cases
 
 
-DECODE = _decode_cases()
+DECODE = _decode_cases() + _decode_cases_wide()
 PREFILL = _prefill_cases()
 CHUNK = _chunk_cases()
 SCATTER = _scatter_cases()
