@@ -86,6 +86,10 @@ def parse():
                    help="skip the separately timed chunked-prefill-behind-cache measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 3 times (counter calibration) and exit")
+    p.add_argument("--decode-shape", metavar="M,H,HKV,D,MAX_LEN,L",
+                   help="only time the decode of one shape (every sequence L keys; seeded normal caches and "
+                        "queries made on the GPU; a 1 GiB fill before each call) over --steps calls, print "
+                        "one JSON line and exit")
     return p.parse_args()
 
 
@@ -219,6 +223,28 @@ def time_call(torch, run, filler=None, warm=5, reps=10, evict=None):
     return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
 
 
+def decode_shape(torch, taf, wl, dev, args):
+    """One decode shape on its own: batch M, H query heads over Hkv KV heads of
+    head_dim D, caches of MAX_LEN rows of which every sequence attends L."""
+    M, H, Hkv, d, max_len, L = (int(x) for x in args.decode_shape.split(","))
+    g = torch.Generator(device=dev)
+    g.manual_seed(20240611)
+    kc = torch.randn(M, Hkv, max_len, d, device=dev, generator=g)
+    vc = torch.randn(M, Hkv, max_len, d, device=dev, generator=g)
+    q = torch.randn(M, H * d, device=dev, generator=g)
+    out = torch.empty_like(q)
+    lens = [L] * M
+    ws = torch.empty(taf.attn_decode_workspace_bytes(M, H, d, max_len) // 4, device=dev)
+    scale = wl.scale_for(d)
+    run = lambda: taf.attn_decode_gqa_batched(q, kc, vc, lens, out, M, H, Hkv, d, max_len, scale, ws)
+    ms = time_call(torch, run, reps=max(1, args.steps), evict=Evictor(torch, dev))
+    nbytes = 2 * Hkv * d * 4 * M * L + 2 * M * H * d * 4
+    print(json.dumps({"decode_shape": {"M": M, "H": H, "Hkv": Hkv, "d": d, "max_len": max_len, "L": L},
+                      "median_us": round(ms * 1e3, 2), "algorithmic_bytes": nbytes,
+                      "gbs": round(nbytes / ms / 1e6, 1), "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                      "note": "median of the timed calls, a 1 GiB fill before each, outside its events"}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -245,6 +271,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes_per_dispatch": {"read": 1 << 30, "write": 1 << 30}}))
         return
     taf.library()  # fail loudly before any setup if the HIP library is missing
+    if args.decode_shape:
+        decode_shape(torch, taf, wl, dev, args)
+        return
 
     pcfg, scfg, dcfg = wl.PREFILL[3], wl.BULK_SCATTER, wl.DECODE[5]
 
