@@ -96,9 +96,10 @@ constexpr int64_t kSlotWeight[kMaxSlotsPerCu] = {100, 72, 28};
 constexpr int64_t kShortKeysPerSlot = 4096;
 
 // Blocks per CU for a call of few units, all of one span: on such calls equal
-// blocks, two per CU, ran faster than the slot-sized first round (M 1, 8 KV
-// heads, 131072 keys: split pass 164 against 178 us).
-constexpr int64_t kFewBlocksPerCu = 2;
+// blocks ran faster than the slot-sized first round (M 1, 8 KV heads, 131072
+// keys: split pass 164 against 178 us), and one per CU faster than two (one
+// KV head, 65536 keys: 25.6 against 30.7 us, half as many splits to merge).
+constexpr int64_t kFewBlocksPerCu = 1;
 
 // The decomposition of one call.  ch: keys per chunk (16 or 32) of the
 // split kernel; grid: its workgroups; most: the largest nsplit[m].
