@@ -23,9 +23,10 @@
 // sum_s w_s l_s, or zeros when the sequence is empty, folded split by split in
 // split order with a running max (the same identity applied incrementally),
 // so the result is the same on every run.  When a sequence has more than 16
-// splits (calls of one or a few sequences, up to 512 splits),
-// decode_combine_wide_kernel gives each (m, h) sixteen waves, each folding a
-// contiguous range of the splits, and folds their states in range order.
+// splits (calls of one or a few sequences, up to 512 splits) and there are no
+// more (m, h) than CUs, decode_combine_wide_kernel gives each (m, h) sixteen
+// waves, each folding a contiguous range of the splits, and folds their
+// states in range order.
 //
 // Register layouts of v_mfma_f32_16x16x4_f32 (lane l, i = l % 16, k = l / 16):
 // operand A supplies A[i][k], operand B supplies B[k][i], and output register
